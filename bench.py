@@ -1,0 +1,179 @@
+#!/usr/bin/env python3
+"""Forward+backward CGTP convolution throughput on one MI355X.
+
+One step = tpconv_forward + tpconv_backward (dx, dY, dW) over the 4096-atom
+SevenNet-l3i5-shaped workload: density 0.1/A^3, periodic box, cutoff 5 A
+(~214.6k edges), irreps 32x0e+32x1o+32x2e+32x3o in and out, SH l<=3, all 23
+parity-allowed paths, fp32, seeded synthetic inputs resident in HBM.
+
+Prints one JSON line: edges/s (value), per-kernel times, the dominant
+kernel's roofline point, and the fp64 CPU oracle timed on a bounded sample
+of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+FP32_VALU_PEAK_TFLOPS = 157.3  # 256 CU x 2.4 GHz x 64 lanes x 2 flop x 2 (packed FMA)
+FP32_VALU_PLAIN_TFLOPS = 78.6  # the same without packed FMA, which this build does not emit
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="c4k")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-edges", type=int, default=40000)
+    return p.parse_args()
+
+
+def algorithmic_bytes(plan, n_nodes, n_edges, b):
+    """Compulsory HBM bytes: every per-edge input read once, every output written once, node rows once."""
+    PU, Dsh = plan.weight_numel, plan.dim_sh
+    fwd = n_edges * ((PU + Dsh) * b + 4) + n_nodes * ((plan.dim_in + plan.dim_out) * b + 4)
+    bwd = n_edges * ((2 * PU + 2 * Dsh) * b + 8) + n_nodes * ((2 * plan.dim_in + plan.dim_out) * b + 4)
+    return fwd, bwd
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("tp_kernels.hip", "cg_real.hpp", "tp_common.hpp"):
+        with open(os.path.join(ROOT, "equivariant_mlip_tensor_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(w, d, sample_edges):
+    """The fp64 numpy oracle, as it stands, on the edges of the first destination rows."""
+    import numpy as np
+    from oracle import TPProblem, tp_backward, tp_forward
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    prob = TPProblem.build(w.irreps_in, w.sh_lmax, w.irreps_out)
+    dst = d["dst"]
+    E = len(dst)
+    m = min(sample_edges, E)
+    # whole destination rows: cut at a row boundary
+    last = dst[m - 1]
+    m = int(np.searchsorted(dst, last, side="right"))
+    sl = slice(0, m)
+    t0 = time.perf_counter()
+    tp_forward(prob, d["x"], d["Y"][sl], d["W"][sl], d["src"][sl], dst[sl], d["n_nodes"])
+    tp_backward(prob, d["x"], d["Y"][sl], d["W"][sl], d["G"], d["src"][sl], dst[sl], d["n_nodes"])
+    dt = time.perf_counter() - t0
+    return {"value": m / dt, "unit": "edges/s", "cores": int(blas), "kind": "oracle",
+            "sample": f"fwd+bwd over the {m} in-edges of destination rows 0..{int(last)} of {E} edges "
+                      f"({dt:.1f} s; numpy/BLAS threads {blas}, "
+                      f"{len(os.sched_getaffinity(0))} cores available)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build runs the convolution on a single MI355X; "
+              "--gpus above 1 is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from equivariant_mlip_tensor_amd import tpconv as tp
+
+    w = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    plan = tp.tpconv_plan(w.irreps_in, w.sh_lmax, w.irreps_out, w.dtype)
+    d = workloads.make_inputs(w, plan.n_paths, plan.weight_numel)
+    N, E = d["n_nodes"], len(d["src"])
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    src, dst = T(d["src"]), T(d["dst"])
+    x, Y, W, G = T(d["x"]), T(d["Y"]), T(d["W"]), T(d["G"])
+    t0 = time.perf_counter()
+    graph = tp.tpconv_graph_create(N, src, dst)
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t0) * 1e3
+    out = torch.empty((N, plan.dim_out), dtype=plan.torch_dtype, device=dev)
+    dx = torch.empty((N, plan.dim_in), dtype=plan.torch_dtype, device=dev)
+    dY = torch.empty((E, plan.dim_sh), dtype=plan.torch_dtype, device=dev)
+    dW = torch.empty((E, plan.weight_numel), dtype=plan.torch_dtype, device=dev)
+
+    def step():
+        tp.tpconv_forward(plan, graph, x, Y, W, out)
+        tp.tpconv_backward(plan, graph, x, Y, W, G, dx, dY, dW)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()   # the kernels are launched on this stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        tp.tpconv_forward(plan, graph, x, Y, W, out)
+        ev[k][1].record(stream)
+        tp.tpconv_backward(plan, graph, x, Y, W, G, dx, dY, dW)
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    bwd_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    peak_gib = torch.cuda.max_memory_allocated() / 2**30
+
+    b = 4 if w.dtype == "f32" else 8
+    fwd_bytes, bwd_bytes = algorithmic_bytes(plan, N, E, b)
+    f_avg, b_avg = float(fwd_ms.mean()), float(bwd_ms.mean())
+    ms_per_step = wall * 1e3 / args.steps
+    dom = ("tpconv_backward", bwd_bytes, b_avg) if b_avg >= f_avg else ("tpconv_forward", fwd_bytes, f_avg)
+    achieved = dom[1] / (dom[2] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom[0]}
+    hbm_fwdbwd = (fwd_bytes + bwd_bytes) / ((f_avg + b_avg) * 1e-3) / 1e9
+
+    res = {
+        "metric": "edges/sec fwd+bwd CGTP conv (l_max=3, 4096 atoms); achieved HBM GB/s % peak",
+        "value": round(E * args.steps / wall, 1),
+        "unit": "edges/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}: {N} atoms, density 0.1/A^3, periodic, cutoff {w.cutoff} A, "
+                               f"{E} edges, {w.irreps_in} -> {w.irreps_out}, SH l<={w.sh_lmax}, "
+                               f"{plan.n_paths} paths", "n_nodes": N, "n_edges": E},
+        "kernels_ms": {"forward_avg": round(f_avg, 4), "forward_min": round(float(fwd_ms.min()), 4),
+                       "backward_avg": round(b_avg, 4), "backward_min": round(float(bwd_ms.min()), 4)},
+        "hbm": {"fwd_bwd_algorithmic_GBps": round(hbm_fwdbwd, 1), "frac_of_peak": round(hbm_fwdbwd / HBM_PEAK_GBS, 4),
+                "fwd_bytes": int(fwd_bytes), "bwd_bytes": int(bwd_bytes)},
+        "roofline": roofline,
+        "graph_build_ms": round(graph_ms, 3),
+        "peak_device_GiB": round(peak_gib, 3),
+        "kernel_source": kernel_source_hash(),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, d, args.cpu_sample_edges)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,116 @@
+// api.cpp -- tpconv_forward / tpconv_backward dispatch and error reporting.
+#include <string>
+
+#include "tpconv_internal.hpp"
+
+namespace tpconv {
+
+namespace {
+thread_local std::string g_last_error;
+
+using Launcher = hipError_t (*)(const KernelArgs&, hipStream_t);
+
+Launcher pick(bool fwd, int L, tpconv_dtype dt) {
+#define TPCONV_PICK(LL)                                                                   \
+  case LL:                                                                                \
+    if (fwd) return dt == TPCONV_F32 ? launch_fwd_l##LL##_f32 : launch_fwd_l##LL##_f64; \
+    return dt == TPCONV_F32 ? launch_bwd_l##LL##_f32 : launch_bwd_l##LL##_f64;
+  switch (L) {
+    TPCONV_PICK(0)
+    TPCONV_PICK(1)
+    TPCONV_PICK(2)
+    TPCONV_PICK(3)
+    TPCONV_PICK(4)
+    default:
+      return nullptr;
+  }
+#undef TPCONV_PICK
+}
+
+KernelArgs base_args(const Plan& p, int64_t n_rows) {
+  KernelArgs a{};
+  a.n_rows = static_cast<int32_t>(n_rows);
+  a.mul = p.mul;
+  int lg = 0;
+  while ((1 << lg) < p.mul) ++lg;
+  a.lps_log2 = lg;
+  a.nslots = 64 >> lg;
+  a.d_in = static_cast<int32_t>(p.dim_in);
+  a.d_out = static_cast<int32_t>(p.dim_out);
+  a.d_sh = static_cast<int32_t>(p.dim_sh);
+  a.wstride = p.weight_numel;
+  a.pmask_lo = p.pmask_lo;
+  a.pmask_hi = p.pmask_hi;
+  for (int l = 0; l <= kMaxL; ++l) {
+    a.in_off[l] = p.in_off[l];
+    a.out_off[l] = p.out_off[l];
+  }
+  for (int t = 0; t < kMaxTriples; ++t) a.woff[t] = p.woff[t];
+  return a;
+}
+
+}  // namespace
+
+tpconv_status fail(tpconv_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+}  // namespace tpconv
+
+using namespace tpconv;
+
+extern "C" const char* tpconv_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" tpconv_status tpconv_forward(tpconv_plan_t hp, tpconv_graph_t hg, const void* x, const void* Y,
+                                        const void* W, void* out, hipStream_t stream) {
+  if (hp == nullptr || hg == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL plan or graph");
+  const Plan& p = *reinterpret_cast<const Plan*>(hp);
+  const Graph& g = *reinterpret_cast<const Graph*>(hg);
+  if (g.n_nodes > 0 && (out == nullptr || x == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL x or out");
+  if (g.n_edges > 0 && (Y == nullptr || W == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL Y or W");
+  if (g.n_nodes == 0) return TPCONV_OK;
+  KernelArgs a = base_args(p, g.n_nodes);
+  a.row_ptr = g.dst_row;
+  a.col = g.dst_col;
+  a.eid = g.dst_eid;
+  a.x = x;
+  a.Y = Y;
+  a.W = W;
+  a.out = out;
+  Launcher f = pick(true, p.kernel_l, p.dtype);
+  if (f == nullptr) return fail(TPCONV_E_UNSUPPORTED, "no kernel for this l bound");
+  const hipError_t he = f(a, stream);
+  if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("forward launch: ") + hipGetErrorString(he));
+  return TPCONV_OK;
+}
+
+extern "C" tpconv_status tpconv_backward(tpconv_plan_t hp, tpconv_graph_t hg, const void* x, const void* Y,
+                                         const void* W, const void* grad_out, void* grad_x, void* grad_Y,
+                                         void* grad_W, hipStream_t stream) {
+  if (hp == nullptr || hg == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL plan or graph");
+  const Plan& p = *reinterpret_cast<const Plan*>(hp);
+  const Graph& g = *reinterpret_cast<const Graph*>(hg);
+  const bool want_edges = g.n_edges > 0 && (grad_Y != nullptr || grad_W != nullptr);
+  if (grad_x == nullptr && !want_edges) return TPCONV_OK;
+  if (g.n_nodes > 0 && (x == nullptr || grad_out == nullptr))
+    return fail(TPCONV_E_INVALID_ARG, "NULL x or grad_out");
+  if (g.n_edges > 0 && (Y == nullptr || W == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL Y or W");
+  if (g.n_nodes == 0) return TPCONV_OK;
+  KernelArgs a = base_args(p, g.n_nodes);
+  a.row_ptr = g.src_row;
+  a.col = g.src_col;
+  a.eid = g.src_eid;
+  a.x = x;
+  a.Y = Y;
+  a.W = W;
+  a.G = grad_out;
+  a.out = grad_x;
+  a.dY = grad_Y;
+  a.dW = grad_W;
+  Launcher f = pick(false, p.kernel_l, p.dtype);
+  if (f == nullptr) return fail(TPCONV_E_UNSUPPORTED, "no kernel for this l bound");
+  const hipError_t he = f(a, stream);
+  if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("backward launch: ") + hipGetErrorString(he));
+  return TPCONV_OK;
+}

@@ -1,0 +1,243 @@
+// graph.hip -- destination- and source-sorted CSR views of an edge list.
+//
+// The convolution runs node-centric (LunaTP Abstract): the forward walks
+// each destination's in-edges, the backward each source's out-edges, so
+// both reductions happen in registers of one wavefront.  The layout is a
+// counting sort done on the device -- histogram, scan, scatter -- followed by
+// a per-row sort on the edge id, so every row lists its edges in the
+// caller's order and the layout (and every sum over a row) is deterministic.
+// Integer atomics are used only here, to count and place edges.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <new>
+#include <string>
+
+#include "tpconv_internal.hpp"
+
+namespace tpconv {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t dst_row, dst_col, dst_eid, src_row, src_col, src_eid, cur_dst, cur_src, err, total;
+};
+
+Layout layout(int64_t n, int64_t e) {
+  Layout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  L.dst_row = take(sizeof(int32_t) * (n + 1));
+  L.dst_col = take(sizeof(int32_t) * e);
+  L.dst_eid = take(sizeof(int32_t) * e);
+  L.src_row = take(sizeof(int32_t) * (n + 1));
+  L.src_col = take(sizeof(int32_t) * e);
+  L.src_eid = take(sizeof(int32_t) * e);
+  L.cur_dst = take(sizeof(int32_t) * n);
+  L.cur_src = take(sizeof(int32_t) * n);
+  L.err = take(sizeof(int32_t));
+  L.total = o;
+  return L;
+}
+
+__global__ void k_fill(int32_t* __restrict__ p, int64_t n, int32_t v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+__global__ void k_count(const int32_t* __restrict__ src, const int32_t* __restrict__ dst, int64_t E, int64_t N,
+                        int32_t* __restrict__ dst_cnt, int32_t* __restrict__ src_cnt, int32_t* __restrict__ err) {
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < E; e += (int64_t)gridDim.x * blockDim.x) {
+    const int32_t s = src[e], d = dst[e];
+    if (s < 0 || s >= N || d < 0 || d >= N) {
+      atomicAdd(err, 1);
+      continue;
+    }
+    atomicAdd(&dst_cnt[d], 1);
+    atomicAdd(&src_cnt[s], 1);
+  }
+}
+
+// In-place inclusive scan of p[0..n) by one 1024-thread block: each thread
+// sums a contiguous run, the run totals are scanned in LDS, then each run is
+// rewritten with its offset.
+__global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ p, int64_t n) {
+  __shared__ int32_t part[1024];
+  const int t = threadIdx.x;
+  const int64_t per = (n + 1023) / 1024;
+  const int64_t a = t * per;
+  const int64_t b = a + per < n ? a + per : n;
+  int32_t s = 0;
+  for (int64_t i = a; i < b; ++i) s += p[i];
+  part[t] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int32_t v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int32_t run = t > 0 ? part[t - 1] : 0;
+  for (int64_t i = a; i < b; ++i) {
+    run += p[i];
+    p[i] = run;
+  }
+}
+
+__global__ void k_scatter(const int32_t* __restrict__ src, const int32_t* __restrict__ dst, int64_t E, int64_t N,
+                          const int32_t* __restrict__ dst_row, int32_t* __restrict__ cur_dst,
+                          int32_t* __restrict__ dst_col, int32_t* __restrict__ dst_eid,
+                          const int32_t* __restrict__ src_row, int32_t* __restrict__ cur_src,
+                          int32_t* __restrict__ src_col, int32_t* __restrict__ src_eid) {
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < E; e += (int64_t)gridDim.x * blockDim.x) {
+    const int32_t s = src[e], d = dst[e];
+    if (s < 0 || s >= N || d < 0 || d >= N) continue;
+    const int32_t pd = dst_row[d] + atomicAdd(&cur_dst[d], 1);
+    dst_col[pd] = s;
+    dst_eid[pd] = static_cast<int32_t>(e);
+    const int32_t ps = src_row[s] + atomicAdd(&cur_src[s], 1);
+    src_col[ps] = d;
+    src_eid[ps] = static_cast<int32_t>(e);
+  }
+}
+
+// One thread per row: insertion sort of the row's (eid, col) pairs by eid.
+__global__ void k_sort_rows(const int32_t* __restrict__ row, int32_t* __restrict__ col, int32_t* __restrict__ eid,
+                            int64_t N) {
+  for (int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; r < N; r += (int64_t)gridDim.x * blockDim.x) {
+    const int32_t a = row[r], b = row[r + 1];
+    for (int32_t i = a + 1; i < b; ++i) {
+      const int32_t ke = eid[i], kc = col[i];
+      int32_t j = i - 1;
+      while (j >= a && eid[j] > ke) {
+        eid[j + 1] = eid[j];
+        col[j + 1] = col[j];
+        --j;
+      }
+      eid[j + 1] = ke;
+      col[j + 1] = kc;
+    }
+  }
+}
+
+int grid_for(int64_t n, int block) {
+  int64_t g = (n + block - 1) / block;
+  if (g < 1) g = 1;
+  if (g > 65536) g = 65536;
+  return static_cast<int>(g);
+}
+
+}  // namespace
+}  // namespace tpconv
+
+using tpconv::fail;
+using tpconv::Graph;
+
+extern "C" size_t tpconv_graph_workspace_bytes(int64_t n_nodes, int64_t n_edges) {
+  if (n_nodes < 0 || n_edges < 0) return 0;
+  return tpconv::layout(n_nodes, n_edges).total;
+}
+
+extern "C" tpconv_status tpconv_graph_create(int64_t n_nodes, int64_t n_edges, const int32_t* src,
+                                             const int32_t* dst, void* workspace, size_t workspace_bytes,
+                                             hipStream_t stream, tpconv_graph_t* out) {
+  using namespace tpconv;
+  if (out == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL output handle");
+  *out = nullptr;
+  if (n_nodes < 0 || n_edges < 0) return fail(TPCONV_E_INVALID_ARG, "negative node or edge count");
+  if (n_edges >= INT32_MAX || n_nodes >= INT32_MAX)
+    return fail(TPCONV_E_INVALID_ARG, "node and edge counts must be below 2^31");
+  if (n_edges > 0 && (src == nullptr || dst == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL src or dst");
+  if (workspace == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL workspace");
+  const Layout L = layout(n_nodes, n_edges);
+  if (workspace_bytes < L.total)
+    return fail(TPCONV_E_WORKSPACE, "workspace holds " + std::to_string(workspace_bytes) + " bytes, needs " +
+                                         std::to_string(L.total));
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return fail(TPCONV_E_WORKSPACE, "workspace must be 256-byte aligned");
+
+  char* base = static_cast<char*>(workspace);
+  auto at = [&](size_t off) { return reinterpret_cast<int32_t*>(base + off); };
+  Graph g;
+  g.n_nodes = n_nodes;
+  g.n_edges = n_edges;
+  g.dst_row = at(L.dst_row);
+  g.dst_col = at(L.dst_col);
+  g.dst_eid = at(L.dst_eid);
+  g.src_row = at(L.src_row);
+  g.src_col = at(L.src_col);
+  g.src_eid = at(L.src_eid);
+  int32_t* cur_dst = at(L.cur_dst);
+  int32_t* cur_src = at(L.cur_src);
+  int32_t* err = at(L.err);
+
+  const int B = 256;
+  hipLaunchKernelGGL(k_fill, dim3(grid_for(n_nodes + 1, B)), dim3(B), 0, stream, g.dst_row, n_nodes + 1, 0);
+  hipLaunchKernelGGL(k_fill, dim3(grid_for(n_nodes + 1, B)), dim3(B), 0, stream, g.src_row, n_nodes + 1, 0);
+  if (n_nodes > 0) {
+    hipLaunchKernelGGL(k_fill, dim3(grid_for(n_nodes, B)), dim3(B), 0, stream, cur_dst, n_nodes, 0);
+    hipLaunchKernelGGL(k_fill, dim3(grid_for(n_nodes, B)), dim3(B), 0, stream, cur_src, n_nodes, 0);
+  }
+  hipLaunchKernelGGL(k_fill, dim3(1), dim3(B), 0, stream, err, int64_t(1), 0);
+  if (n_edges > 0) {
+    hipLaunchKernelGGL(k_count, dim3(grid_for(n_edges, B)), dim3(B), 0, stream, src, dst, n_edges, n_nodes,
+                       g.dst_row + 1, g.src_row + 1, err);
+  }
+  if (n_nodes > 0) {
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, g.dst_row + 1, n_nodes);
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, g.src_row + 1, n_nodes);
+  }
+  if (n_edges > 0) {
+    hipLaunchKernelGGL(k_scatter, dim3(grid_for(n_edges, B)), dim3(B), 0, stream, src, dst, n_edges, n_nodes,
+                       g.dst_row, cur_dst, g.dst_col, g.dst_eid, g.src_row, cur_src, g.src_col, g.src_eid);
+    hipLaunchKernelGGL(k_sort_rows, dim3(grid_for(n_nodes, 64)), dim3(64), 0, stream, g.dst_row, g.dst_col,
+                       g.dst_eid, n_nodes);
+    hipLaunchKernelGGL(k_sort_rows, dim3(grid_for(n_nodes, 64)), dim3(64), 0, stream, g.src_row, g.src_col,
+                       g.src_eid, n_nodes);
+  }
+  hipError_t he = hipGetLastError();
+  if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("graph build launch: ") + hipGetErrorString(he));
+  int32_t h_err = 0;
+  he = hipMemcpyAsync(&h_err, err, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (he == hipSuccess) he = hipStreamSynchronize(stream);
+  if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("graph build: ") + hipGetErrorString(he));
+  if (h_err > 0)
+    return fail(TPCONV_E_INDEX, std::to_string(h_err) + " edge(s) have src or dst outside [0, " +
+                                    std::to_string(n_nodes) + ")");
+  Graph* h = new (std::nothrow) Graph(g);
+  if (h == nullptr) return fail(TPCONV_E_INVALID_ARG, "out of host memory");
+  *out = reinterpret_cast<tpconv_graph_t>(h);
+  return TPCONV_OK;
+}
+
+extern "C" tpconv_status tpconv_graph_export(tpconv_graph_t hg, int32_t* dst_row_ptr, int32_t* dst_col,
+                                             int32_t* dst_eid, int32_t* src_row_ptr, int32_t* src_col,
+                                             int32_t* src_eid, hipStream_t stream) {
+  if (hg == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL graph");
+  const Graph& g = *reinterpret_cast<const Graph*>(hg);
+  struct Item {
+    int32_t* host;
+    const int32_t* dev;
+    int64_t n;
+  } items[] = {{dst_row_ptr, g.dst_row, g.n_nodes + 1}, {dst_col, g.dst_col, g.n_edges},
+               {dst_eid, g.dst_eid, g.n_edges},         {src_row_ptr, g.src_row, g.n_nodes + 1},
+               {src_col, g.src_col, g.n_edges},         {src_eid, g.src_eid, g.n_edges}};
+  for (const Item& it : items) {
+    if (it.host == nullptr || it.n == 0) continue;
+    const hipError_t he =
+        hipMemcpyAsync(it.host, it.dev, sizeof(int32_t) * it.n, hipMemcpyDeviceToHost, stream);
+    if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("graph export: ") + hipGetErrorString(he));
+  }
+  const hipError_t he = hipStreamSynchronize(stream);
+  if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("graph export: ") + hipGetErrorString(he));
+  return TPCONV_OK;
+}
+
+extern "C" void tpconv_graph_destroy(tpconv_graph_t g) { delete reinterpret_cast<Graph*>(g); }

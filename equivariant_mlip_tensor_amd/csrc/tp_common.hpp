@@ -1,0 +1,82 @@
+// tp_common.hpp -- shared declarations between the host API and the kernels.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime_api.h>
+
+#include "cg_real.hpp"
+
+namespace tpconv {
+
+constexpr int kMaxL = cg::kLMax;
+
+// Triples (l1, l2, l3) with all l <= L and the triangle rule, enumerated in
+// lexicographic order; the kernels index per-path data by this id.
+constexpr int triple_count(int L) {
+  int n = 0;
+  for (int a = 0; a <= L; ++a)
+    for (int b = 0; b <= L; ++b)
+      for (int c = 0; c <= L; ++c)
+        if (cg::triangle(a, b, c)) ++n;
+  return n;
+}
+
+constexpr int triple_id(int L, int l1, int l2, int l3) {
+  int n = 0;
+  for (int a = 0; a <= L; ++a)
+    for (int b = 0; b <= L; ++b)
+      for (int c = 0; c <= L; ++c)
+        if (cg::triangle(a, b, c)) {
+          if (a == l1 && b == l2 && c == l3) return n;
+          ++n;
+        }
+  return -1;
+}
+
+constexpr int kMaxTriples = triple_count(kMaxL);  // 65
+static_assert(kMaxTriples <= 128, "triple ids must fit the two path-mask words");
+
+// Launch arguments shared by the forward and backward kernels.  `row_ptr`,
+// `col` and `eid` are the CSR view the kernel walks: destination-sorted for
+// the forward (col = src), source-sorted for the backward (col = dst).
+struct KernelArgs {
+  int32_t n_rows;       // nodes
+  int32_t mul;          // U, channels per segment (1..64)
+  int32_t lps_log2;     // log2 of lanes per edge slot: next power of two >= U
+  int32_t nslots;       // edges a wave processes side by side: 64 >> lps_log2
+  int32_t d_in, d_out, d_sh;
+  int32_t pad0;
+  int64_t wstride;      // weight_numel
+  uint64_t pmask_lo;    // bit t: triple t is a path of the plan (t < 64)
+  uint64_t pmask_hi;    // bit t-64
+  const int32_t* row_ptr;
+  const int32_t* col;
+  const int32_t* eid;
+  int32_t in_off[kMaxL + 1];   // x column of segment with this l, -1 if absent
+  int32_t out_off[kMaxL + 1];  // out column of segment with this l, -1 if absent
+  int32_t woff[kMaxTriples];   // W column of path with this triple, -1 if absent
+  const void* x;        // forward: x;  backward: x
+  const void* Y;
+  const void* W;
+  const void* G;        // backward only
+  void* out;            // forward: out; backward: grad_x (may be null)
+  void* dY;             // backward only (may be null)
+  void* dW;             // backward only (may be null)
+};
+
+// Launchers, one per (lmax, dtype), defined by tp_kernels.hip compiled once per lmax.
+#define TPCONV_DECLARE_LAUNCHERS(L)                                                \
+  hipError_t launch_fwd_l##L##_f32(const KernelArgs& a, hipStream_t s);            \
+  hipError_t launch_fwd_l##L##_f64(const KernelArgs& a, hipStream_t s);            \
+  hipError_t launch_bwd_l##L##_f32(const KernelArgs& a, hipStream_t s);            \
+  hipError_t launch_bwd_l##L##_f64(const KernelArgs& a, hipStream_t s);
+
+TPCONV_DECLARE_LAUNCHERS(0)
+TPCONV_DECLARE_LAUNCHERS(1)
+TPCONV_DECLARE_LAUNCHERS(2)
+TPCONV_DECLARE_LAUNCHERS(3)
+TPCONV_DECLARE_LAUNCHERS(4)
+
+}  // namespace tpconv

@@ -1,0 +1,62 @@
+// tpconv_internal.hpp -- host-side structs behind the opaque C handles.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "tp_common.hpp"
+#include "tpconv.h"
+
+namespace tpconv {
+
+struct Segment {
+  int mul;
+  int l;
+  int p;  // +1 even, -1 odd
+};
+
+struct Path {
+  int s1, l2, s3;
+  int64_t woff;  // first W column of the path
+};
+
+struct Plan {
+  std::vector<Segment> in, out;
+  int sh_lmax = 0;
+  tpconv_dtype dtype = TPCONV_F32;
+  int mul = 0;
+  int kernel_l = 0;
+  int64_t dim_in = 0, dim_out = 0, dim_sh = 0;
+  std::vector<Path> paths;
+  int64_t weight_numel = 0;
+  // sparse real CG table
+  std::vector<uint32_t> entries;
+  std::vector<int32_t> path_ptr;
+  std::vector<double> values;
+  // kernel arguments fixed by the plan
+  int32_t in_off[kMaxL + 1];
+  int32_t out_off[kMaxL + 1];
+  int32_t woff[kMaxTriples];
+  uint64_t pmask_lo = 0, pmask_hi = 0;
+
+  static tpconv_status build(const char* irreps_in, int sh_lmax, const char* irreps_out, tpconv_dtype dt,
+                             Plan& p);
+};
+
+struct Graph {
+  int64_t n_nodes = 0, n_edges = 0;
+  // destination-sorted CSR: row i lists edges with dst == i; col = src
+  int32_t* dst_row = nullptr;
+  int32_t* dst_col = nullptr;
+  int32_t* dst_eid = nullptr;
+  // source-sorted CSR: row j lists edges with src == j; col = dst
+  int32_t* src_row = nullptr;
+  int32_t* src_col = nullptr;
+  int32_t* src_eid = nullptr;
+};
+
+// Records the message for tpconv_last_error() and returns the status.
+tpconv_status fail(tpconv_status st, const std::string& msg);
+
+}  // namespace tpconv

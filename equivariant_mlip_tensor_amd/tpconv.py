@@ -1,0 +1,243 @@
+"""ctypes binding of libtpconv.so: the C entry points under the same names.
+
+Argument marshalling only: torch supplies device memory and the stream, every
+step of the convolution runs in the library's HIP kernels.  Importing this
+module loads the library and raises if it is missing -- there is no fallback.
+
+    plan  = tpconv_plan("32x0e+32x1o", 1, "32x0e+32x1o", "f32")
+    graph = tpconv_graph_create(n_nodes, src, dst)          # src, dst: int32 cuda
+    out   = tpconv_forward(plan, graph, x, Y, W)
+    dx, dY, dW = tpconv_backward(plan, graph, x, Y, W, grad_out)
+
+The layouts are those of include/tpconv.h.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch  # loads the HIP runtime the library then binds to
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpconv.so")
+
+F32, F64 = 0, 1
+STATUS = {0: "TPCONV_OK", 1: "TPCONV_E_INVALID_ARG", 2: "TPCONV_E_IRREPS", 3: "TPCONV_E_UNSUPPORTED",
+          4: "TPCONV_E_NO_PATHS", 5: "TPCONV_E_WORKSPACE", 6: "TPCONV_E_INDEX", 7: "TPCONV_E_HIP"}
+
+EXPORTS = ("tpconv_plan", "tpconv_plan_query", "tpconv_plan_paths", "tpconv_plan_table", "tpconv_plan_destroy",
+           "tpconv_graph_workspace_bytes", "tpconv_graph_create", "tpconv_graph_export", "tpconv_graph_destroy",
+           "tpconv_forward", "tpconv_backward", "tpconv_last_error")
+
+
+class TPConvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("dim_in", ctypes.c_int64), ("dim_out", ctypes.c_int64), ("dim_sh", ctypes.c_int64),
+                ("n_paths", ctypes.c_int64), ("weight_numel", ctypes.c_int64), ("cg_nnz", ctypes.c_int64),
+                ("cg_nvalues", ctypes.c_int64), ("mul", ctypes.c_int64), ("kernel_lmax", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(python -m equivariant_mlip_tensor_amd.build)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "tpconv_plan": (i32, [ctypes.c_char_p, ctypes.c_int, ctypes.c_char_p, ctypes.c_int, ctypes.POINTER(vp)]),
+        "tpconv_plan_query": (i32, [vp, ctypes.POINTER(PlanInfo)]),
+        "tpconv_plan_paths": (i32, [vp, vp]),
+        "tpconv_plan_table": (i32, [vp, vp, vp, vp]),
+        "tpconv_plan_destroy": (None, [vp]),
+        "tpconv_graph_workspace_bytes": (sz, [i64, i64]),
+        "tpconv_graph_create": (i32, [i64, i64, vp, vp, vp, sz, vp, ctypes.POINTER(vp)]),
+        "tpconv_graph_export": (i32, [vp, vp, vp, vp, vp, vp, vp, vp]),
+        "tpconv_graph_destroy": (None, [vp]),
+        "tpconv_forward": (i32, [vp, vp, vp, vp, vp, vp, vp]),
+        "tpconv_backward": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "tpconv_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise TPConvError(status, _lib.tpconv_last_error().decode(errors="replace"))
+
+
+def tpconv_last_error() -> str:
+    return _lib.tpconv_last_error().decode(errors="replace")
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+# ---------------------------------------------------------------------- plans
+class Plan:
+    """Owns a tpconv_plan_t; sizes as attributes."""
+
+    def __init__(self, handle: ctypes.c_void_p):
+        self.handle = handle
+        info = PlanInfo()
+        _check(_lib.tpconv_plan_query(handle, ctypes.byref(info)))
+        self.info = info
+        for f, _ in PlanInfo._fields_:
+            setattr(self, f, getattr(info, f))
+        self.torch_dtype = torch.float32 if info.dtype == F32 else torch.float64
+
+    def __del__(self):
+        h, self.handle = getattr(self, "handle", None), None
+        if h and _lib is not None:
+            _lib.tpconv_plan_destroy(h)
+
+
+def tpconv_plan(irreps_in: str, sh_lmax: int, irreps_out: str, dtype="f32") -> Plan:
+    dt = {"f32": F32, "f64": F64, torch.float32: F32, torch.float64: F64, F32: F32, F64: F64}.get(dtype, dtype)
+    h = ctypes.c_void_p()
+    _check(_lib.tpconv_plan(irreps_in.encode(), int(sh_lmax), irreps_out.encode(), int(dt), ctypes.byref(h)))
+    return Plan(h)
+
+
+def tpconv_plan_query(plan: Plan) -> PlanInfo:
+    info = PlanInfo()
+    _check(_lib.tpconv_plan_query(plan.handle, ctypes.byref(info)))
+    return info
+
+
+def tpconv_plan_paths(plan: Plan):
+    """List of (s1, l2, s3, weight_offset)."""
+    buf = (ctypes.c_int32 * (4 * plan.n_paths))()
+    _check(_lib.tpconv_plan_paths(plan.handle, buf))
+    return [tuple(buf[4 * i:4 * i + 4]) for i in range(plan.n_paths)]
+
+
+def tpconv_plan_table(plan: Plan):
+    """(entries uint32 [nnz], path_ptr int32 [P+1], values float64 [nvalues]) as Python lists."""
+    ent = (ctypes.c_uint32 * max(1, plan.cg_nnz))()
+    ptr = (ctypes.c_int32 * (plan.n_paths + 1))()
+    val = (ctypes.c_double * max(1, plan.cg_nvalues))()
+    _check(_lib.tpconv_plan_table(plan.handle, ent, ptr, val))
+    return list(ent)[:plan.cg_nnz], list(ptr), list(val)[:plan.cg_nvalues]
+
+
+def tpconv_plan_destroy(plan: Plan) -> None:
+    plan.__del__()
+
+
+# --------------------------------------------------------------------- graphs
+def tpconv_graph_workspace_bytes(n_nodes: int, n_edges: int) -> int:
+    return int(_lib.tpconv_graph_workspace_bytes(int(n_nodes), int(n_edges)))
+
+
+class Graph:
+    """Owns a tpconv_graph_t and the device workspace tensor it lives in."""
+
+    def __init__(self, handle, workspace: torch.Tensor, n_nodes: int, n_edges: int):
+        self.handle, self.workspace, self.n_nodes, self.n_edges = handle, workspace, n_nodes, n_edges
+
+    def __del__(self):
+        h, self.handle = getattr(self, "handle", None), None
+        if h and _lib is not None:
+            _lib.tpconv_graph_destroy(h)
+
+
+def tpconv_graph_create(n_nodes: int, src: torch.Tensor, dst: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                        stream=None) -> Graph:
+    if src.dtype != torch.int32 or dst.dtype != torch.int32 or not src.is_cuda or not dst.is_cuda:
+        raise TypeError("src and dst must be int32 device tensors")
+    if src.shape != dst.shape or src.dim() != 1:
+        raise ValueError("src and dst must be 1-D and of equal length")
+    src, dst = src.contiguous(), dst.contiguous()
+    n_edges = src.numel()
+    need = tpconv_graph_workspace_bytes(n_nodes, n_edges)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=src.device)
+    h = ctypes.c_void_p()
+    _check(_lib.tpconv_graph_create(int(n_nodes), int(n_edges), _ptr(src), _ptr(dst), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream_handle(stream),
+                                    ctypes.byref(h)))
+    return Graph(h, workspace, int(n_nodes), int(n_edges))
+
+
+def tpconv_graph_export(graph: Graph, stream=None):
+    """Host copies (numpy int32) of dst_row_ptr, dst_col, dst_eid, src_row_ptr, src_col, src_eid."""
+    import numpy as np
+    n, e = graph.n_nodes, graph.n_edges
+    arrs = [np.zeros(n + 1, np.int32), np.zeros(e, np.int32), np.zeros(e, np.int32),
+            np.zeros(n + 1, np.int32), np.zeros(e, np.int32), np.zeros(e, np.int32)]
+    _check(_lib.tpconv_graph_export(graph.handle, *[ctypes.c_void_p(a.ctypes.data) for a in arrs],
+                                    _stream_handle(stream)))
+    return arrs
+
+
+def tpconv_graph_destroy(graph: Graph) -> None:
+    graph.__del__()
+
+
+# -------------------------------------------------------------------- compute
+def _need(t, shape, dtype, name):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda or t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous {dtype} cuda tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)} (cuda={t.is_cuda}, contiguous={t.is_contiguous()})")
+    return t
+
+
+def tpconv_forward(plan: Plan, graph: Graph, x, Y, W, out=None, stream=None) -> torch.Tensor:
+    N, E, dt = graph.n_nodes, graph.n_edges, plan.torch_dtype
+    _need(x, (N, plan.dim_in), dt, "x")
+    _need(Y, (E, plan.dim_sh), dt, "Y")
+    _need(W, (E, plan.weight_numel), dt, "W")
+    if out is None:
+        out = torch.empty((N, plan.dim_out), dtype=dt, device=x.device)
+    _need(out, (N, plan.dim_out), dt, "out")
+    _check(_lib.tpconv_forward(plan.handle, graph.handle, _ptr(x), _ptr(Y), _ptr(W), _ptr(out),
+                               _stream_handle(stream)))
+    return out
+
+
+def tpconv_backward(plan: Plan, graph: Graph, x, Y, W, grad_out, grad_x=None, grad_Y=None, grad_W=None,
+                    need=(True, True, True), stream=None) -> Tuple[Optional[torch.Tensor], ...]:
+    """Returns (grad_x, grad_Y, grad_W); an output is None when `need` turns it off."""
+    N, E, dt = graph.n_nodes, graph.n_edges, plan.torch_dtype
+    _need(x, (N, plan.dim_in), dt, "x")
+    _need(Y, (E, plan.dim_sh), dt, "Y")
+    _need(W, (E, plan.weight_numel), dt, "W")
+    _need(grad_out, (N, plan.dim_out), dt, "grad_out")
+    dev = x.device
+    if need[0] and grad_x is None:
+        grad_x = torch.empty((N, plan.dim_in), dtype=dt, device=dev)
+    if need[1] and grad_Y is None:
+        grad_Y = torch.empty((E, plan.dim_sh), dtype=dt, device=dev)
+    if need[2] and grad_W is None:
+        grad_W = torch.empty((E, plan.weight_numel), dtype=dt, device=dev)
+    for t, shp, nm in ((grad_x, (N, plan.dim_in), "grad_x"), (grad_Y, (E, plan.dim_sh), "grad_Y"),
+                       (grad_W, (E, plan.weight_numel), "grad_W")):
+        if t is not None:
+            _need(t, shp, dt, nm)
+    _check(_lib.tpconv_backward(plan.handle, graph.handle, _ptr(x), _ptr(Y), _ptr(W), _ptr(grad_out),
+                                _ptr(grad_x), _ptr(grad_Y), _ptr(grad_W), _stream_handle(stream)))
+    return grad_x, grad_Y, grad_W

@@ -1,0 +1,195 @@
+/*
+ * tpconv.h -- C ABI of the MI355X (gfx950) Clebsch-Gordan tensor-product
+ * convolution library, libtpconv.so.
+ *
+ * The operation is the "CGTP convolution" of equivariant interatomic
+ * potentials (LunaTP: Enabling Efficient and Scalable Tensor Product for
+ * Equivariant MLIPs -- Abstract): a tensor-product layer and its following
+ * reduce layer over a sparse Clebsch-Gordan coefficient matrix (FlashTP:
+ * Fused, Sparsity-Aware Tensor Product for Machine Learning Interatomic
+ * Potentials -- "Problem" and "Approach").  For an edge e with j = src(e),
+ * i = dst(e), a path p = (s1, l2, s3) of real-basis CG tensor C_p and a
+ * channel u:
+ *
+ *   out[i,s3,u,m3] = sum_{e: dst=i} sum_{p->s3} W[e,p,u]
+ *                    sum_{m1,m2} C_p[m1,m2,m3] x[j,s1,u,m1] Y[e,l2,m2]
+ *
+ * and the backward gives dx, dY, dW of <G, out> for a supplied G.  Where
+ * the pages are silent the library takes these readings: channelwise (uvu)
+ * coupling, one weight per (edge, path, channel), paths into the same
+ * output segment summed with coefficient 1, complex CG from Racah's formula
+ * (Condon-Shortley phase) turned real through the basis change U^l listed
+ * in cg_real.hpp, odd l1+l2+l3 taking the imaginary part.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensor pointers are DEVICE pointers in the plan's dtype, row-major and
+ *    contiguous:
+ *      x   [N][D_in]    segments concatenated in irreps order; segment s
+ *                       stored [mul_s][2 l_s + 1], m ascending -l..l
+ *      Y   [E][D_sh]    D_sh = (sh_lmax+1)^2, (l, m) at column l*l + l + m
+ *      W   [E][weight_numel]  path p at columns [off_p, off_p + mul_p),
+ *                       paths in lexicographic (s1, l2, s3) order
+ *      out [N][D_out]   like x
+ *    Per-edge tensors are in the caller's edge order (the order of the
+ *    src/dst arrays given to tpconv_graph_create).
+ *  - Ownership: the caller owns every device buffer, including the graph
+ *    workspace.  The library never allocates device memory.  Plans and
+ *    graph handles own only small host structs.
+ *  - Every call is asynchronous on `stream`, except tpconv_graph_create,
+ *    which synchronises `stream` once to report index errors.
+ *  - A status other than TPCONV_OK means nothing was launched; the message
+ *    is available from tpconv_last_error() on the calling thread.  No C++
+ *    exception crosses this interface.
+ *  - Results are deterministic: the reductions use no floating-point
+ *    atomics, so repeated calls give bitwise identical outputs.
+ *
+ * Kernel coverage: every irreps string may hold each l at most once, all
+ * segments of irreps_in and irreps_out share one multiplicity U (any
+ * U >= 1), and every l (inputs, outputs, SH) is at most TPCONV_MAX_L.
+ * Other plans are rejected with TPCONV_E_UNSUPPORTED.
+ */
+#ifndef TPCONV_H
+#define TPCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TPCONV_MAX_L 4
+
+typedef enum { TPCONV_F32 = 0, TPCONV_F64 = 1 } tpconv_dtype;
+
+typedef enum {
+  TPCONV_OK = 0,
+  TPCONV_E_INVALID_ARG = 1, /* NULL pointer, negative size, bad dtype, size mismatch */
+  TPCONV_E_IRREPS = 2,      /* irreps string does not parse */
+  TPCONV_E_UNSUPPORTED = 3, /* l > TPCONV_MAX_L, repeated l, unequal multiplicities */
+  TPCONV_E_NO_PATHS = 4,    /* no admissible (s1, l2, s3) path */
+  TPCONV_E_WORKSPACE = 5,   /* graph workspace too small or misaligned */
+  TPCONV_E_INDEX = 6,       /* some src/dst index outside [0, n_nodes) */
+  TPCONV_E_HIP = 7          /* a HIP runtime call or kernel launch failed */
+} tpconv_status;
+
+typedef struct tpconv_plan_s* tpconv_plan_t;
+typedef struct tpconv_graph_s* tpconv_graph_t;
+
+typedef struct {
+  int64_t dim_in;        /* D_in  = sum mul*(2l+1) over irreps_in  */
+  int64_t dim_out;       /* D_out = sum mul*(2l+1) over irreps_out */
+  int64_t dim_sh;        /* (sh_lmax+1)^2 */
+  int64_t n_paths;       /* P */
+  int64_t weight_numel;  /* sum_p mul_p = row width of W and dW */
+  int64_t cg_nnz;        /* nonzero real CG entries summed over the paths */
+  int64_t cg_nvalues;    /* distinct |CG| values after deduplication */
+  int64_t mul;           /* the common multiplicity U */
+  int64_t kernel_lmax;   /* l bound the dispatched kernels are built for */
+  int32_t dtype;         /* tpconv_dtype */
+  int32_t reserved;
+} tpconv_plan_info;
+
+/* ---------------------------------------------------------------- plans --
+ * tpconv_plan: parse the irreps, enumerate the admissible paths and build
+ * the sparse real CG table (COO with deduplicated values), all on the host.
+ * The sparse COO table with deduplicated values and the grouping of paths
+ * that share an input follow FlashTP's "Approach" section and the path
+ * aggregation rows of its measured-effects table.
+ *   irreps_in, irreps_out: "mul x l p" terms joined by '+', e.g.
+ *     "32x0e+32x1o+32x2e"; mul defaults to 1; p is 'e' or 'o'.
+ *   sh_lmax: the SH input holds one copy of every l = 0..sh_lmax, parity (-1)^l.
+ *   Path rule: |l1-l2| <= l3 <= l1+l2, p1 (-1)^l2 == p3, mul_s1 == mul_s3.
+ * Errors: TPCONV_E_INVALID_ARG (NULL, sh_lmax < 0, bad dtype),
+ *   TPCONV_E_IRREPS, TPCONV_E_UNSUPPORTED, TPCONV_E_NO_PATHS.
+ * On success *out owns a host struct; free it with tpconv_plan_destroy. */
+tpconv_status tpconv_plan(const char* irreps_in, int sh_lmax, const char* irreps_out,
+                          tpconv_dtype dtype, tpconv_plan_t* out);
+
+/* Sizes of a plan.  Errors: TPCONV_E_INVALID_ARG on NULL. */
+tpconv_status tpconv_plan_query(tpconv_plan_t plan, tpconv_plan_info* info);
+
+/* Path list, host buffer of n_paths*4 int32: (s1, l2, s3, weight column
+ * offset) per path, in W's column order.  Errors: TPCONV_E_INVALID_ARG. */
+tpconv_status tpconv_plan_paths(tpconv_plan_t plan, int32_t* paths);
+
+/* The plan's sparse real CG table, host buffers:
+ *   entries[cg_nnz]: packed u32  m1 | m2<<4 | m3<<8 | neg<<12 | value_index<<13
+ *                    (m indices are m + l, 0..2l; value = (neg ? -1 : 1) *
+ *                    values[value_index]); entries of a path are ordered by
+ *                    (m1, m2, m3)
+ *   path_ptr[n_paths+1]: entries of path p are [path_ptr[p], path_ptr[p+1])
+ *   values[cg_nvalues]: distinct |C| in fp64.
+ * Any pointer may be NULL to skip that array.  The kernels are compiled
+ * from the same builder (cg_real.hpp), so these are the coefficients they
+ * apply.  Errors: TPCONV_E_INVALID_ARG on a NULL plan. */
+tpconv_status tpconv_plan_table(tpconv_plan_t plan, uint32_t* entries, int32_t* path_ptr,
+                                double* values);
+
+void tpconv_plan_destroy(tpconv_plan_t plan);
+
+/* ---------------------------------------------------------------- graphs --
+ * Destination-sorted and source-sorted CSR views of an edge list (node-
+ * centric execution, LunaTP Abstract).  Rows are stable: inside a row,
+ * edges keep the caller's order, so the layout and every result built on
+ * it are deterministic.
+ *
+ * tpconv_graph_workspace_bytes: device bytes the caller must provide for
+ * n_nodes nodes and n_edges edges (returns 0 for negative sizes). */
+size_t tpconv_graph_workspace_bytes(int64_t n_nodes, int64_t n_edges);
+
+/* tpconv_graph_create: build both CSR views on `stream` into `workspace`
+ * (device, >= tpconv_graph_workspace_bytes, 256-byte aligned).
+ *   src, dst: device int32 [n_edges]; edge e goes src[e] -> dst[e].
+ * The workspace must outlive the graph and must not be written by the
+ * caller while the graph is in use.  Edges with an index outside
+ * [0, n_nodes) are dropped from the layout and reported: the call then
+ * returns TPCONV_E_INDEX (after synchronising `stream`) and *out is NULL.
+ * Other errors: TPCONV_E_INVALID_ARG (NULL, n_nodes < 0, n_edges < 0,
+ * n_edges >= 2^31), TPCONV_E_WORKSPACE, TPCONV_E_HIP. */
+tpconv_status tpconv_graph_create(int64_t n_nodes, int64_t n_edges, const int32_t* src,
+                                  const int32_t* dst, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream, tpconv_graph_t* out);
+
+/* Copy the CSR arrays to host buffers (any may be NULL), for inspection:
+ * dst_row_ptr/src_row_ptr [n_nodes+1], dst_col (=src), dst_eid, src_col
+ * (=dst), src_eid [n_edges].  Synchronous on `stream`. */
+tpconv_status tpconv_graph_export(tpconv_graph_t g, int32_t* dst_row_ptr, int32_t* dst_col,
+                                  int32_t* dst_eid, int32_t* src_row_ptr, int32_t* src_col,
+                                  int32_t* src_eid, hipStream_t stream);
+
+void tpconv_graph_destroy(tpconv_graph_t g);
+
+/* ------------------------------------------------------------- compute --
+ * tpconv_forward: out = CGTP convolution of x, Y, W over graph g.
+ * One fused kernel: gather of x[src], tensor product and segmented
+ * reduction over each destination's CSR row, no per-edge tensor written
+ * (FlashTP "Approach": the tensor-product and reduce layers fused into one
+ * kernel; its measured-effects table credits this fusion with the larger
+ * systems it can hold).  out is overwritten; a node without in-edges gets
+ * zeros.  Errors: TPCONV_E_INVALID_ARG (NULL handle or tensor pointer when
+ * the tensor is non-empty), TPCONV_E_HIP (launch failure). */
+tpconv_status tpconv_forward(tpconv_plan_t plan, tpconv_graph_t g, const void* x, const void* Y,
+                             const void* W, void* out, hipStream_t stream);
+
+/* tpconv_backward: gradients of <G, out> for G = grad_out [N][D_out]:
+ *   grad_x [N][D_in], grad_Y [E][D_sh], grad_W [E][weight_numel].
+ * One fused kernel over the source-sorted CSR: dx is reduced per source
+ * row in registers, dY and dW are written once per edge.  Each output is
+ * overwritten; pass NULL to skip one (its work is still done when another
+ * output needs it).  Errors as tpconv_forward. */
+tpconv_status tpconv_backward(tpconv_plan_t plan, tpconv_graph_t g, const void* x, const void* Y,
+                              const void* W, const void* grad_out, void* grad_x, void* grad_Y,
+                              void* grad_W, hipStream_t stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* tpconv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPCONV_H */

@@ -1,0 +1,138 @@
+"""Host-side checks of libtpconv.so (CPU only: no kernel is launched).
+
+The library loads, exports every entry point the header declares, and its
+host CG-table builder, path list and error paths agree with the oracle and
+with the header's contract.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import TPProblem, cg_real
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "equivariant_mlip_tensor_amd", "libtpconv.so")
+HEADER = os.path.join(ROOT, "include", "tpconv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libtpconv.so not built")
+
+
+@pytest.fixture(scope="module")
+def tp():
+    from equivariant_mlip_tensor_amd import tpconv
+    return tpconv
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tpconv_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(tp):
+    declared = header_functions()
+    assert len(declared) == 12
+    assert sorted(tp.EXPORTS) == declared
+    lib = ctypes.CDLL(LIB)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+CASES = [(w.irreps_in, w.sh_lmax, w.irreps_out, w.dtype) for w in workloads.WORKLOADS.values()] + [
+    ("3x1o+3x0e", 2, "3x1e+3x2o+3x0o", "f64"),        # odd paths, unsorted segments
+    ("5x0e+5x2e", 1, "5x1o+5x2e+5x3o", "f32"),        # missing l, sh below the l bound
+    ("1x4e", 4, "1x0e+1x4e", "f64"),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_plan_matches_oracle_paths_and_cg(tp, case):
+    irr_in, lsh, irr_out, dt = case
+    prob = TPProblem.build(irr_in, lsh, irr_out)
+    plan = tp.tpconv_plan(irr_in, lsh, irr_out, dt)
+    assert plan.n_paths == len(prob.paths)
+    assert plan.weight_numel == prob.weight_numel
+    assert (plan.dim_in, plan.dim_out, plan.dim_sh) == (prob.dim_in, prob.dim_out, prob.dim_sh)
+    paths = tp.tpconv_plan_paths(plan)
+    assert [p[:3] for p in paths] == [tuple(p) for p in prob.paths]
+    assert [p[3] for p in paths] == prob.weight_offsets
+    entries, ptr, values = tp.tpconv_plan_table(plan)
+    assert len(entries) == plan.cg_nnz and ptr[-1] == plan.cg_nnz and len(values) == plan.cg_nvalues
+    vals = np.array(values)
+    assert np.all(vals > 0)
+    # deduplicated: no two stored magnitudes coincide
+    assert len(np.unique(np.round(vals, 12))) == len(vals)
+    nnz = 0
+    for p in range(plan.n_paths):
+        l1, l2, l3 = prob.path_ls(p)
+        dense = np.zeros((2 * l1 + 1, 2 * l2 + 1, 2 * l3 + 1))
+        keys = []
+        for e in entries[ptr[p]:ptr[p + 1]]:
+            m1, m2, m3, neg, vi = e & 15, (e >> 4) & 15, (e >> 8) & 15, (e >> 12) & 1, e >> 13
+            dense[m1, m2, m3] = (-1.0 if neg else 1.0) * values[vi]
+            keys.append((m1, m2, m3))
+        assert keys == sorted(keys)                       # entries ordered by (m1, m2, m3)
+        ref = cg_real(l1, l2, l3)
+        np.testing.assert_allclose(dense, ref, atol=2e-15, rtol=0)
+        assert np.count_nonzero(dense) == np.count_nonzero(ref)   # zeros skipped, none lost
+        nnz += np.count_nonzero(ref)
+    assert nnz == plan.cg_nnz
+
+
+def test_survey_sizes(tp):
+    # path count, nonzeros and distinct values of the l<=3 and l<=4 workloads
+    w3 = workloads.WORKLOADS["c4k"]
+    p3 = tp.tpconv_plan(w3.irreps_in, 3, w3.irreps_out, "f32")
+    assert (p3.n_paths, p3.cg_nnz, p3.weight_numel) == (23, 353, 736)
+    w4 = workloads.WORKLOADS["c2k"]
+    p4 = tp.tpconv_plan(w4.irreps_in, 4, w4.irreps_out, "f64")
+    assert (p4.n_paths, p4.cg_nnz) == (42, 1158)
+
+
+@pytest.mark.parametrize("irr_in,lsh,irr_out,dt,status", [
+    ("4x1q", 1, "4x1o", "f32", "TPCONV_E_IRREPS"),
+    ("4x", 1, "4x1o", "f32", "TPCONV_E_IRREPS"),
+    ("", 1, "4x1o", "f32", "TPCONV_E_IRREPS"),
+    ("4x1o+", 1, "4x1o", "f32", "TPCONV_E_IRREPS"),
+    ("0x1o", 1, "4x1o", "f32", "TPCONV_E_IRREPS"),
+    ("4x5e", 1, "4x5e", "f32", "TPCONV_E_UNSUPPORTED"),
+    ("4x1o", 5, "4x1o", "f32", "TPCONV_E_UNSUPPORTED"),
+    ("4x1o+4x1e", 1, "4x1o", "f32", "TPCONV_E_UNSUPPORTED"),
+    ("4x1o+4x1o", 1, "4x1o", "f32", "TPCONV_E_UNSUPPORTED"),
+    ("4x0e", 1, "8x1o", "f32", "TPCONV_E_UNSUPPORTED"),
+    ("128x0e", 0, "128x0e", "f32", "TPCONV_E_UNSUPPORTED"),
+    ("1x0e", 1, "1x2e", "f32", "TPCONV_E_NO_PATHS"),
+    ("1x0e", -1, "1x0e", "f32", "TPCONV_E_INVALID_ARG"),
+    ("1x0e", 0, "1x0e", 7, "TPCONV_E_INVALID_ARG"),
+])
+def test_plan_errors(tp, irr_in, lsh, irr_out, dt, status):
+    with pytest.raises(tp.TPConvError) as ei:
+        tp.tpconv_plan(irr_in, lsh, irr_out, dt)
+    assert ei.value.name == status
+    assert tp.tpconv_last_error()
+
+
+def test_null_and_size_errors_need_no_gpu(tp):
+    lib = tp._lib
+    h = ctypes.c_void_p()
+    assert lib.tpconv_plan(None, 1, b"1x0e", 0, ctypes.byref(h)) == 1
+    assert lib.tpconv_plan(b"1x0e", 1, b"1x0e", 0, None) == 1
+    assert lib.tpconv_plan_query(None, None) == 1
+    assert lib.tpconv_forward(None, None, None, None, None, None, None) == 1
+    assert lib.tpconv_backward(None, None, None, None, None, None, None, None, None, None) == 1
+    assert lib.tpconv_graph_workspace_bytes(-1, 5) == 0
+    ws = tp.tpconv_graph_workspace_bytes(10, 100)
+    assert ws >= 4 * (2 * 11 + 4 * 100 + 2 * 10 + 1)
+    g = ctypes.c_void_p()
+    buf = (ctypes.c_uint8 * 64)()
+    # errors detected before anything is launched
+    assert lib.tpconv_graph_create(-1, 0, None, None, buf, 64, None, ctypes.byref(g)) == 1
+    assert lib.tpconv_graph_create(10, 1 << 31, buf, buf, buf, 64, None, ctypes.byref(g)) == 1
+    assert lib.tpconv_graph_create(10, 5, None, None, buf, 64, None, ctypes.byref(g)) == 1
+    assert lib.tpconv_graph_create(10, 100, buf, buf, buf, 64, None, ctypes.byref(g)) == 5
+    assert "workspace" in tp.tpconv_last_error()
