@@ -112,6 +112,34 @@ __device__ __forceinline__ bool present(const KernelArgs& a) {
     return (a.pmask_hi >> (T - 64)) & 1ull;
 }
 
+template <int T>
+__device__ __forceinline__ bool first3(const KernelArgs& a) {
+  if constexpr (T < 64)
+    return (a.first3_lo >> T) & 1ull;
+  else
+    return (a.first3_hi >> (T - 64)) & 1ull;
+}
+
+template <int T>
+__device__ __forceinline__ bool first1(const KernelArgs& a) {
+  if constexpr (T < 64)
+    return (a.first1_lo >> T) & 1ull;
+  else
+    return (a.first1_hi >> (T - 64)) & 1ull;
+}
+
+// Row accumulators: a row sums one term per edge, so for fp32 data it is
+// kept in fp64 (full rate on CDNA); each edge's own sum over its paths stays
+// in the data type.
+template <typename T>
+struct RowAcc {
+  using type = T;
+};
+template <>
+struct RowAcc<float> {
+  using type = double;
+};
+
 template <int L, int PAR, int L1, int L2>
 __device__ __forceinline__ bool group_present(const KernelArgs& a) {
   bool any = false;
@@ -134,9 +162,9 @@ struct Fwd {
   static constexpr int NL = (L + 1) * (L + 1);
   static constexpr int NT = triple_count(L);
 
-  // acc += sum over the edge's paths of W[p,u] * CG_p(x, y)
+  // te[l3 block] = sum over the edge's paths into l3 of W[p,u] * CG_p(x, y)
   static __device__ __forceinline__ void edge(const KernelArgs& a, const T (&x)[NL], const T (&y)[NL],
-                                              const T (&w)[NT], T (&acc)[NL]) {
+                                              const T (&w)[NT], T (&te)[NL]) {
     static_for<L + 1>([&](auto I1) {
       constexpr int l1 = I1;
       static_for<L + 1>([&](auto I2) {
@@ -166,9 +194,11 @@ struct Fwd {
                 else
                   z[en.m3] = fmaT(c, p, z[en.m3]);
               });
-              static_for<n3>([&](auto M3) {
-                if constexpr (TI::has_m3(M3)) acc[l3 * l3 + M3] = fmaT(w[t], z[M3], acc[l3 * l3 + M3]);
-              });
+              if (first3<t>(a)) {
+                static_for<n3>([&](auto M3) { te[l3 * l3 + M3] = w[t] * z[M3]; });
+              } else {
+                static_for<n3>([&](auto M3) { te[l3 * l3 + M3] = fmaT(w[t], z[M3], te[l3 * l3 + M3]); });
+              }
             }
           }
         });
@@ -194,8 +224,9 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
   const T* __restrict__ Wp = static_cast<const T*>(a.W);
   T* __restrict__ O = static_cast<T*>(a.out);
 
-  T acc[NL];
-  static_for<NL>([&](auto I) { acc[I] = T(0); });
+  using A = typename RowAcc<T>::type;
+  A acc[NL];
+  static_for<NL>([&](auto I) { acc[I] = A(0); });
 
   const int beg = a.row_ptr[node];
   const int end = a.row_ptr[node + 1];
@@ -221,7 +252,14 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
       if (present<I>(a)) w[I] = ldg_stream(wr + a.woff[I]);
       else w[I] = T(0);
     });
-    F::edge(a, x, y, w, acc);
+    T te[NL];
+    F::edge(a, x, y, w, te);
+    static_for<L + 1>([&](auto I) {
+      constexpr int l = I;
+      if ((a.out_l_mask >> l) & 1) {
+        static_for<2 * l + 1>([&](auto M) { acc[l * l + M] += static_cast<A>(te[l * l + M]); });
+      }
+    });
   }
 
   // sum the slots' partial rows: slots sit at lane offsets 2^lps_log2 .. 32
@@ -234,7 +272,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
       constexpr int l = I;
       const int off = a.out_off[l];
       if (off >= 0) {
-        static_for<2 * l + 1>([&](auto M) { orow[off + u * (2 * l + 1) + M] = acc[l * l + M]; });
+        static_for<2 * l + 1>([&](auto M) { orow[off + u * (2 * l + 1) + M] = static_cast<T>(acc[l * l + M]); });
       }
     });
   }
@@ -250,7 +288,7 @@ struct Bwd {
   // (accumulated over the row) and to dY (summed over channels afterwards).
   template <int NV>
   static __device__ __forceinline__ void edge(const KernelArgs& a, const T (&x)[NL], const T (&y)[NL],
-                                              const T (&g)[NL], const T (&w)[NT], T (&dxa)[NL],
+                                              const T (&g)[NL], const T (&w)[NT], T (&dxe)[NL],
                                               T (&dya)[NV], T (&dw)[NT]) {
     static_assert(NV >= NL, "dY accumulator too short");
     static_for<L + 1>([&](auto I1) {
@@ -281,12 +319,19 @@ struct Bwd {
               });
               T s = T(0);
               static_for<n1>([&](auto M1) {
-                if constexpr (TI::has_m1(M1)) {
-                  s = fmaT(x[l1 * l1 + M1], dxp[M1], s);
-                  dxa[l1 * l1 + M1] = fmaT(w[t], dxp[M1], dxa[l1 * l1 + M1]);
-                }
+                if constexpr (TI::has_m1(M1)) s = fmaT(x[l1 * l1 + M1], dxp[M1], s);
               });
               dw[t] = s;
+              if (first1<t>(a)) {
+                static_for<n1>([&](auto M1) {
+                  if constexpr (TI::has_m1(M1)) dxe[l1 * l1 + M1] = w[t] * dxp[M1];
+                  else dxe[l1 * l1 + M1] = T(0);
+                });
+              } else {
+                static_for<n1>([&](auto M1) {
+                  if constexpr (TI::has_m1(M1)) dxe[l1 * l1 + M1] = fmaT(w[t], dxp[M1], dxe[l1 * l1 + M1]);
+                });
+              }
               static_for<n2>([&](auto M2) {
                 if constexpr (TI::has_m2(M2)) dya[l2 * l2 + M2] = fmaT(w[t], dyp[M2], dya[l2 * l2 + M2]);
               });
@@ -339,8 +384,9 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
       });
     });
   }
-  T dxa[NL];
-  static_for<NL>([&](auto I) { dxa[I] = T(0); });
+  using A = typename RowAcc<T>::type;
+  A dxa[NL];
+  static_for<NL>([&](auto I) { dxa[I] = A(0); });
 
   const int beg = a.row_ptr[node];
   const int end = a.row_ptr[node + 1];
@@ -369,7 +415,14 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
 
     T dya[NV], dw[NT];
     static_for<NV>([&](auto I) { dya[I] = T(0); });
-    B::edge(a, x, y, g, w, dxa, dya, dw);
+    T dxe[NL];
+    B::edge(a, x, y, g, w, dxe, dya, dw);
+    static_for<L + 1>([&](auto I) {
+      constexpr int l = I;
+      if ((a.in_l_mask >> l) & 1) {
+        static_for<2 * l + 1>([&](auto M) { dxa[l * l + M] += static_cast<A>(dxe[l * l + M]); });
+      }
+    });
 
     if (DW != nullptr && chan_ok) {
       T* dwr = DW + (int64_t)e * a.wstride + u;
@@ -423,7 +476,7 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
         constexpr int l = I;
         const int off = a.in_off[l];
         if (off >= 0) {
-          static_for<2 * l + 1>([&](auto M) { drow[off + u * (2 * l + 1) + M] = dxa[l * l + M]; });
+          static_for<2 * l + 1>([&](auto M) { drow[off + u * (2 * l + 1) + M] = static_cast<T>(dxa[l * l + M]); });
         }
       });
     }
