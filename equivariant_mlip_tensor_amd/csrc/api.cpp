@@ -46,28 +46,38 @@ KernelArgs base_args(const Plan& p, int64_t n_rows) {
     a.out_off[l] = p.out_off[l];
   }
   for (int t = 0; t < kMaxTriples; ++t) a.woff[t] = p.woff[t];
-  // first path into each output l and out of each input l, in the kernels'
-  // (l1, l2, l3) loop order
-  int t = 0;
-  bool seen3[kMaxL + 1] = {}, seen1[kMaxL + 1] = {};
+  // first path into each output l in the forward's (l1, l2, l3) loop order,
+  // and first path out of each input l in the backward's (l3, l1, l2) order
   const int L = p.kernel_l;
+  auto on = [&](int t) { return t < 64 ? ((p.pmask_lo >> t) & 1ull) : ((p.pmask_hi >> (t - 64)) & 1ull); };
+  auto set = [](uint64_t& lo, uint64_t& hi, int t) { (t < 64 ? lo : hi) |= 1ull << (t < 64 ? t : t - 64); };
+  bool seen3[kMaxL + 1] = {}, seen1[kMaxL + 1] = {};
   for (int l1 = 0; l1 <= L; ++l1)
     for (int l2 = 0; l2 <= L; ++l2)
       for (int l3 = 0; l3 <= L; ++l3) {
-        if (!cg::triangle(l1, l2, l3)) continue;
-        const bool on = t < 64 ? ((p.pmask_lo >> t) & 1ull) : ((p.pmask_hi >> (t - 64)) & 1ull);
-        if (on) {
-          uint64_t& f3 = t < 64 ? a.first3_lo : a.first3_hi;
-          uint64_t& f1 = t < 64 ? a.first1_lo : a.first1_hi;
-          const uint64_t bit = 1ull << (t < 64 ? t : t - 64);
-          if (!seen3[l3]) f3 |= bit;
-          if (!seen1[l1]) f1 |= bit;
-          seen3[l3] = seen1[l1] = true;
-          a.out_l_mask |= 1 << l3;
-          a.in_l_mask |= 1 << l1;
-        }
-        ++t;
+        const int t = triple_id(L, l1, l2, l3);
+        if (t < 0 || !on(t)) continue;
+        if (!seen3[l3]) set(a.first3_lo, a.first3_hi, t);
+        seen3[l3] = true;
+        a.out_l_mask |= 1 << l3;
+        a.in_l_mask |= 1 << l1;
       }
+  for (int l3 = 0; l3 <= L; ++l3)
+    for (int l1 = 0; l1 <= L; ++l1)
+      for (int l2 = 0; l2 <= L; ++l2) {
+        const int t = triple_id(L, l1, l2, l3);
+        if (t < 0 || !on(t)) continue;
+        if (!seen1[l1]) set(a.first1_lo, a.first1_hi, t);
+        seen1[l1] = true;
+      }
+  // the compile-time ("full") kernels cover plans whose segments are l = 0..L
+  // in order with natural parity on both sides and SH up to the same L
+  bool full = p.sh_lmax == L && static_cast<int>(p.in.size()) == L + 1 && static_cast<int>(p.out.size()) == L + 1;
+  for (int l = 0; full && l <= L; ++l) {
+    const int par = (l % 2 == 0) ? 1 : -1;
+    full = p.in[l].l == l && p.out[l].l == l && p.in[l].p == par && p.out[l].p == par;
+  }
+  a.full_plan = full ? 1 : 0;
   return a;
 }
 

@@ -51,12 +51,15 @@ struct KernelArgs {
   int64_t wstride;      // weight_numel
   uint64_t pmask_lo;    // bit t: triple t is a path of the plan (t < 64)
   uint64_t pmask_hi;    // bit t-64
-  uint64_t first3_lo;   // bit t: path t is the first path (in triple order) into its output l
+  uint64_t first3_lo;   // bit t: path t is the first path (in (l1, l2, l3) order) into its output l
   uint64_t first3_hi;
-  uint64_t first1_lo;   // bit t: path t is the first path (in triple order) out of its input l
+  uint64_t first1_lo;   // bit t: path t is the first path (in (l3, l1, l2) order) out of its input l
   uint64_t first1_hi;
   int32_t out_l_mask;   // bit l: some path writes output l
   int32_t in_l_mask;    // bit l: some path reads input l
+  int32_t full_plan;    // 1: segments l = 0..L in order with parity (-1)^l in and out, SH l <= L,
+                        //    so the plan holds every even-sum triple in triple order
+  int32_t pad1;
   const int32_t* row_ptr;
   const int32_t* col;
   const int32_t* eid;

@@ -19,6 +19,12 @@
 //    products x[m1]*Y[m2] are formed once per (l1, l2) group and shared by
 //    all paths of the group (path aggregation, FlashTP "Approach" and its
 //    measured-effects table).
+//
+// Two plan policies instantiate the same code: FullPlan<L, U> for plans whose
+// segments are l = 0..L in order with natural parity (every offset, path and
+// lane mapping a compile-time constant, no branch inside an edge), and
+// RtPlan<L, PAR> for any other plan (path set, offsets and U read from the
+// launch arguments, one uniform branch per path).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -45,12 +51,184 @@ __device__ __forceinline__ void static_for(F&& f) {
 __device__ __forceinline__ float fmaT(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
 __device__ __forceinline__ double fmaT(double a, double b, double c) { return __builtin_fma(a, b, c); }
 
-// Path parity classes a kernel is specialised for.
+template <typename T>
+__device__ __forceinline__ T ldg_stream(const T* p) {
+  return __builtin_nontemporal_load(p);
+}
+
+// Row accumulators: a row sums one term per edge, so for fp32 data it is
+// kept in fp64 (full rate on CDNA); each edge's own sum over its paths stays
+// in the data type.
+template <typename T>
+struct RowAcc {
+  using type = T;
+};
+template <>
+struct RowAcc<float> {
+  using type = double;
+};
+
 enum Parity { kAnyParity = 0, kEvenOnly = 1 };
 
 constexpr bool triple_in_class(int l1, int l2, int l3, int par) {
   return par == kAnyParity || ((l1 + l2 + l3) % 2 == 0);
 }
+
+constexpr int log2_ceil(int n) {
+  int k = 0;
+  while ((1 << k) < n) ++k;
+  return k;
+}
+
+// ----------------------------------------------------- triple bookkeeping
+struct TripleInfo {
+  int l1 = -1, l2 = -1, l3 = -1;
+};
+
+constexpr TripleInfo triple_at(int L, int t) {
+  int n = 0;
+  for (int a = 0; a <= L; ++a)
+    for (int b = 0; b <= L; ++b)
+      for (int c = 0; c <= L; ++c)
+        if (cg::triangle(a, b, c)) {
+          if (n == t) return TripleInfo{a, b, c};
+          ++n;
+        }
+  return TripleInfo{};
+}
+
+constexpr bool triple_even(int L, int t) {
+  const TripleInfo i = triple_at(L, t);
+  return ((i.l1 + i.l2 + i.l3) % 2) == 0;
+}
+
+// rank of triple t among the even triples (its path index in a full plan)
+constexpr int even_rank(int L, int t) {
+  int r = 0;
+  for (int s = 0; s < t; ++s)
+    if (triple_even(L, s)) ++r;
+  return r;
+}
+
+constexpr int even_count(int L) { return even_rank(L, triple_count(L)); }
+
+constexpr bool even_first3(int L, int t) {
+  const int l3 = triple_at(L, t).l3;
+  for (int s = 0; s < t; ++s)
+    if (triple_even(L, s) && triple_at(L, s).l3 == l3) return false;
+  return true;
+}
+
+// Backward visits paths in (l3, l1, l2) order, so the products |c| * G[m3]
+// shared by paths into the same l3 stay inside one block of code.
+constexpr int bwd_pos(int L, int l1, int l2, int l3) { return (l3 * (L + 1) + l1) * (L + 1) + l2; }
+
+constexpr bool even_first1_bwd(int L, int t) {
+  const TripleInfo me = triple_at(L, t);
+  const int pos = bwd_pos(L, me.l1, me.l2, me.l3);
+  for (int s = 0; s < triple_count(L); ++s) {
+    const TripleInfo o = triple_at(L, s);
+    if (triple_even(L, s) && o.l1 == me.l1 && bwd_pos(L, o.l1, o.l2, o.l3) < pos) return false;
+  }
+  return true;
+}
+
+__device__ __forceinline__ bool bit(uint64_t lo, uint64_t hi, int t) {
+  return t < 64 ? ((lo >> t) & 1ull) : ((hi >> (t - 64)) & 1ull);
+}
+
+// ------------------------------------------------------------- policies
+template <int L, int PAR>
+struct RtPlan {
+  static constexpr int kPar = PAR;
+  static __device__ __forceinline__ int lps_log2(const KernelArgs& a) { return a.lps_log2; }
+  static __device__ __forceinline__ int nslots(const KernelArgs& a) { return a.nslots; }
+  static __device__ __forceinline__ int mul(const KernelArgs& a) { return a.mul; }
+  static __device__ __forceinline__ int d_in(const KernelArgs& a) { return a.d_in; }
+  static __device__ __forceinline__ int d_out(const KernelArgs& a) { return a.d_out; }
+  static __device__ __forceinline__ int d_sh(const KernelArgs& a) { return a.d_sh; }
+  static __device__ __forceinline__ int64_t wstride(const KernelArgs& a) { return a.wstride; }
+  static __device__ __forceinline__ int in_off(const KernelArgs& a, int l) { return a.in_off[l]; }
+  static __device__ __forceinline__ int out_off(const KernelArgs& a, int l) { return a.out_off[l]; }
+  static __device__ __forceinline__ bool in_l(const KernelArgs& a, int l) { return (a.in_l_mask >> l) & 1; }
+  static __device__ __forceinline__ bool out_l(const KernelArgs& a, int l) { return (a.out_l_mask >> l) & 1; }
+  template <int t>
+  static __device__ __forceinline__ bool on(const KernelArgs& a) {
+    return bit(a.pmask_lo, a.pmask_hi, t);
+  }
+  template <int t>
+  static __device__ __forceinline__ bool first3(const KernelArgs& a) {
+    return bit(a.first3_lo, a.first3_hi, t);
+  }
+  template <int t>
+  static __device__ __forceinline__ bool first1(const KernelArgs& a) {
+    return bit(a.first1_lo, a.first1_hi, t);
+  }
+  template <int t>
+  static __device__ __forceinline__ int woff(const KernelArgs& a) {
+    return a.woff[t];
+  }
+  // guard of a path's arithmetic
+  template <int t>
+  static __device__ __forceinline__ bool run(const KernelArgs& a, int) {
+    return on<t>(a);
+  }
+};
+
+template <int L, int U>
+struct FullPlan {
+  static_assert(U >= 1 && U <= 64, "one wave holds at most 64 channels");
+  static constexpr int kPar = kEvenOnly;
+  static constexpr int kLg = log2_ceil(U);
+  static constexpr int kD = U * (L + 1) * (L + 1);
+  static __device__ __forceinline__ constexpr int lps_log2(const KernelArgs&) { return kLg; }
+  static __device__ __forceinline__ constexpr int nslots(const KernelArgs&) { return 64 >> kLg; }
+  static __device__ __forceinline__ constexpr int mul(const KernelArgs&) { return U; }
+  static __device__ __forceinline__ constexpr int d_in(const KernelArgs&) { return kD; }
+  static __device__ __forceinline__ constexpr int d_out(const KernelArgs&) { return kD; }
+  static __device__ __forceinline__ constexpr int d_sh(const KernelArgs&) { return (L + 1) * (L + 1); }
+  static __device__ __forceinline__ constexpr int64_t wstride(const KernelArgs&) {
+    constexpr int64_t v = int64_t(U) * even_count(L);
+    return v;
+  }
+  static __device__ __forceinline__ constexpr int in_off(const KernelArgs&, int l) { return U * l * l; }
+  static __device__ __forceinline__ constexpr int out_off(const KernelArgs&, int l) { return U * l * l; }
+  static __device__ __forceinline__ constexpr bool in_l(const KernelArgs&, int) { return true; }
+  static __device__ __forceinline__ constexpr bool out_l(const KernelArgs&, int) { return true; }
+  // constexpr locals force compile-time evaluation of the helpers
+  template <int t>
+  static __device__ __forceinline__ constexpr bool on(const KernelArgs&) {
+    constexpr bool v = triple_even(L, t);
+    return v;
+  }
+  template <int t>
+  static __device__ __forceinline__ constexpr bool first3(const KernelArgs&) {
+    constexpr bool v = even_first3(L, t);
+    return v;
+  }
+  template <int t>
+  static __device__ __forceinline__ constexpr bool first1(const KernelArgs&) {
+    constexpr bool v = even_first1_bwd(L, t);
+    return v;
+  }
+  template <int t>
+  static __device__ __forceinline__ constexpr int woff(const KernelArgs&) {
+    constexpr int v = even_rank(L, t) * U;
+    return v;
+  }
+  // Guard of a path's arithmetic: `tok` is the wave's first edge id of this
+  // iteration, never negative, but unknown to the compiler, different in
+  // every iteration and copied through a scalar move per path, so every path
+  // stays its own basic block.  Without these block boundaries the compiler
+  // schedules the whole edge as one block, hoists products across paths and
+  // runs out of registers.
+  template <int t>
+  static __device__ __forceinline__ bool run(const KernelArgs&, int tok) {
+    int v;
+    asm volatile("s_mov_b32 %0, %1" : "=s"(v) : "s"(tok));  // opaque per path: no merging of guards
+    return v >= 0;
+  }
+};
 
 // Compile-time facts about a CG table.
 template <int L1, int L2, int L3>
@@ -104,84 +282,44 @@ constexpr bool group_uses(int m1, int m2) {
   }
 }
 
-template <int T>
-__device__ __forceinline__ bool present(const KernelArgs& a) {
-  if constexpr (T < 64)
-    return (a.pmask_lo >> T) & 1ull;
-  else
-    return (a.pmask_hi >> (T - 64)) & 1ull;
-}
-
-template <int T>
-__device__ __forceinline__ bool first3(const KernelArgs& a) {
-  if constexpr (T < 64)
-    return (a.first3_lo >> T) & 1ull;
-  else
-    return (a.first3_hi >> (T - 64)) & 1ull;
-}
-
-template <int T>
-__device__ __forceinline__ bool first1(const KernelArgs& a) {
-  if constexpr (T < 64)
-    return (a.first1_lo >> T) & 1ull;
-  else
-    return (a.first1_hi >> (T - 64)) & 1ull;
-}
-
-// Row accumulators: a row sums one term per edge, so for fp32 data it is
-// kept in fp64 (full rate on CDNA); each edge's own sum over its paths stays
-// in the data type.
-template <typename T>
-struct RowAcc {
-  using type = T;
-};
-template <>
-struct RowAcc<float> {
-  using type = double;
-};
-
-template <int L, int PAR, int L1, int L2>
-__device__ __forceinline__ bool group_present(const KernelArgs& a) {
+template <int L, class P, int L1, int L2>
+__device__ __forceinline__ bool group_on(const KernelArgs& a) {
   bool any = false;
   static_for<L + 1>([&](auto I3) {
     constexpr int l3 = I3;
-    if constexpr (cg::triangle(L1, L2, l3) && triple_in_class(L1, L2, l3, PAR))
-      any = any || present<triple_id(L, L1, L2, l3)>(a);
+    if constexpr (cg::triangle(L1, L2, l3) && triple_in_class(L1, L2, l3, P::kPar))
+      any = any || P::template on<triple_id(L, L1, L2, l3)>(a);
   });
   return any;
 }
 
-template <typename T>
-__device__ __forceinline__ T ldg_stream(const T* p) {
-  return __builtin_nontemporal_load(p);
-}
-
 // ------------------------------------------------------------------ forward
-template <typename T, int L, int PAR>
+template <typename T, int L, class P>
 struct Fwd {
   static constexpr int NL = (L + 1) * (L + 1);
   static constexpr int NT = triple_count(L);
 
   // te[l3 block] = sum over the edge's paths into l3 of W[p,u] * CG_p(x, y)
-  static __device__ __forceinline__ void edge(const KernelArgs& a, const T (&x)[NL], const T (&y)[NL],
+  static __device__ __forceinline__ void edge(const KernelArgs& a, int tok, const T (&x)[NL], const T (&y)[NL],
                                               const T (&w)[NT], T (&te)[NL]) {
     static_for<L + 1>([&](auto I1) {
       constexpr int l1 = I1;
       static_for<L + 1>([&](auto I2) {
         constexpr int l2 = I2;
-        if (!group_present<L, PAR, l1, l2>(a)) return;
+        if (!group_on<L, P, l1, l2>(a)) return;
         constexpr int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1;
         T pr[n1 * n2];
         static_for<n1>([&](auto M1) {
           static_for<n2>([&](auto M2) {
-            if constexpr (group_uses<L, PAR, l1, l2>(M1, M2)) pr[M1 * n2 + M2] = x[l1 * l1 + M1] * y[l2 * l2 + M2];
+            if constexpr (group_uses<L, P::kPar, l1, l2>(M1, M2))
+              pr[M1 * n2 + M2] = x[l1 * l1 + M1] * y[l2 * l2 + M2];
           });
         });
         static_for<L + 1>([&](auto I3) {
           constexpr int l3 = I3;
-          if constexpr (cg::triangle(l1, l2, l3) && triple_in_class(l1, l2, l3, PAR)) {
+          if constexpr (cg::triangle(l1, l2, l3) && triple_in_class(l1, l2, l3, P::kPar)) {
             constexpr int t = triple_id(L, l1, l2, l3);
-            if (present<t>(a)) {
+            if (P::template on<t>(a) && P::template run<t>(a, tok)) {
               using TI = TabInfo<l1, l2, l3>;
               constexpr int n3 = 2 * l3 + 1;
               T z[n3];
@@ -194,7 +332,7 @@ struct Fwd {
                 else
                   z[en.m3] = fmaT(c, p, z[en.m3]);
               });
-              if (first3<t>(a)) {
+              if (P::template first3<t>(a)) {
                 static_for<n3>([&](auto M3) { te[l3 * l3 + M3] = w[t] * z[M3]; });
               } else {
                 static_for<n3>([&](auto M3) { te[l3 * l3 + M3] = fmaT(w[t], z[M3], te[l3 * l3 + M3]); });
@@ -207,70 +345,79 @@ struct Fwd {
   }
 };
 
-template <typename T, int L, int PAR>
+template <typename T, int L, class P>
 __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
-  using F = Fwd<T, L, PAR>;
+  using F = Fwd<T, L, P>;
+  using A = typename RowAcc<T>::type;
   constexpr int NL = F::NL, NT = F::NT;
   const int lane = threadIdx.x & 63;
   const int node = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (node >= a.n_rows) return;  // wave-uniform
-  const int slot = lane >> a.lps_log2;
-  const int u = lane & ((1 << a.lps_log2) - 1);
-  const bool chan_ok = u < a.mul;
-  const int uc = chan_ok ? u : 0;  // inactive lanes read channel 0 (valid addresses), never store
+  const int lg = P::lps_log2(a);
+  const int slot = lane >> lg;
+  const int u = lane & ((1 << lg) - 1);
+  const bool chan_ok = u < P::mul(a);
+  const int uc = chan_ok ? u : 0;  // idle lanes read channel 0 (valid addresses) and never store
 
   const T* __restrict__ X = static_cast<const T*>(a.x);
   const T* __restrict__ Yp = static_cast<const T*>(a.Y);
   const T* __restrict__ Wp = static_cast<const T*>(a.W);
   T* __restrict__ O = static_cast<T*>(a.out);
+  const int d_in = P::d_in(a), d_sh = P::d_sh(a);
+  const int64_t wstride = P::wstride(a);
 
-  using A = typename RowAcc<T>::type;
   A acc[NL];
   static_for<NL>([&](auto I) { acc[I] = A(0); });
 
   const int beg = a.row_ptr[node];
   const int end = a.row_ptr[node + 1];
-  for (int k = beg + slot; k < end; k += a.nslots) {
+  for (int k = beg + slot; k < end; k += P::nslots(a)) {
     const int e = a.eid[k];
     const int j = a.col[k];
     T x[NL], y[NL], w[NT];
-    const T* xr = X + (int64_t)j * a.d_in;
+    const T* xr = X + (int64_t)j * d_in;
     static_for<L + 1>([&](auto I) {
       constexpr int l = I;
-      const int off = a.in_off[l];
+      const int off = P::in_off(a, l);
       static_for<2 * l + 1>([&](auto M) {
-        x[l * l + M] = off >= 0 ? xr[off + uc * (2 * l + 1) + M] : T(0);
+        if (off >= 0) x[l * l + M] = xr[off + uc * (2 * l + 1) + M];
+        else x[l * l + M] = T(0);
       });
     });
-    const T* yr = Yp + (int64_t)e * a.d_sh;
+    const T* yr = Yp + (int64_t)e * d_sh;
     static_for<NL>([&](auto I) {
-      if (I < a.d_sh) y[I] = ldg_stream(yr + I);
+      if (I < d_sh) y[I] = ldg_stream(yr + I);
       else y[I] = T(0);
     });
-    const T* wr = Wp + (int64_t)e * a.wstride + uc;
+    const T* wr = Wp + (int64_t)e * wstride + uc;
     static_for<NT>([&](auto I) {
-      if (present<I>(a)) w[I] = ldg_stream(wr + a.woff[I]);
-      else w[I] = T(0);
+      constexpr TripleInfo ti = triple_at(L, I);
+      if constexpr (triple_in_class(ti.l1, ti.l2, ti.l3, P::kPar)) {
+        if (P::template on<I>(a)) w[I] = ldg_stream(wr + P::template woff<I>(a));
+        else w[I] = T(0);
+      } else {
+        w[I] = T(0);
+      }
     });
     T te[NL];
-    F::edge(a, x, y, w, te);
+    F::edge(a, __builtin_amdgcn_readfirstlane(e), x, y, w, te);
     static_for<L + 1>([&](auto I) {
       constexpr int l = I;
-      if ((a.out_l_mask >> l) & 1) {
+      if (P::out_l(a, l)) {
         static_for<2 * l + 1>([&](auto M) { acc[l * l + M] += static_cast<A>(te[l * l + M]); });
       }
     });
   }
 
-  // sum the slots' partial rows: slots sit at lane offsets 2^lps_log2 .. 32
-  for (int off = 1 << a.lps_log2; off < 64; off <<= 1) {
+  // sum the slots' partial rows: slots sit at lane offsets 2^lg .. 32
+  for (int off = 1 << lg; off < 64; off <<= 1) {
     static_for<NL>([&](auto I) { acc[I] += __shfl_xor(acc[I], off, 64); });
   }
   if (slot == 0 && chan_ok) {
-    T* orow = O + (int64_t)node * a.d_out;
+    T* orow = O + (int64_t)node * P::d_out(a);
     static_for<L + 1>([&](auto I) {
       constexpr int l = I;
-      const int off = a.out_off[l];
+      const int off = P::out_off(a, l);
       if (off >= 0) {
         static_for<2 * l + 1>([&](auto M) { orow[off + u * (2 * l + 1) + M] = static_cast<T>(acc[l * l + M]); });
       }
@@ -279,27 +426,28 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
 }
 
 // ----------------------------------------------------------------- backward
-template <typename T, int L, int PAR>
+template <typename T, int L, class P>
 struct Bwd {
   static constexpr int NL = (L + 1) * (L + 1);
   static constexpr int NT = triple_count(L);
 
-  // One edge: dW for every path (unreduced), and per-lane contributions to dx
-  // (accumulated over the row) and to dY (summed over channels afterwards).
+  // One edge: dW for every path, the edge's contribution dxe to dx (summed
+  // over its paths), and per-lane contributions to dY (summed over channels
+  // afterwards).
   template <int NV>
-  static __device__ __forceinline__ void edge(const KernelArgs& a, const T (&x)[NL], const T (&y)[NL],
+  static __device__ __forceinline__ void edge(const KernelArgs& a, int tok, const T (&x)[NL], const T (&y)[NL],
                                               const T (&g)[NL], const T (&w)[NT], T (&dxe)[NL],
-                                              T (&dya)[NV], T (&dw)[NT]) {
+                                              T (&dya)[NV], bool store_dw, T* dwr) {
     static_assert(NV >= NL, "dY accumulator too short");
-    static_for<L + 1>([&](auto I1) {
-      constexpr int l1 = I1;
-      static_for<L + 1>([&](auto I2) {
-        constexpr int l2 = I2;
-        static_for<L + 1>([&](auto I3) {
-          constexpr int l3 = I3;
-          if constexpr (cg::triangle(l1, l2, l3) && triple_in_class(l1, l2, l3, PAR)) {
+    static_for<L + 1>([&](auto I3) {
+      constexpr int l3 = I3;
+      static_for<L + 1>([&](auto I1) {
+        constexpr int l1 = I1;
+        static_for<L + 1>([&](auto I2) {
+          constexpr int l2 = I2;
+          if constexpr (cg::triangle(l1, l2, l3) && triple_in_class(l1, l2, l3, P::kPar)) {
             constexpr int t = triple_id(L, l1, l2, l3);
-            if (present<t>(a)) {
+            if (P::template on<t>(a) && P::template run<t>(a, tok)) {
               using TI = TabInfo<l1, l2, l3>;
               constexpr int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1;
               T dxp[n1], dyp[n2];
@@ -321,11 +469,13 @@ struct Bwd {
               static_for<n1>([&](auto M1) {
                 if constexpr (TI::has_m1(M1)) s = fmaT(x[l1 * l1 + M1], dxp[M1], s);
               });
-              dw[t] = s;
-              if (first1<t>(a)) {
+              if (store_dw) __builtin_nontemporal_store(s, dwr + P::template woff<t>(a));
+              if (P::template first1<t>(a)) {
                 static_for<n1>([&](auto M1) {
-                  if constexpr (TI::has_m1(M1)) dxe[l1 * l1 + M1] = w[t] * dxp[M1];
-                  else dxe[l1 * l1 + M1] = T(0);
+                  if constexpr (TI::has_m1(M1))
+                    dxe[l1 * l1 + M1] = w[t] * dxp[M1];
+                  else
+                    dxe[l1 * l1 + M1] = T(0);
                 });
               } else {
                 static_for<n1>([&](auto M1) {
@@ -349,18 +499,20 @@ constexpr int pow2_ceil(int n) {
   return p;
 }
 
-template <typename T, int L, int PAR>
+template <typename T, int L, class P>
 __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
-  using B = Bwd<T, L, PAR>;
+  using B = Bwd<T, L, P>;
+  using A = typename RowAcc<T>::type;
   constexpr int NL = B::NL, NT = B::NT;
   constexpr int NV = pow2_ceil(NL);  // dY values, padded to a power of two for the reduce-scatter
   const int lane = threadIdx.x & 63;
   const int node = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (node >= a.n_rows) return;  // wave-uniform
-  const int lps = 1 << a.lps_log2;
-  const int slot = lane >> a.lps_log2;
+  const int lg = P::lps_log2(a);
+  const int lps = 1 << lg;
+  const int slot = lane >> lg;
   const int u = lane & (lps - 1);
-  const bool chan_ok = u < a.mul;
+  const bool chan_ok = u < P::mul(a);
   const int uc = chan_ok ? u : 0;
 
   const T* __restrict__ X = static_cast<const T*>(a.x);
@@ -370,66 +522,71 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
   T* __restrict__ DX = static_cast<T*>(a.out);
   T* __restrict__ DY = static_cast<T*>(a.dY);
   T* __restrict__ DW = static_cast<T*>(a.dW);
+  const int d_out = P::d_out(a), d_sh = P::d_sh(a);
+  const int64_t wstride = P::wstride(a);
 
-  // this source node's features stay in registers for the whole row; lanes
-  // beyond U hold zeros so they add nothing to the channel sums of dY
+  // this source node's features stay in registers for the whole row; idle
+  // lanes hold zeros so they add nothing to the channel sums of dY
   T x[NL];
   {
-    const T* xr = X + (int64_t)node * a.d_in;
+    const T* xr = X + (int64_t)node * P::d_in(a);
     static_for<L + 1>([&](auto I) {
       constexpr int l = I;
-      const int off = a.in_off[l];
+      const int off = P::in_off(a, l);
       static_for<2 * l + 1>([&](auto M) {
-        x[l * l + M] = (off >= 0 && chan_ok) ? xr[off + u * (2 * l + 1) + M] : T(0);
+        if (off >= 0 && chan_ok) x[l * l + M] = xr[off + u * (2 * l + 1) + M];
+        else x[l * l + M] = T(0);
       });
     });
   }
-  using A = typename RowAcc<T>::type;
   A dxa[NL];
   static_for<NL>([&](auto I) { dxa[I] = A(0); });
 
   const int beg = a.row_ptr[node];
   const int end = a.row_ptr[node + 1];
-  for (int k = beg + slot; k < end; k += a.nslots) {
+  for (int k = beg + slot; k < end; k += P::nslots(a)) {
     const int e = a.eid[k];
     const int i = a.col[k];
     T g[NL], y[NL], w[NT];
-    const T* gr = Gp + (int64_t)i * a.d_out;
+    const T* gr = Gp + (int64_t)i * d_out;
     static_for<L + 1>([&](auto I) {
       constexpr int l = I;
-      const int off = a.out_off[l];
+      const int off = P::out_off(a, l);
       static_for<2 * l + 1>([&](auto M) {
-        g[l * l + M] = off >= 0 ? gr[off + uc * (2 * l + 1) + M] : T(0);
+        if (off >= 0) g[l * l + M] = gr[off + uc * (2 * l + 1) + M];
+        else g[l * l + M] = T(0);
       });
     });
-    const T* yr = Yp + (int64_t)e * a.d_sh;
+    const T* yr = Yp + (int64_t)e * d_sh;
     static_for<NL>([&](auto I) {
-      if (I < a.d_sh) y[I] = ldg_stream(yr + I);
+      if (I < d_sh) y[I] = ldg_stream(yr + I);
       else y[I] = T(0);
     });
-    const T* wr = Wp + (int64_t)e * a.wstride + uc;
+    const T* wr = Wp + (int64_t)e * wstride + uc;
     static_for<NT>([&](auto I) {
-      if (present<I>(a)) w[I] = ldg_stream(wr + a.woff[I]);
-      else w[I] = T(0);
+      constexpr TripleInfo ti = triple_at(L, I);
+      if constexpr (triple_in_class(ti.l1, ti.l2, ti.l3, P::kPar)) {
+        if (P::template on<I>(a)) w[I] = ldg_stream(wr + P::template woff<I>(a));
+        else w[I] = T(0);
+      } else {
+        w[I] = T(0);
+      }
     });
 
-    T dya[NV], dw[NT];
+    T dya[NV], dxe[NL];
     static_for<NV>([&](auto I) { dya[I] = T(0); });
-    T dxe[NL];
-    B::edge(a, x, y, g, w, dxe, dya, dw);
+    // idle lanes (u >= U) aim their dW stores at channel 0 of the same row
+    // and store only when chan_ok; for a power-of-two U every lane is active
+    const bool store_dw = DW != nullptr;
+    T* dwr = store_dw ? DW + (int64_t)e * wstride + uc : nullptr;
+    B::edge(a, __builtin_amdgcn_readfirstlane(e), x, y, g, w, dxe, dya, store_dw && chan_ok, dwr);
     static_for<L + 1>([&](auto I) {
       constexpr int l = I;
-      if ((a.in_l_mask >> l) & 1) {
+      if (P::in_l(a, l)) {
         static_for<2 * l + 1>([&](auto M) { dxa[l * l + M] += static_cast<A>(dxe[l * l + M]); });
       }
     });
 
-    if (DW != nullptr && chan_ok) {
-      T* dwr = DW + (int64_t)e * a.wstride + u;
-      static_for<NT>([&](auto I) {
-        if (present<I>(a)) __builtin_nontemporal_store(dw[I], dwr + a.woff[I]);
-      });
-    }
     if (DY != nullptr) {
       // reduce-scatter of the NV dY values over the slot's lanes.  Step s
       // pairs lanes across bit b = lps >> (s+1); while more than one value is
@@ -458,9 +615,9 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
       // bits below lps/NV were plain sums: one lane of each such group stores
       const int plain_mask = lps > NV ? lps / NV - 1 : 0;
       if ((u & plain_mask) == 0) {
-        T* dyr = DY + (int64_t)e * a.d_sh;
+        T* dyr = DY + (int64_t)e * d_sh;
         static_for<NV>([&](auto V) {
-          if (V < nv && base + V < a.d_sh) dyr[base + V] = dya[V];
+          if (V < nv && base + V < d_sh) dyr[base + V] = dya[V];
         });
       }
     }
@@ -471,10 +628,10 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
       static_for<NL>([&](auto I) { dxa[I] += __shfl_xor(dxa[I], off, 64); });
     }
     if (slot == 0 && chan_ok) {
-      T* drow = DX + (int64_t)node * a.d_in;
+      T* drow = DX + (int64_t)node * P::d_in(a);
       static_for<L + 1>([&](auto I) {
         constexpr int l = I;
-        const int off = a.in_off[l];
+        const int off = P::in_off(a, l);
         if (off >= 0) {
           static_for<2 * l + 1>([&](auto M) { drow[off + u * (2 * l + 1) + M] = static_cast<T>(dxa[l * l + M]); });
         }
@@ -483,21 +640,22 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
   }
 }
 
-template <typename T, int PAR>
+// ---------------------------------------------------------------- launchers
+template <typename T, class P>
 hipError_t launch_fwd(const KernelArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
   const int waves_per_block = 4;
   const int blocks = (a.n_rows + waves_per_block - 1) / waves_per_block;
-  hipLaunchKernelGGL((fwd_kernel<T, TPCONV_L, PAR>), dim3(blocks), dim3(64 * waves_per_block), 0, s, a);
+  hipLaunchKernelGGL((fwd_kernel<T, TPCONV_L, P>), dim3(blocks), dim3(64 * waves_per_block), 0, s, a);
   return hipGetLastError();
 }
 
-template <typename T, int PAR>
+template <typename T, class P>
 hipError_t launch_bwd(const KernelArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
   const int waves_per_block = 4;
   const int blocks = (a.n_rows + waves_per_block - 1) / waves_per_block;
-  hipLaunchKernelGGL((bwd_kernel<T, TPCONV_L, PAR>), dim3(blocks), dim3(64 * waves_per_block), 0, s, a);
+  hipLaunchKernelGGL((bwd_kernel<T, TPCONV_L, P>), dim3(blocks), dim3(64 * waves_per_block), 0, s, a);
   return hipGetLastError();
 }
 
@@ -507,7 +665,7 @@ bool all_even(const KernelArgs& a) {
   int t = 0;
   for (int l1 = 0; l1 <= L; ++l1)
     for (int l2 = 0; l2 <= L; ++l2)
-      for (int l3 = 0; l3<= L; ++l3)
+      for (int l3 = 0; l3 <= L; ++l3)
         if (cg::triangle(l1, l2, l3)) {
           const bool on = t < 64 ? ((a.pmask_lo >> t) & 1ull) : ((a.pmask_hi >> (t - 64)) & 1ull);
           if (on && (l1 + l2 + l3) % 2) even = false;
@@ -516,23 +674,42 @@ bool all_even(const KernelArgs& a) {
   return even;
 }
 
+// multiplicities with a compile-time kernel for full plans
+template <int... Us>
+struct UList {};
+using FullMuls = UList<16, 32, 64>;
+
+template <typename T, bool FWD, int U0, int... Us>
+bool launch_full(const KernelArgs& a, hipStream_t s, hipError_t& err, UList<U0, Us...>) {
+  if (a.mul == U0) {
+    err = FWD ? launch_fwd<T, FullPlan<TPCONV_L, U0>>(a, s) : launch_bwd<T, FullPlan<TPCONV_L, U0>>(a, s);
+    return true;
+  }
+  if constexpr (sizeof...(Us) > 0) {
+    return launch_full<T, FWD, Us...>(a, s, err, UList<Us...>{});
+  } else {
+    return false;
+  }
+}
+
+template <typename T, bool FWD>
+hipError_t dispatch(const KernelArgs& a, hipStream_t s) {
+  hipError_t err = hipSuccess;
+  if (a.full_plan && launch_full<T, FWD>(a, s, err, FullMuls{})) return err;
+  if (all_even(a))
+    return FWD ? launch_fwd<T, RtPlan<TPCONV_L, kEvenOnly>>(a, s) : launch_bwd<T, RtPlan<TPCONV_L, kEvenOnly>>(a, s);
+  return FWD ? launch_fwd<T, RtPlan<TPCONV_L, kAnyParity>>(a, s) : launch_bwd<T, RtPlan<TPCONV_L, kAnyParity>>(a, s);
+}
+
 }  // namespace
 
 #define TPCONV_CAT2(a, b) a##b
 #define TPCONV_CAT(a, b) TPCONV_CAT2(a, b)
 #define TPCONV_LNAME(stem, ty) TPCONV_CAT(TPCONV_CAT(stem, TPCONV_L), ty)
 
-hipError_t TPCONV_LNAME(launch_fwd_l, _f32)(const KernelArgs& a, hipStream_t s) {
-  return all_even(a) ? launch_fwd<float, kEvenOnly>(a, s) : launch_fwd<float, kAnyParity>(a, s);
-}
-hipError_t TPCONV_LNAME(launch_fwd_l, _f64)(const KernelArgs& a, hipStream_t s) {
-  return all_even(a) ? launch_fwd<double, kEvenOnly>(a, s) : launch_fwd<double, kAnyParity>(a, s);
-}
-hipError_t TPCONV_LNAME(launch_bwd_l, _f32)(const KernelArgs& a, hipStream_t s) {
-  return all_even(a) ? launch_bwd<float, kEvenOnly>(a, s) : launch_bwd<float, kAnyParity>(a, s);
-}
-hipError_t TPCONV_LNAME(launch_bwd_l, _f64)(const KernelArgs& a, hipStream_t s) {
-  return all_even(a) ? launch_bwd<double, kEvenOnly>(a, s) : launch_bwd<double, kAnyParity>(a, s);
-}
+hipError_t TPCONV_LNAME(launch_fwd_l, _f32)(const KernelArgs& a, hipStream_t s) { return dispatch<float, true>(a, s); }
+hipError_t TPCONV_LNAME(launch_fwd_l, _f64)(const KernelArgs& a, hipStream_t s) { return dispatch<double, true>(a, s); }
+hipError_t TPCONV_LNAME(launch_bwd_l, _f32)(const KernelArgs& a, hipStream_t s) { return dispatch<float, false>(a, s); }
+hipError_t TPCONV_LNAME(launch_bwd_l, _f64)(const KernelArgs& a, hipStream_t s) { return dispatch<double, false>(a, s); }
 
 }  // namespace tpconv
