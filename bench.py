@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--workload", default="c4k")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-edges", type=int, default=40000)
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="also run one plain device copy of this many MiB (scales rocprofv3 FETCH/WRITE_SIZE)")
     return p.parse_args()
 
 
@@ -118,6 +120,14 @@ def main():
     def step():
         tp.tpconv_forward(plan, graph, x, Y, W, out)
         tp.tpconv_backward(plan, graph, x, Y, W, G, dx, dY, dW)
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * 2**20 // 4
+        a_src = torch.ones(n, dtype=torch.float32, device=dev)
+        a_dst = torch.empty_like(a_src)
+        a_dst.copy_(a_src)
+        torch.cuda.synchronize()
+        del a_src, a_dst
 
     for _ in range(args.warmup):
         step()

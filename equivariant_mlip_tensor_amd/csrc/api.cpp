@@ -106,6 +106,7 @@ extern "C" tpconv_status tpconv_forward(tpconv_plan_t hp, tpconv_graph_t hg, con
   a.row_ptr = g.dst_row;
   a.col = g.dst_col;
   a.eid = g.dst_eid;
+  a.order = g.dst_order;
   a.x = x;
   a.Y = Y;
   a.W = W;
@@ -133,6 +134,7 @@ extern "C" tpconv_status tpconv_backward(tpconv_plan_t hp, tpconv_graph_t hg, co
   a.row_ptr = g.src_row;
   a.col = g.src_col;
   a.eid = g.src_eid;
+  a.order = g.src_order;
   a.x = x;
   a.Y = Y;
   a.W = W;

@@ -6,7 +6,11 @@
 // counting sort done on the device -- histogram, scan, scatter -- followed by
 // a per-row sort on the edge id, so every row lists its edges in the
 // caller's order and the layout (and every sum over a row) is deterministic.
-// Integer atomics are used only here, to count and place edges.
+// Each view also gets a row order, longest rows first, in which the kernels
+// hand rows to wavefronts: the long rows start early and the short ones fill
+// the tail of the dispatch.  Rows of equal degree may come in any order; a
+// row's result does not depend on when it runs.  Integer atomics are used
+// only here, to count and place edges and rows.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -22,8 +26,13 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// Rows are handed to wavefronts longest first: bucket of a row = min(degree,
+// kDegBuckets - 1), buckets visited from the highest degree down.
+constexpr int kDegBuckets = 1024;
+
 struct Layout {
-  size_t dst_row, dst_col, dst_eid, src_row, src_col, src_eid, cur_dst, cur_src, err, total;
+  size_t dst_row, dst_col, dst_eid, src_row, src_col, src_eid, dst_order, src_order, cur_dst, cur_src, hist,
+      hcur, err, total;
 };
 
 Layout layout(int64_t n, int64_t e) {
@@ -40,8 +49,12 @@ Layout layout(int64_t n, int64_t e) {
   L.src_row = take(sizeof(int32_t) * (n + 1));
   L.src_col = take(sizeof(int32_t) * e);
   L.src_eid = take(sizeof(int32_t) * e);
+  L.dst_order = take(sizeof(int32_t) * n);
+  L.src_order = take(sizeof(int32_t) * n);
   L.cur_dst = take(sizeof(int32_t) * n);
   L.cur_src = take(sizeof(int32_t) * n);
+  L.hist = take(sizeof(int32_t) * 2 * kDegBuckets);
+  L.hcur = take(sizeof(int32_t) * 2 * kDegBuckets);
   L.err = take(sizeof(int32_t));
   L.total = o;
   return L;
@@ -127,6 +140,27 @@ __global__ void k_sort_rows(const int32_t* __restrict__ row, int32_t* __restrict
   }
 }
 
+__device__ __forceinline__ int deg_bucket(const int32_t* row, int64_t r) {
+  const int d = row[r + 1] - row[r];
+  const int b = d < kDegBuckets - 1 ? d : kDegBuckets - 1;
+  return kDegBuckets - 1 - b;  // bucket 0 holds the longest rows
+}
+
+__global__ void k_deg_hist(const int32_t* __restrict__ row, int64_t N, int32_t* __restrict__ hist) {
+  for (int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; r < N; r += (int64_t)gridDim.x * blockDim.x)
+    atomicAdd(&hist[deg_bucket(row, r)], 1);
+}
+
+// hist holds inclusive bucket ends after k_scan; order[] lists rows longest first
+__global__ void k_deg_order(const int32_t* __restrict__ row, int64_t N, const int32_t* __restrict__ hist,
+                            int32_t* __restrict__ hcur, int32_t* __restrict__ order) {
+  for (int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; r < N; r += (int64_t)gridDim.x * blockDim.x) {
+    const int b = deg_bucket(row, r);
+    const int32_t start = b > 0 ? hist[b - 1] : 0;
+    order[start + atomicAdd(&hcur[b], 1)] = static_cast<int32_t>(r);
+  }
+}
+
 int grid_for(int64_t n, int block) {
   int64_t g = (n + block - 1) / block;
   if (g < 1) g = 1;
@@ -174,6 +208,10 @@ extern "C" tpconv_status tpconv_graph_create(int64_t n_nodes, int64_t n_edges, c
   g.src_row = at(L.src_row);
   g.src_col = at(L.src_col);
   g.src_eid = at(L.src_eid);
+  g.dst_order = at(L.dst_order);
+  g.src_order = at(L.src_order);
+  int32_t* hist = at(L.hist);
+  int32_t* hcur = at(L.hcur);
   int32_t* cur_dst = at(L.cur_dst);
   int32_t* cur_src = at(L.cur_src);
   int32_t* err = at(L.err);
@@ -186,6 +224,8 @@ extern "C" tpconv_status tpconv_graph_create(int64_t n_nodes, int64_t n_edges, c
     hipLaunchKernelGGL(k_fill, dim3(grid_for(n_nodes, B)), dim3(B), 0, stream, cur_src, n_nodes, 0);
   }
   hipLaunchKernelGGL(k_fill, dim3(1), dim3(B), 0, stream, err, int64_t(1), 0);
+  hipLaunchKernelGGL(k_fill, dim3(grid_for(4 * kDegBuckets, B)), dim3(B), 0, stream, hist, int64_t(2 * kDegBuckets), 0);
+  hipLaunchKernelGGL(k_fill, dim3(grid_for(4 * kDegBuckets, B)), dim3(B), 0, stream, hcur, int64_t(2 * kDegBuckets), 0);
   if (n_edges > 0) {
     hipLaunchKernelGGL(k_count, dim3(grid_for(n_edges, B)), dim3(B), 0, stream, src, dst, n_edges, n_nodes,
                        g.dst_row + 1, g.src_row + 1, err);
@@ -201,6 +241,17 @@ extern "C" tpconv_status tpconv_graph_create(int64_t n_nodes, int64_t n_edges, c
                        g.dst_eid, n_nodes);
     hipLaunchKernelGGL(k_sort_rows, dim3(grid_for(n_nodes, 64)), dim3(64), 0, stream, g.src_row, g.src_col,
                        g.src_eid, n_nodes);
+  }
+  if (n_nodes > 0) {
+    const int32_t* rows[2] = {g.dst_row, g.src_row};
+    int32_t* orders[2] = {g.dst_order, g.src_order};
+    for (int v = 0; v < 2; ++v) {
+      int32_t* h = hist + v * kDegBuckets;
+      hipLaunchKernelGGL(k_deg_hist, dim3(grid_for(n_nodes, B)), dim3(B), 0, stream, rows[v], n_nodes, h);
+      hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, h, int64_t(kDegBuckets));
+      hipLaunchKernelGGL(k_deg_order, dim3(grid_for(n_nodes, B)), dim3(B), 0, stream, rows[v], n_nodes, h,
+                         hcur + v * kDegBuckets, orders[v]);
+    }
   }
   hipError_t he = hipGetLastError();
   if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("graph build launch: ") + hipGetErrorString(he));

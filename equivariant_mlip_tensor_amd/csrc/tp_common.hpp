@@ -63,6 +63,7 @@ struct KernelArgs {
   const int32_t* row_ptr;
   const int32_t* col;
   const int32_t* eid;
+  const int32_t* order; // rows in the order wavefronts take them (longest first)
   int32_t in_off[kMaxL + 1];   // x column of segment with this l, -1 if absent
   int32_t out_off[kMaxL + 1];  // out column of segment with this l, -1 if absent
   int32_t woff[kMaxTriples];   // W column of path with this triple, -1 if absent

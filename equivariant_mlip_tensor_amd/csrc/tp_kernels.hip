@@ -1,7 +1,8 @@
 // tp_kernels.hip -- fused CGTP convolution kernels for gfx950 (CDNA4).
 //
-// Compiled once per l bound (-DTPCONV_L=0..4); each object defines the four
-// launchers declared in tp_common.hpp for that bound.
+// Compiled once per l bound and data type (-DTPCONV_L=0..4,
+// -DTPCONV_DOUBLE=0|1); each object defines that pair's two launchers
+// declared in tp_common.hpp.
 //
 // Execution (node-centric, LunaTP Abstract; one fused kernel per direction,
 // FlashTP "Approach"):
@@ -34,6 +35,9 @@
 
 #ifndef TPCONV_L
 #error "compile with -DTPCONV_L=<l bound>"
+#endif
+#ifndef TPCONV_DOUBLE
+#error "compile with -DTPCONV_DOUBLE=0 (fp32) or 1 (fp64)"
 #endif
 
 namespace tpconv {
@@ -351,8 +355,9 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
   using A = typename RowAcc<T>::type;
   constexpr int NL = F::NL, NT = F::NT;
   const int lane = threadIdx.x & 63;
-  const int node = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (node >= a.n_rows) return;  // wave-uniform
+  const int wid = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (wid >= a.n_rows) return;  // wave-uniform
+  const int node = __builtin_amdgcn_readfirstlane(a.order[wid]);
   const int lg = P::lps_log2(a);
   const int slot = lane >> lg;
   const int u = lane & ((1 << lg) - 1);
@@ -506,8 +511,9 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
   constexpr int NL = B::NL, NT = B::NT;
   constexpr int NV = pow2_ceil(NL);  // dY values, padded to a power of two for the reduce-scatter
   const int lane = threadIdx.x & 63;
-  const int node = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (node >= a.n_rows) return;  // wave-uniform
+  const int wid = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (wid >= a.n_rows) return;  // wave-uniform
+  const int node = __builtin_amdgcn_readfirstlane(a.order[wid]);
   const int lg = P::lps_log2(a);
   const int lps = 1 << lg;
   const int slot = lane >> lg;
@@ -707,9 +713,12 @@ hipError_t dispatch(const KernelArgs& a, hipStream_t s) {
 #define TPCONV_CAT(a, b) TPCONV_CAT2(a, b)
 #define TPCONV_LNAME(stem, ty) TPCONV_CAT(TPCONV_CAT(stem, TPCONV_L), ty)
 
-hipError_t TPCONV_LNAME(launch_fwd_l, _f32)(const KernelArgs& a, hipStream_t s) { return dispatch<float, true>(a, s); }
+#if TPCONV_DOUBLE
 hipError_t TPCONV_LNAME(launch_fwd_l, _f64)(const KernelArgs& a, hipStream_t s) { return dispatch<double, true>(a, s); }
-hipError_t TPCONV_LNAME(launch_bwd_l, _f32)(const KernelArgs& a, hipStream_t s) { return dispatch<float, false>(a, s); }
 hipError_t TPCONV_LNAME(launch_bwd_l, _f64)(const KernelArgs& a, hipStream_t s) { return dispatch<double, false>(a, s); }
+#else
+hipError_t TPCONV_LNAME(launch_fwd_l, _f32)(const KernelArgs& a, hipStream_t s) { return dispatch<float, true>(a, s); }
+hipError_t TPCONV_LNAME(launch_bwd_l, _f32)(const KernelArgs& a, hipStream_t s) { return dispatch<float, false>(a, s); }
+#endif
 
 }  // namespace tpconv

@@ -54,6 +54,9 @@ struct Graph {
   int32_t* src_row = nullptr;
   int32_t* src_col = nullptr;
   int32_t* src_eid = nullptr;
+  // rows of each view sorted by decreasing degree (scheduling order)
+  int32_t* dst_order = nullptr;
+  int32_t* src_order = nullptr;
 };
 
 // Records the message for tpconv_last_error() and returns the status.
