@@ -376,9 +376,19 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
 
   const int beg = a.row_ptr[node];
   const int end = a.row_ptr[node + 1];
-  for (int k = beg + slot; k < end; k += P::nslots(a)) {
-    const int e = a.eid[k];
-    const int j = a.col[k];
+  const int nsl = P::nslots(a);
+  // the row's edge ids and neighbours are loaded 64 at a time, one per lane,
+  // and handed to the slots with lane shuffles while the wave is converged
+  for (int cb = beg; cb < end; cb += 64) {
+    const int cn = min(64, end - cb);
+    const int my_e = lane < cn ? a.eid[cb + lane] : 0;
+    const int my_j = lane < cn ? a.col[cb + lane] : 0;
+    const int iters = (cn + nsl - 1) / nsl;
+    for (int it = 0; it < iters; ++it) {
+    const int q = it * nsl + slot;
+    const int e = __shfl(my_e, q & 63, 64);
+    const int j = __shfl(my_j, q & 63, 64);
+    if (q >= cn) continue;
     T x[NL], y[NL], w[NT];
     const T* xr = X + (int64_t)j * d_in;
     static_for<L + 1>([&](auto I) {
@@ -412,6 +422,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
         static_for<2 * l + 1>([&](auto M) { acc[l * l + M] += static_cast<A>(te[l * l + M]); });
       }
     });
+    }
   }
 
   // sum the slots' partial rows: slots sit at lane offsets 2^lg .. 32
@@ -550,9 +561,17 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
 
   const int beg = a.row_ptr[node];
   const int end = a.row_ptr[node + 1];
-  for (int k = beg + slot; k < end; k += P::nslots(a)) {
-    const int e = a.eid[k];
-    const int i = a.col[k];
+  const int nsl = P::nslots(a);
+  for (int cb = beg; cb < end; cb += 64) {
+    const int cn = min(64, end - cb);
+    const int my_e = lane < cn ? a.eid[cb + lane] : 0;
+    const int my_i = lane < cn ? a.col[cb + lane] : 0;
+    const int iters = (cn + nsl - 1) / nsl;
+    for (int it = 0; it < iters; ++it) {
+    const int q = it * nsl + slot;
+    const int e = __shfl(my_e, q & 63, 64);
+    const int i = __shfl(my_i, q & 63, 64);
+    if (q >= cn) continue;
     T g[NL], y[NL], w[NT];
     const T* gr = Gp + (int64_t)i * d_out;
     static_for<L + 1>([&](auto I) {
@@ -626,6 +645,7 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
           if (V < nv && base + V < d_sh) dyr[base + V] = dya[V];
         });
       }
+    }
     }
   }
 
