@@ -74,6 +74,7 @@ struct RowAcc<float> {
 
 enum Parity { kAnyParity = 0, kEvenOnly = 1 };
 
+
 constexpr bool triple_in_class(int l1, int l2, int l3, int par) {
   return par == kAnyParity || ((l1 + l2 + l3) % 2 == 0);
 }
@@ -297,6 +298,22 @@ __device__ __forceinline__ bool group_on(const KernelArgs& a) {
   return any;
 }
 
+// w[t] = this lane's channel of path t in weight row e
+template <typename T, int L, class P>
+__device__ __forceinline__ void load_w(const KernelArgs& a, const T* __restrict__ Wp, int64_t wstride, int uc, int e,
+                                       T (&w)[triple_count(L)]) {
+  const T* wr = Wp + (int64_t)e * wstride + uc;
+  static_for<triple_count(L)>([&](auto I) {
+    constexpr TripleInfo ti = triple_at(L, I);
+    if constexpr (triple_in_class(ti.l1, ti.l2, ti.l3, P::kPar)) {
+      if (P::template on<I>(a)) w[I] = ldg_stream(wr + P::template woff<I>(a));
+      else w[I] = T(0);
+    } else {
+      w[I] = T(0);
+    }
+  });
+}
+
 // ------------------------------------------------------------------ forward
 template <typename T, int L, class P>
 struct Fwd {
@@ -371,8 +388,32 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
   const int d_in = P::d_in(a), d_sh = P::d_sh(a);
   const int64_t wstride = P::wstride(a);
 
-  A acc[NL];
-  static_for<NL>([&](auto I) { acc[I] = A(0); });
+  // Row sum.  fp64 data: fp64 registers.  fp32 data: each edge's path sum
+  // te is added in fp32 into acc for kFlush edges at a time, and acc is then
+  // added into an fp64 row sum kept in LDS (one slab per wave, lane-major),
+  // which costs no VGPRs.
+  constexpr bool kLdsRow = !std::is_same<T, A>::value;
+  constexpr int kFlush = 4;
+  __shared__ A s_row[kLdsRow ? 4 : 1][kLdsRow ? NL : 1][64];
+  A* my_row = &s_row[kLdsRow ? (threadIdx.x >> 6) : 0][0][lane];
+  T acc[NL];
+  static_for<NL>([&](auto I) { acc[I] = T(0); });
+  if constexpr (kLdsRow) {
+    static_for<NL>([&](auto I) { my_row[I * 64] = A(0); });
+  }
+  auto flush = [&]() {
+    if constexpr (kLdsRow) {
+      static_for<L + 1>([&](auto I) {
+        constexpr int l = I;
+        if (P::out_l(a, l)) {
+          static_for<2 * l + 1>([&](auto M) {
+            my_row[(l * l + M) * 64] += static_cast<A>(acc[l * l + M]);
+            acc[l * l + M] = T(0);
+          });
+        }
+      });
+    }
+  };
 
   const int beg = a.row_ptr[node];
   const int end = a.row_ptr[node + 1];
@@ -404,30 +445,28 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
       if (I < d_sh) y[I] = ldg_stream(yr + I);
       else y[I] = T(0);
     });
-    const T* wr = Wp + (int64_t)e * wstride + uc;
-    static_for<NT>([&](auto I) {
-      constexpr TripleInfo ti = triple_at(L, I);
-      if constexpr (triple_in_class(ti.l1, ti.l2, ti.l3, P::kPar)) {
-        if (P::template on<I>(a)) w[I] = ldg_stream(wr + P::template woff<I>(a));
-        else w[I] = T(0);
-      } else {
-        w[I] = T(0);
-      }
-    });
+    load_w<T, L, P>(a, Wp, wstride, uc, e, w);
     T te[NL];
     F::edge(a, __builtin_amdgcn_readfirstlane(e), x, y, w, te);
     static_for<L + 1>([&](auto I) {
       constexpr int l = I;
       if (P::out_l(a, l)) {
-        static_for<2 * l + 1>([&](auto M) { acc[l * l + M] += static_cast<A>(te[l * l + M]); });
+        static_for<2 * l + 1>([&](auto M) { acc[l * l + M] += te[l * l + M]; });
       }
     });
+    if (it % kFlush == kFlush - 1) flush();
     }
   }
+  flush();
 
   // sum the slots' partial rows: slots sit at lane offsets 2^lg .. 32
+  A tot[NL];
+  static_for<NL>([&](auto I) {
+    if constexpr (kLdsRow) tot[I] = my_row[I * 64];
+    else tot[I] = acc[I];
+  });
   for (int off = 1 << lg; off < 64; off <<= 1) {
-    static_for<NL>([&](auto I) { acc[I] += __shfl_xor(acc[I], off, 64); });
+    static_for<NL>([&](auto I) { tot[I] += __shfl_xor(tot[I], off, 64); });
   }
   if (slot == 0 && chan_ok) {
     T* orow = O + (int64_t)node * P::d_out(a);
@@ -435,7 +474,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
       constexpr int l = I;
       const int off = P::out_off(a, l);
       if (off >= 0) {
-        static_for<2 * l + 1>([&](auto M) { orow[off + u * (2 * l + 1) + M] = static_cast<T>(acc[l * l + M]); });
+        static_for<2 * l + 1>([&](auto M) { orow[off + u * (2 * l + 1) + M] = static_cast<T>(tot[l * l + M]); });
       }
     });
   }
@@ -587,16 +626,7 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
       if (I < d_sh) y[I] = ldg_stream(yr + I);
       else y[I] = T(0);
     });
-    const T* wr = Wp + (int64_t)e * wstride + uc;
-    static_for<NT>([&](auto I) {
-      constexpr TripleInfo ti = triple_at(L, I);
-      if constexpr (triple_in_class(ti.l1, ti.l2, ti.l3, P::kPar)) {
-        if (P::template on<I>(a)) w[I] = ldg_stream(wr + P::template woff<I>(a));
-        else w[I] = T(0);
-      } else {
-        w[I] = T(0);
-      }
-    });
+    load_w<T, L, P>(a, Wp, wstride, uc, e, w);
 
     T dya[NV], dxe[NL];
     static_for<NV>([&](auto I) { dya[I] = T(0); });
