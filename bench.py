@@ -170,8 +170,10 @@ def main():
         "config": {"workload": f"{w.name}: {N} atoms, density 0.1/A^3, periodic, cutoff {w.cutoff} A, "
                                f"{E} edges, {w.irreps_in} -> {w.irreps_out}, SH l<={w.sh_lmax}, "
                                f"{plan.n_paths} paths", "n_nodes": N, "n_edges": E},
-        "kernels_ms": {"forward_avg": round(f_avg, 4), "forward_min": round(float(fwd_ms.min()), 4),
-                       "backward_avg": round(b_avg, 4), "backward_min": round(float(bwd_ms.min()), 4)},
+        "kernels_ms": {"forward_avg": round(f_avg, 4), "forward_median": round(float(np.median(fwd_ms)), 4),
+                       "forward_min": round(float(fwd_ms.min()), 4),
+                       "backward_avg": round(b_avg, 4), "backward_median": round(float(np.median(bwd_ms)), 4),
+                       "backward_min": round(float(bwd_ms.min()), 4)},
         "hbm": {"fwd_bwd_algorithmic_GBps": round(hbm_fwdbwd, 1), "frac_of_peak": round(hbm_fwdbwd / HBM_PEAK_GBS, 4),
                 "fwd_bytes": int(fwd_bytes), "bwd_bytes": int(bwd_bytes)},
         "roofline": roofline,

@@ -626,7 +626,16 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
       if (I < d_sh) y[I] = ldg_stream(yr + I);
       else y[I] = T(0);
     });
-    load_w<T, L, P>(a, Wp, wstride, uc, e, w);
+    const T* wr = Wp + (int64_t)e * wstride + uc;
+    static_for<NT>([&](auto I) {
+      constexpr TripleInfo ti = triple_at(L, I);
+      if constexpr (triple_in_class(ti.l1, ti.l2, ti.l3, P::kPar)) {
+        if (P::template on<I>(a)) w[I] = ldg_stream(wr + P::template woff<I>(a));
+        else w[I] = T(0);
+      } else {
+        w[I] = T(0);
+      }
+    });
 
     T dya[NV], dxe[NL];
     static_for<NV>([&](auto I) { dya[I] = T(0); });
