@@ -55,6 +55,12 @@ __device__ __forceinline__ void static_for(F&& f) {
 __device__ __forceinline__ float fmaT(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
 __device__ __forceinline__ double fmaT(double a, double b, double c) { return __builtin_fma(a, b, c); }
 
+// Empty asm that keeps a value in a VGPR as an opaque SSA value.
+template <typename T>
+__device__ __forceinline__ void pin_vgpr(T& v) {
+  asm volatile("" : "+v"(v));
+}
+
 template <typename T>
 __device__ __forceinline__ T ldg_stream(const T* p) {
   return __builtin_nontemporal_load(p);
@@ -665,8 +671,14 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
             constexpr int h = NV >> (s + 1);
             const bool upper = (u & b) != 0;
             static_for<h>([&](auto V) {
-              const T keep = upper ? dya[V + h] : dya[V];
-              const T send = upper ? dya[V] : dya[V + h];
+              // opaque copies: a select between two array elements could be
+              // folded into one load with a run-time index, which would move
+              // the whole array to LDS
+              T lo = dya[V], hi = dya[V + h];
+              pin_vgpr(lo);
+              pin_vgpr(hi);
+              const T keep = upper ? hi : lo;
+              const T send = upper ? lo : hi;
               dya[V] = keep + __shfl_xor(send, b, 64);
             });
             if (upper) base += h;
