@@ -59,6 +59,22 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def counter_traffic(workload, kernel):
+    """Calibrated HBM bytes per launch from the committed rocprofv3 counters,
+    or None when they are missing or were taken on another kernel source."""
+    path = os.path.join(ROOT, "profiles", f"tpconv_{workload}_counters.json")
+    try:
+        with open(path) as fh:
+            c = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source") != kernel_source_hash():
+        return None
+    key = "bwd_kernel" if kernel == "tpconv_backward" else "fwd_kernel"
+    v = c.get("hbm_bytes_per_launch", {}).get(key)
+    return None if v is None else int(round(v))
+
+
 def cpu_baseline(w, d, sample_edges):
     """The fp64 numpy oracle, as it stands, on the edges of the first destination rows."""
     import numpy as np
@@ -156,7 +172,8 @@ def main():
     dom = ("tpconv_backward", bwd_bytes, b_avg) if b_avg >= f_avg else ("tpconv_forward", fwd_bytes, f_avg)
     achieved = dom[1] / (dom[2] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom[0]}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic(w.name, dom[0]),
+                "kernel": dom[0], "algorithmic_bytes": int(dom[1]), "avg_ms": round(dom[2], 4)}
     hbm_fwdbwd = (fwd_bytes + bwd_bytes) / ((f_avg + b_avg) * 1e-3) / 1e9
 
     res = {
