@@ -560,6 +560,15 @@ constexpr int pow2_ceil(int n) {
   return p;
 }
 
+// The backward keeps a second set of edge-input registers (one edge ahead)
+// where that still fits in 256 VGPRs: fp32 up to l = 2, and l = 3 with the
+// even-parity path set.  Wider kernels already spill to AGPRs with one set,
+// and a second would double that.
+template <typename T, int L, class P>
+constexpr bool bwd_pipelined() {
+  return sizeof(T) == 4 && (L <= 2 || (L == 3 && P::kPar == kEvenOnly));
+}
+
 template <typename T, int L, class P>
 __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
   using B = Bwd<T, L, P>;
@@ -600,24 +609,34 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
         else x[l * l + M] = T(0);
       });
     });
+    // wait for the row here, before any dW / dY store is in flight
+    static_for<NL>([&](auto I) { pin_vgpr(x[I]); });
   }
   A dxa[NL];
   static_for<NL>([&](auto I) { dxa[I] = A(0); });
 
+  // The wave walks the row in steps of nslots edges: step k gives slot s the
+  // edge at row position k * nslots + s.  Edge ids arrive 64 at a time (one
+  // per lane) and are handed to the slots with lane shuffles.  The inputs of
+  // step k + 1 are requested before step k computes and stores, so their
+  // latency hides behind step k and the in-order memory counter never has to
+  // wait for this step's dW / dY stores before the next step can start.
   const int beg = a.row_ptr[node];
-  const int end = a.row_ptr[node + 1];
-  const int nsl = P::nslots(a);
-  for (int cb = beg; cb < end; cb += 64) {
-    const int cn = min(64, end - cb);
-    const int my_e = lane < cn ? a.eid[cb + lane] : 0;
-    const int my_i = lane < cn ? a.col[cb + lane] : 0;
-    const int iters = (cn + nsl - 1) / nsl;
-    for (int it = 0; it < iters; ++it) {
-    const int q = it * nsl + slot;
-    const int e = __shfl(my_e, q & 63, 64);
-    const int i = __shfl(my_i, q & 63, 64);
-    if (q >= cn) continue;
-    T g[NL], y[NL], w[NT];
+  const int deg = a.row_ptr[node + 1] - beg;
+  const int lgs = 6 - lg;                       // log2(slots per wave)
+  const int n_steps = (deg + (1 << lgs) - 1) >> lgs;
+  const int chunk_mask = (64 >> lgs) - 1;       // steps per chunk of 64 ids, minus one
+  int my_e = 0, my_i = 0;
+  auto fetch_ids = [&](int k) {
+    const int p = (k << lgs) + lane;
+    my_e = p < deg ? a.eid[beg + p] : 0;
+    my_i = p < deg ? a.col[beg + p] : 0;
+    // wait for the ids here: a wait at their first use inside the loop
+    // would also wait for every store still in flight
+    pin_vgpr(my_e);
+    pin_vgpr(my_i);
+  };
+  auto load_edge = [&](int e, int i, T (&g)[NL], T (&y)[NL], T (&w)[NT]) {
     const T* gr = Gp + (int64_t)i * d_out;
     static_for<L + 1>([&](auto I) {
       constexpr int l = I;
@@ -642,18 +661,36 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
         w[I] = T(0);
       }
     });
+  };
 
+  // Two register sets for the edge inputs, used alternately, so the step
+  // that prefetches into one set never copies registers still being loaded.
+  // Loads and arithmetic run unconditionally: a slot past the end of the row
+  // reads edge 0 / node 0 (its ids are 0) and only its stores and its share
+  // of dx are masked, which keeps every load out of divergent control flow.
+  auto prefetch = [&](int k, int& e, bool& valid, T (&g)[NL], T (&y)[NL], T (&w)[NT]) {
+    const int r = k & chunk_mask;
+    if (r == 0) fetch_ids(k);
+    const int q = (r << lgs) + slot;
+    e = __shfl(my_e, q, 64);
+    const int i = __shfl(my_i, q, 64);
+    valid = (k << lgs) + slot < deg;
+    load_edge(e, i, g, y, w);
+  };
+  auto compute = [&](const int e, const bool valid, const T (&g)[NL], const T (&y)[NL], const T (&w)[NT]) {
     T dya[NV], dxe[NL];
     static_for<NV>([&](auto I) { dya[I] = T(0); });
     // idle lanes (u >= U) aim their dW stores at channel 0 of the same row
     // and store only when chan_ok; for a power-of-two U every lane is active
     const bool store_dw = DW != nullptr;
     T* dwr = store_dw ? DW + (int64_t)e * wstride + uc : nullptr;
-    B::edge(a, __builtin_amdgcn_readfirstlane(e), x, y, g, w, dxe, dya, store_dw && chan_ok, dwr);
+    B::edge(a, __builtin_amdgcn_readfirstlane(e), x, y, g, w, dxe, dya, store_dw && chan_ok && valid, dwr);
     static_for<L + 1>([&](auto I) {
       constexpr int l = I;
       if (P::in_l(a, l)) {
-        static_for<2 * l + 1>([&](auto M) { dxa[l * l + M] += static_cast<A>(dxe[l * l + M]); });
+        static_for<2 * l + 1>([&](auto M) {
+          dxa[l * l + M] += valid ? static_cast<A>(dxe[l * l + M]) : A(0);
+        });
       }
     });
 
@@ -690,13 +727,34 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
       });
       // bits below lps/NV were plain sums: one lane of each such group stores
       const int plain_mask = lps > NV ? lps / NV - 1 : 0;
-      if ((u & plain_mask) == 0) {
+      if ((u & plain_mask) == 0 && valid) {
         T* dyr = DY + (int64_t)e * d_sh;
         static_for<NV>([&](auto V) {
           if (V < nv && base + V < d_sh) dyr[base + V] = dya[V];
         });
       }
     }
+  };
+
+  T ga[NL], ya[NL], wa[NT];
+  int ea = 0;
+  bool va = false;
+  if constexpr (bwd_pipelined<T, L, P>()) {
+    T gb[NL], yb[NL], wb[NT];
+    int eb = 0;
+    bool vb = false;
+    if (n_steps > 0) prefetch(0, ea, va, ga, ya, wa);
+    for (int k = 0; k < n_steps; k += 2) {  // wave-uniform trip count
+      prefetch(k + 1, eb, vb, gb, yb, wb);
+      compute(ea, va, ga, ya, wa);
+      if (k + 1 >= n_steps) break;
+      prefetch(k + 2, ea, va, ga, ya, wa);
+      compute(eb, vb, gb, yb, wb);
+    }
+  } else {
+    for (int k = 0; k < n_steps; ++k) {
+      prefetch(k, ea, va, ga, ya, wa);
+      compute(ea, va, ga, ya, wa);
     }
   }
 
