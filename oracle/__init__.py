@@ -24,7 +24,7 @@ Modules:
   irreps  -- irreps strings and the path list (W layout).
   cg      -- complex CG by Racah's closed form, real-basis CG.
   sh      -- real spherical harmonics built from scipy's complex ones.
-  tp      -- dense per-edge forward and backward.
+  tp      -- dense per-edge forward, backward and double backward.
 
 Every function here is pinned by a test in ``tests/test_oracle_*.py`` against
 mathematics it does not itself use (library routines, closed forms,
@@ -34,4 +34,4 @@ invariants, finite differences, brute force).
 from .irreps import Irreps, parse_irreps, enumerate_paths  # noqa: F401
 from .cg import cg_complex, real_basis_U, cg_real  # noqa: F401
 from .sh import sh_complex, sh_real  # noqa: F401
-from .tp import TPProblem, tp_forward, tp_backward  # noqa: F401
+from .tp import TPProblem, tp_forward, tp_backward, tp_double_backward  # noqa: F401
