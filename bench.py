@@ -38,6 +38,9 @@ def parse():
     p.add_argument("--workload", default="c4k")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-edges", type=int, default=40000)
+    p.add_argument("--cold-reps", type=int, default=20,
+                   help="after the timed steps, this many extra steps each preceded by reading a 1 GiB buffer "
+                        "(evicts the 256 MB Infinity Cache); kernel medians reported as kernels_ms_cold")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="also run one plain device copy of this many MiB (scales rocprofv3 FETCH/WRITE_SIZE)")
     return p.parse_args()
@@ -165,6 +168,27 @@ def main():
     bwd_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
     peak_gib = torch.cuda.max_memory_allocated() / 2**30
 
+    cold = None
+    if args.cold_reps > 0:
+        # cold-cache kernel times: a 1 GiB read before each step pushes the
+        # inputs out of L2 and the Infinity Cache without leaving dirty lines
+        evict = torch.ones(2**28, dtype=torch.float32, device=dev)
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.cold_reps)]
+        for k in range(args.cold_reps):
+            evict.sum()
+            cev[k][0].record(stream)
+            tp.tpconv_forward(plan, graph, x, Y, W, out)
+            cev[k][1].record(stream)
+            tp.tpconv_backward(plan, graph, x, Y, W, G, dx, dY, dW)
+            cev[k][2].record(stream)
+        torch.cuda.synchronize()
+        cf = float(np.median([e[0].elapsed_time(e[1]) for e in cev]))
+        cb = float(np.median([e[1].elapsed_time(e[2]) for e in cev]))
+        cold = {"forward_median": round(cf, 4), "backward_median": round(cb, 4), "reps": args.cold_reps,
+                "edges_per_s": round(E / ((cf + cb) * 1e-3), 1),
+                "evict": "1 GiB device read (torch.sum) before each step"}
+        del evict
+
     b = 4 if w.dtype == "f32" else 8
     fwd_bytes, bwd_bytes = algorithmic_bytes(plan, N, E, b)
     f_avg, b_avg = float(fwd_ms.mean()), float(bwd_ms.mean())
@@ -191,6 +215,7 @@ def main():
                        "forward_min": round(float(fwd_ms.min()), 4),
                        "backward_avg": round(b_avg, 4), "backward_median": round(float(np.median(bwd_ms)), 4),
                        "backward_min": round(float(bwd_ms.min()), 4)},
+        "kernels_ms_cold": cold,
         "hbm": {"fwd_bwd_algorithmic_GBps": round(hbm_fwdbwd, 1), "frac_of_peak": round(hbm_fwdbwd / HBM_PEAK_GBS, 4),
                 "fwd_bytes": int(fwd_bytes), "bwd_bytes": int(bwd_bytes)},
         "roofline": roofline,

@@ -3,8 +3,9 @@
     python -m equivariant_mlip_tensor_amd.build     # or __graft_entry__.build()
 
 Objects go to <repo>/_build/, the shared library to this package directory.
-The kernel translation unit is compiled once per (l bound, data type) so the
-ten objects build in parallel.
+The kernel translation unit is compiled once per (l bound, data type, kernel
+family: forward/backward or double backward) so the twenty objects build in
+parallel.
 """
 
 from __future__ import annotations
@@ -39,9 +40,12 @@ COMMON = [
 def _jobs():
     units = []
     for L in (4, 3, 2, 1, 0):          # longest compiles first
-        for dbl in (1, 0):
-            units.append((os.path.join(CSRC, "tp_kernels.hip"), os.path.join(BUILD, f"tp_l{L}_{'f64' if dbl else 'f32'}.o"),
-                          [f"-DTPCONV_L={L}", f"-DTPCONV_DOUBLE={dbl}"]))
+        for dd in (1, 0):
+            for dbl in (1, 0):
+                stem = "tp_dd" if dd else "tp"
+                units.append((os.path.join(CSRC, "tp_kernels.hip"),
+                              os.path.join(BUILD, f"{stem}_l{L}_{'f64' if dbl else 'f32'}.o"),
+                              [f"-DTPCONV_L={L}", f"-DTPCONV_DOUBLE={dbl}", f"-DTPCONV_DD={dd}"]))
     units.append((os.path.join(CSRC, "graph.hip"), os.path.join(BUILD, "graph.o"), []))
     # the host CG builder runs without FMA contraction so its run-time values
     # are bit-identical to the kernels' compile-time evaluation

@@ -1,4 +1,5 @@
-// api.cpp -- tpconv_forward / tpconv_backward dispatch and error reporting.
+// api.cpp -- tpconv_forward / tpconv_backward / tpconv_double_backward dispatch
+// and error reporting.
 #include <string>
 
 #include "tpconv_internal.hpp"
@@ -10,11 +11,19 @@ thread_local std::string g_last_error;
 
 using Launcher = hipError_t (*)(const KernelArgs&, hipStream_t);
 
-Launcher pick(bool fwd, int L, tpconv_dtype dt) {
-#define TPCONV_PICK(LL)                                                                   \
-  case LL:                                                                                \
-    if (fwd) return dt == TPCONV_F32 ? launch_fwd_l##LL##_f32 : launch_fwd_l##LL##_f64; \
-    return dt == TPCONV_F32 ? launch_bwd_l##LL##_f32 : launch_bwd_l##LL##_f64;
+enum class Kind { kFwd, kBwd, kDDF, kDDB };
+
+Launcher pick(Kind k, int L, tpconv_dtype dt) {
+  const bool f32 = dt == TPCONV_F32;
+#define TPCONV_PICK(LL)                                                             \
+  case LL:                                                                          \
+    switch (k) {                                                                    \
+      case Kind::kFwd: return f32 ? launch_fwd_l##LL##_f32 : launch_fwd_l##LL##_f64; \
+      case Kind::kBwd: return f32 ? launch_bwd_l##LL##_f32 : launch_bwd_l##LL##_f64; \
+      case Kind::kDDF: return f32 ? launch_ddf_l##LL##_f32 : launch_ddf_l##LL##_f64; \
+      case Kind::kDDB: return f32 ? launch_ddb_l##LL##_f32 : launch_ddb_l##LL##_f64; \
+    }                                                                               \
+    return nullptr;
   switch (L) {
     TPCONV_PICK(0)
     TPCONV_PICK(1)
@@ -111,7 +120,7 @@ extern "C" tpconv_status tpconv_forward(tpconv_plan_t hp, tpconv_graph_t hg, con
   a.Y = Y;
   a.W = W;
   a.out = out;
-  Launcher f = pick(true, p.kernel_l, p.dtype);
+  Launcher f = pick(Kind::kFwd, p.kernel_l, p.dtype);
   if (f == nullptr) return fail(TPCONV_E_UNSUPPORTED, "no kernel for this l bound");
   const hipError_t he = f(a, stream);
   if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("forward launch: ") + hipGetErrorString(he));
@@ -142,9 +151,60 @@ extern "C" tpconv_status tpconv_backward(tpconv_plan_t hp, tpconv_graph_t hg, co
   a.out = grad_x;
   a.dY = grad_Y;
   a.dW = grad_W;
-  Launcher f = pick(false, p.kernel_l, p.dtype);
+  Launcher f = pick(Kind::kBwd, p.kernel_l, p.dtype);
   if (f == nullptr) return fail(TPCONV_E_UNSUPPORTED, "no kernel for this l bound");
   const hipError_t he = f(a, stream);
   if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("backward launch: ") + hipGetErrorString(he));
+  return TPCONV_OK;
+}
+
+extern "C" tpconv_status tpconv_double_backward(tpconv_plan_t hp, tpconv_graph_t hg, const void* x, const void* Y,
+                                                const void* W, const void* grad_out, const void* ggx,
+                                                const void* ggY, const void* ggW, void* grad_x, void* grad_Y,
+                                                void* grad_W, void* grad_G, hipStream_t stream) {
+  if (hp == nullptr || hg == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL plan or graph");
+  const Plan& p = *reinterpret_cast<const Plan*>(hp);
+  const Graph& g = *reinterpret_cast<const Graph*>(hg);
+  const bool want_edges = g.n_edges > 0 && (grad_Y != nullptr || grad_W != nullptr);
+  const bool want_src = grad_x != nullptr || want_edges;  // second kernel
+  const bool want_dst = grad_G != nullptr;                 // first kernel
+  if (!want_src && !want_dst) return TPCONV_OK;
+  if (g.n_nodes > 0 && x == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL x");
+  if (g.n_nodes > 0 && want_src && grad_out == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL grad_out");
+  if (g.n_edges > 0 && (Y == nullptr || W == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL Y or W");
+  if (g.n_nodes == 0) return TPCONV_OK;
+  Launcher ff = pick(Kind::kDDF, p.kernel_l, p.dtype);
+  Launcher fb = pick(Kind::kDDB, p.kernel_l, p.dtype);
+  if (ff == nullptr || fb == nullptr) return fail(TPCONV_E_UNSUPPORTED, "no kernel for this l bound");
+  KernelArgs a = base_args(p, g.n_nodes);
+  a.x = x;
+  a.Y = Y;
+  a.W = W;
+  a.xa = ggx;
+  a.Yb = ggY;
+  a.Wc = ggW;
+  if (want_dst) {
+    KernelArgs f = a;
+    f.row_ptr = g.dst_row;
+    f.col = g.dst_col;
+    f.eid = g.dst_eid;
+    f.order = g.dst_order;
+    f.out = grad_G;
+    const hipError_t he = ff(f, stream);
+    if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("double backward launch: ") + hipGetErrorString(he));
+  }
+  if (want_src) {
+    KernelArgs b = a;
+    b.row_ptr = g.src_row;
+    b.col = g.src_col;
+    b.eid = g.src_eid;
+    b.order = g.src_order;
+    b.G = grad_out;
+    b.out = grad_x;
+    b.dY = grad_Y;
+    b.dW = grad_W;
+    const hipError_t he = fb(b, stream);
+    if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("double backward launch: ") + hipGetErrorString(he));
+  }
   return TPCONV_OK;
 }

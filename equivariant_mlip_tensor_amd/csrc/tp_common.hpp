@@ -38,9 +38,10 @@ constexpr int triple_id(int L, int l1, int l2, int l3) {
 constexpr int kMaxTriples = triple_count(kMaxL);  // 65
 static_assert(kMaxTriples <= 128, "triple ids must fit the two path-mask words");
 
-// Launch arguments shared by the forward and backward kernels.  `row_ptr`,
-// `col` and `eid` are the CSR view the kernel walks: destination-sorted for
-// the forward (col = src), source-sorted for the backward (col = dst).
+// Launch arguments shared by all kernels.  `row_ptr`, `col` and `eid` are the
+// CSR view the kernel walks: destination-sorted for the forward and the
+// double backward's grad_G (col = src), source-sorted for the backward and
+// the double backward's grad_x / grad_Y / grad_W (col = dst).
 struct KernelArgs {
   int32_t n_rows;       // nodes
   int32_t mul;          // U, channels per segment (1..64)
@@ -67,21 +68,30 @@ struct KernelArgs {
   int32_t in_off[kMaxL + 1];   // x column of segment with this l, -1 if absent
   int32_t out_off[kMaxL + 1];  // out column of segment with this l, -1 if absent
   int32_t woff[kMaxTriples];   // W column of path with this triple, -1 if absent
-  const void* x;        // forward: x;  backward: x
+  const void* x;
   const void* Y;
   const void* W;
-  const void* G;        // backward only
-  void* out;            // forward: out; backward: grad_x (may be null)
-  void* dY;             // backward only (may be null)
-  void* dW;             // backward only (may be null)
+  const void* G;        // backward kernels only
+  const void* xa;       // double backward: cotangent of grad_x, like x (null = zero)
+  const void* Yb;       // double backward: cotangent of grad_Y, like Y (null = zero)
+  const void* Wc;       // double backward: cotangent of grad_W, like W (null = zero)
+  void* out;            // forward: out; backward: grad_x; double backward: grad_G or grad_x (may be null)
+  void* dY;             // backward kernels: grad_Y (may be null)
+  void* dW;             // backward kernels: grad_W (may be null)
 };
 
-// Launchers, one per (lmax, dtype), defined by tp_kernels.hip compiled once per lmax.
+// Launchers, one per (lmax, dtype), defined by tp_kernels.hip compiled once
+// per (lmax, dtype, TPCONV_DD): fwd/bwd with TPCONV_DD=0, and the double
+// backward's two passes ddf (grad_G) / ddb (grad_x, grad_Y, grad_W) with 1.
 #define TPCONV_DECLARE_LAUNCHERS(L)                                                \
   hipError_t launch_fwd_l##L##_f32(const KernelArgs& a, hipStream_t s);            \
   hipError_t launch_fwd_l##L##_f64(const KernelArgs& a, hipStream_t s);            \
   hipError_t launch_bwd_l##L##_f32(const KernelArgs& a, hipStream_t s);            \
-  hipError_t launch_bwd_l##L##_f64(const KernelArgs& a, hipStream_t s);
+  hipError_t launch_bwd_l##L##_f64(const KernelArgs& a, hipStream_t s);            \
+  hipError_t launch_ddf_l##L##_f32(const KernelArgs& a, hipStream_t s);            \
+  hipError_t launch_ddf_l##L##_f64(const KernelArgs& a, hipStream_t s);            \
+  hipError_t launch_ddb_l##L##_f32(const KernelArgs& a, hipStream_t s);            \
+  hipError_t launch_ddb_l##L##_f64(const KernelArgs& a, hipStream_t s);
 
 TPCONV_DECLARE_LAUNCHERS(0)
 TPCONV_DECLARE_LAUNCHERS(1)

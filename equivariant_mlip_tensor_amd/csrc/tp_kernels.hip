@@ -1,7 +1,7 @@
 // tp_kernels.hip -- fused CGTP convolution kernels for gfx950 (CDNA4).
 //
-// Compiled once per l bound and data type (-DTPCONV_L=0..4,
-// -DTPCONV_DOUBLE=0|1); each object defines that pair's two launchers
+// Compiled once per l bound, data type and kernel family (-DTPCONV_L=0..4,
+// -DTPCONV_DOUBLE=0|1, -DTPCONV_DD=0|1); each object defines that triple's two launchers
 // declared in tp_common.hpp.
 //
 // Execution (node-centric, LunaTP Abstract; one fused kernel per direction,
@@ -38,6 +38,9 @@
 #endif
 #ifndef TPCONV_DOUBLE
 #error "compile with -DTPCONV_DOUBLE=0 (fp32) or 1 (fp64)"
+#endif
+#ifndef TPCONV_DD
+#error "compile with -DTPCONV_DD=0 (forward, backward) or 1 (double backward)"
 #endif
 
 namespace tpconv {
@@ -372,9 +375,76 @@ struct Fwd {
   }
 };
 
+// Double backward, grad_G: with a, b, c the cotangents of grad_x, grad_Y and
+// grad_W, te[l3 block] = sum over the edge's paths of
+//   W[p,u] * CG_p(a, y) + W[p,u] * CG_p(x, b) + c[p,u] * CG_p(x, y).
+// The first two share one product array per group, p2 = a (x) y + x (x) b.
 template <typename T, int L, class P>
+struct FwdDD {
+  static constexpr int NL = (L + 1) * (L + 1);
+  static constexpr int NT = triple_count(L);
+
+  static __device__ __forceinline__ void edge(const KernelArgs& a, int tok, const T (&x)[NL], const T (&xa)[NL],
+                                              const T (&y)[NL], const T (&yb)[NL], const T (&w)[NT],
+                                              const T (&wc)[NT], T (&te)[NL]) {
+    static_for<L + 1>([&](auto I1) {
+      constexpr int l1 = I1;
+      static_for<L + 1>([&](auto I2) {
+        constexpr int l2 = I2;
+        if (!group_on<L, P, l1, l2>(a)) return;
+        constexpr int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1;
+        T p1[n1 * n2], p2[n1 * n2];
+        static_for<n1>([&](auto M1) {
+          static_for<n2>([&](auto M2) {
+            if constexpr (group_uses<L, P::kPar, l1, l2>(M1, M2)) {
+              const T xv = x[l1 * l1 + M1], yv = y[l2 * l2 + M2];
+              p1[M1 * n2 + M2] = xv * yv;
+              p2[M1 * n2 + M2] = fmaT(xa[l1 * l1 + M1], yv, xv * yb[l2 * l2 + M2]);
+            }
+          });
+        });
+        static_for<L + 1>([&](auto I3) {
+          constexpr int l3 = I3;
+          if constexpr (cg::triangle(l1, l2, l3) && triple_in_class(l1, l2, l3, P::kPar)) {
+            constexpr int t = triple_id(L, l1, l2, l3);
+            if (P::template on<t>(a) && P::template run<t>(a, tok)) {
+              using TI = TabInfo<l1, l2, l3>;
+              constexpr int n3 = 2 * l3 + 1;
+              T z1[n3], z2[n3];
+              static_for<TI::tab.n>([&](auto K) {
+                constexpr cg::Entry en = TI::tab.e[K];
+                constexpr T c = en.neg ? T(-en.mag) : T(en.mag);
+                constexpr int pi = en.m1 * n2 + en.m2;
+                if constexpr (TI::first_m3(K)) {
+                  z1[en.m3] = c * p1[pi];
+                  z2[en.m3] = c * p2[pi];
+                } else {
+                  z1[en.m3] = fmaT(c, p1[pi], z1[en.m3]);
+                  z2[en.m3] = fmaT(c, p2[pi], z2[en.m3]);
+                }
+              });
+              if (P::template first3<t>(a)) {
+                static_for<n3>([&](auto M3) { te[l3 * l3 + M3] = fmaT(w[t], z2[M3], wc[t] * z1[M3]); });
+              } else {
+                static_for<n3>([&](auto M3) {
+                  te[l3 * l3 + M3] = fmaT(w[t], z2[M3], fmaT(wc[t], z1[M3], te[l3 * l3 + M3]));
+                });
+              }
+            }
+          }
+        });
+      });
+    });
+  }
+};
+
+// Forward (DD = false): out = the convolution.  Double backward's first pass
+// (DD = true): out = grad_G, from the cotangents a (gathered like x), b (like
+// Y) and c (like W); a null cotangent reads as zeros.
+template <typename T, int L, class P, bool DD>
 __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
   using F = Fwd<T, L, P>;
+  using FD = FwdDD<T, L, P>;
   using A = typename RowAcc<T>::type;
   constexpr int NL = F::NL, NT = F::NT;
   const int lane = threadIdx.x & 63;
@@ -390,6 +460,9 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
   const T* __restrict__ X = static_cast<const T*>(a.x);
   const T* __restrict__ Yp = static_cast<const T*>(a.Y);
   const T* __restrict__ Wp = static_cast<const T*>(a.W);
+  const T* __restrict__ XA = static_cast<const T*>(a.xa);
+  const T* __restrict__ YB = static_cast<const T*>(a.Yb);
+  const T* __restrict__ WC = static_cast<const T*>(a.Wc);
   T* __restrict__ O = static_cast<T*>(a.out);
   const int d_in = P::d_in(a), d_sh = P::d_sh(a);
   const int64_t wstride = P::wstride(a);
@@ -437,23 +510,40 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
     const int j = __shfl(my_j, q & 63, 64);
     if (q >= cn) continue;
     T x[NL], y[NL], w[NT];
-    const T* xr = X + (int64_t)j * d_in;
-    static_for<L + 1>([&](auto I) {
-      constexpr int l = I;
-      const int off = P::in_off(a, l);
-      static_for<2 * l + 1>([&](auto M) {
-        if (off >= 0) x[l * l + M] = xr[off + uc * (2 * l + 1) + M];
-        else x[l * l + M] = T(0);
+    auto load_x = [&](const T* __restrict__ base, T (&v)[NL]) {
+      const T* xr = base + (int64_t)j * d_in;
+      static_for<L + 1>([&](auto I) {
+        constexpr int l = I;
+        const int off = P::in_off(a, l);
+        static_for<2 * l + 1>([&](auto M) {
+          if (off >= 0) v[l * l + M] = xr[off + uc * (2 * l + 1) + M];
+          else v[l * l + M] = T(0);
+        });
       });
-    });
-    const T* yr = Yp + (int64_t)e * d_sh;
-    static_for<NL>([&](auto I) {
-      if (I < d_sh) y[I] = ldg_stream(yr + I);
-      else y[I] = T(0);
-    });
+    };
+    auto load_y = [&](const T* __restrict__ base, T (&v)[NL]) {
+      const T* yr = base + (int64_t)e * d_sh;
+      static_for<NL>([&](auto I) {
+        if (I < d_sh) v[I] = ldg_stream(yr + I);
+        else v[I] = T(0);
+      });
+    };
+    load_x(X, x);
+    load_y(Yp, y);
     load_w<T, L, P>(a, Wp, wstride, uc, e, w);
     T te[NL];
-    F::edge(a, __builtin_amdgcn_readfirstlane(e), x, y, w, te);
+    if constexpr (DD) {
+      T xa[NL], yb[NL], wc[NT];
+      if (XA != nullptr) load_x(XA, xa);
+      else static_for<NL>([&](auto I) { xa[I] = T(0); });
+      if (YB != nullptr) load_y(YB, yb);
+      else static_for<NL>([&](auto I) { yb[I] = T(0); });
+      if (WC != nullptr) load_w<T, L, P>(a, WC, wstride, uc, e, wc);
+      else static_for<NT>([&](auto I) { wc[I] = T(0); });
+      FD::edge(a, __builtin_amdgcn_readfirstlane(e), x, xa, y, yb, w, wc, te);
+    } else {
+      F::edge(a, __builtin_amdgcn_readfirstlane(e), x, y, w, te);
+    }
     static_for<L + 1>([&](auto I) {
       constexpr int l = I;
       if (P::out_l(a, l)) {
@@ -554,6 +644,102 @@ struct Bwd {
   }
 };
 
+// Double backward, second pass (source-sorted rows).  With a, b, c the
+// cotangents of grad_x, grad_Y, grad_W, per path:
+//   dxp = CG(., Y, G), dxq = CG(., b, G), dyp = CG(x, ., G), dyq = CG(a, ., G)
+//   grad_W[p,u]   = a . dxp + x . dxq            (stored at once)
+//   grad_x (row) += W dxq + c dxp
+//   grad_Y (lane)+= W dyq + c dyp                (summed over channels later)
+// Each nonzero costs four FMAs sharing one product |c| * G[m3].
+template <typename T, int L, class P>
+struct BwdDD {
+  static constexpr int NL = (L + 1) * (L + 1);
+  static constexpr int NT = triple_count(L);
+
+  template <int NV>
+  static __device__ __forceinline__ void edge(const KernelArgs& a, int tok, const T (&x)[NL], const T (&xa)[NL],
+                                              const T (&y)[NL], const T (&yb)[NL], const T (&g)[NL],
+                                              const T (&w)[NT], const T (&wc)[NT], T (&dxe)[NL], T (&dya)[NV],
+                                              bool store_dw, T* dwr) {
+    static_assert(NV >= NL, "dY accumulator too short");
+    static_for<L + 1>([&](auto I3) {
+      constexpr int l3 = I3;
+      static_for<L + 1>([&](auto I1) {
+        constexpr int l1 = I1;
+        static_for<L + 1>([&](auto I2) {
+          constexpr int l2 = I2;
+          if constexpr (cg::triangle(l1, l2, l3) && triple_in_class(l1, l2, l3, P::kPar)) {
+            constexpr int t = triple_id(L, l1, l2, l3);
+            if (P::template on<t>(a) && P::template run<t>(a, tok)) {
+              using TI = TabInfo<l1, l2, l3>;
+              constexpr int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1;
+              T dxp[n1], dxq[n1], dyp[n2], dyq[n2];
+              static_for<TI::tab.n>([&](auto K) {
+                constexpr cg::Entry en = TI::tab.e[K];
+                constexpr T mag = T(en.mag);
+                const T cgm = mag * g[l3 * l3 + en.m3];
+                const T cgs = en.neg ? -cgm : cgm;
+                const T yv = y[l2 * l2 + en.m2], bv = yb[l2 * l2 + en.m2];
+                const T xv = x[l1 * l1 + en.m1], av = xa[l1 * l1 + en.m1];
+                if constexpr (TI::first_m1(K)) {
+                  dxp[en.m1] = cgs * yv;
+                  dxq[en.m1] = cgs * bv;
+                } else {
+                  dxp[en.m1] = fmaT(cgs, yv, dxp[en.m1]);
+                  dxq[en.m1] = fmaT(cgs, bv, dxq[en.m1]);
+                }
+                if constexpr (TI::first_m2(K)) {
+                  dyp[en.m2] = cgs * xv;
+                  dyq[en.m2] = cgs * av;
+                } else {
+                  dyp[en.m2] = fmaT(cgs, xv, dyp[en.m2]);
+                  dyq[en.m2] = fmaT(cgs, av, dyq[en.m2]);
+                }
+              });
+              T s = T(0);
+              static_for<n1>([&](auto M1) {
+                if constexpr (TI::has_m1(M1)) {
+                  s = fmaT(xa[l1 * l1 + M1], dxp[M1], s);
+                  s = fmaT(x[l1 * l1 + M1], dxq[M1], s);
+                }
+              });
+              if (store_dw) __builtin_nontemporal_store(s, dwr + P::template woff<t>(a));
+              if (P::template first1<t>(a)) {
+                static_for<n1>([&](auto M1) {
+                  if constexpr (TI::has_m1(M1))
+                    dxe[l1 * l1 + M1] = fmaT(w[t], dxq[M1], wc[t] * dxp[M1]);
+                  else
+                    dxe[l1 * l1 + M1] = T(0);
+                });
+              } else {
+                static_for<n1>([&](auto M1) {
+                  if constexpr (TI::has_m1(M1))
+                    dxe[l1 * l1 + M1] = fmaT(w[t], dxq[M1], fmaT(wc[t], dxp[M1], dxe[l1 * l1 + M1]));
+                });
+              }
+              static_for<n2>([&](auto M2) {
+                if constexpr (TI::has_m2(M2))
+                  dya[l2 * l2 + M2] = fmaT(w[t], dyq[M2], fmaT(wc[t], dyp[M2], dya[l2 * l2 + M2]));
+              });
+            }
+          }
+        });
+      });
+    });
+  }
+};
+
+// Per-edge inputs of the backward kernels: G row of the destination, the
+// edge's Y row and weights, and for the double backward the cotangents b
+// (like Y) and c (like W).
+template <typename T, int L, bool DD>
+struct EdgeIn {
+  static constexpr int NL = (L + 1) * (L + 1);
+  static constexpr int NT = triple_count(L);
+  T g[NL], y[NL], w[NT];
+  T yb[DD ? NL : 1], wc[DD ? NT : 1];
+};
+
 constexpr int pow2_ceil(int n) {
   int p = 1;
   while (p < n) p <<= 1;
@@ -564,14 +750,20 @@ constexpr int pow2_ceil(int n) {
 // where that still fits in 256 VGPRs: fp32 up to l = 2, and l = 3 with the
 // even-parity path set.  Wider kernels already spill to AGPRs with one set,
 // and a second would double that.
-template <typename T, int L, class P>
+template <typename T, int L, class P, bool DD>
 constexpr bool bwd_pipelined() {
-  return sizeof(T) == 4 && (L <= 2 || (L == 3 && P::kPar == kEvenOnly));
+  return !DD && sizeof(T) == 4 && (L <= 2 || (L == 3 && P::kPar == kEvenOnly));
 }
 
-template <typename T, int L, class P>
+// Backward (DD = false): grad_x (out), grad_Y (dY), grad_W (dW) of <G, out>.
+// Double backward's second pass (DD = true): the same three outputs of
+// <a, dx> + <b, dY> + <c, dW>, with the cotangents a (row-resident like x),
+// b and c; a null cotangent reads as zeros.
+template <typename T, int L, class P, bool DD>
 __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
   using B = Bwd<T, L, P>;
+  using BD = BwdDD<T, L, P>;
+  using In = EdgeIn<T, L, DD>;
   using A = typename RowAcc<T>::type;
   constexpr int NL = B::NL, NT = B::NT;
   constexpr int NV = pow2_ceil(NL);  // dY values, padded to a power of two for the reduce-scatter
@@ -593,25 +785,32 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
   T* __restrict__ DX = static_cast<T*>(a.out);
   T* __restrict__ DY = static_cast<T*>(a.dY);
   T* __restrict__ DW = static_cast<T*>(a.dW);
+  const T* __restrict__ XA = static_cast<const T*>(a.xa);
+  const T* __restrict__ YB = static_cast<const T*>(a.Yb);
+  const T* __restrict__ WC = static_cast<const T*>(a.Wc);
   const int d_out = P::d_out(a), d_sh = P::d_sh(a);
   const int64_t wstride = P::wstride(a);
 
-  // this source node's features stay in registers for the whole row; idle
-  // lanes hold zeros so they add nothing to the channel sums of dY
-  T x[NL];
-  {
-    const T* xr = X + (int64_t)node * P::d_in(a);
+  // this source node's features (and for the double backward its cotangent
+  // a) stay in registers for the whole row; idle lanes hold zeros so they
+  // add nothing to the channel sums of dY
+  auto load_row = [&](const T* __restrict__ base, bool present, T (&v)[NL]) {
+    const T* xr = base + (int64_t)node * P::d_in(a);
     static_for<L + 1>([&](auto I) {
       constexpr int l = I;
       const int off = P::in_off(a, l);
       static_for<2 * l + 1>([&](auto M) {
-        if (off >= 0 && chan_ok) x[l * l + M] = xr[off + u * (2 * l + 1) + M];
-        else x[l * l + M] = T(0);
+        if (off >= 0 && chan_ok && present) v[l * l + M] = xr[off + u * (2 * l + 1) + M];
+        else v[l * l + M] = T(0);
       });
     });
     // wait for the row here, before any dW / dY store is in flight
-    static_for<NL>([&](auto I) { pin_vgpr(x[I]); });
-  }
+    static_for<NL>([&](auto I) { pin_vgpr(v[I]); });
+  };
+  T x[NL];
+  T xa[DD ? NL : 1];
+  load_row(X, true, x);
+  if constexpr (DD) load_row(XA, XA != nullptr, xa);
   A dxa[NL];
   static_for<NL>([&](auto I) { dxa[I] = A(0); });
 
@@ -636,31 +835,41 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
     pin_vgpr(my_e);
     pin_vgpr(my_i);
   };
-  auto load_edge = [&](int e, int i, T (&g)[NL], T (&y)[NL], T (&w)[NT]) {
-    const T* gr = Gp + (int64_t)i * d_out;
-    static_for<L + 1>([&](auto I) {
-      constexpr int l = I;
-      const int off = P::out_off(a, l);
-      static_for<2 * l + 1>([&](auto M) {
-        if (off >= 0) g[l * l + M] = gr[off + uc * (2 * l + 1) + M];
-        else g[l * l + M] = T(0);
-      });
-    });
-    const T* yr = Yp + (int64_t)e * d_sh;
+  auto load_y = [&](const T* __restrict__ base, bool present, int e, T (&y)[NL]) {
+    const T* yr = base + (int64_t)e * d_sh;
     static_for<NL>([&](auto I) {
-      if (I < d_sh) y[I] = ldg_stream(yr + I);
+      if (I < d_sh && present) y[I] = ldg_stream(yr + I);
       else y[I] = T(0);
     });
-    const T* wr = Wp + (int64_t)e * wstride + uc;
+  };
+  auto load_wrow = [&](const T* __restrict__ base, bool present, int e, T (&w)[NT]) {
+    const T* wr = base + (int64_t)e * wstride + uc;
     static_for<NT>([&](auto I) {
       constexpr TripleInfo ti = triple_at(L, I);
       if constexpr (triple_in_class(ti.l1, ti.l2, ti.l3, P::kPar)) {
-        if (P::template on<I>(a)) w[I] = ldg_stream(wr + P::template woff<I>(a));
+        if (P::template on<I>(a) && present) w[I] = ldg_stream(wr + P::template woff<I>(a));
         else w[I] = T(0);
       } else {
         w[I] = T(0);
       }
     });
+  };
+  auto load_edge = [&](int e, int i, In& in) {
+    const T* gr = Gp + (int64_t)i * d_out;
+    static_for<L + 1>([&](auto I) {
+      constexpr int l = I;
+      const int off = P::out_off(a, l);
+      static_for<2 * l + 1>([&](auto M) {
+        if (off >= 0) in.g[l * l + M] = gr[off + uc * (2 * l + 1) + M];
+        else in.g[l * l + M] = T(0);
+      });
+    });
+    load_y(Yp, true, e, in.y);
+    load_wrow(Wp, true, e, in.w);
+    if constexpr (DD) {
+      load_y(YB, YB != nullptr, e, in.yb);
+      load_wrow(WC, WC != nullptr, e, in.wc);
+    }
   };
 
   // Two register sets for the edge inputs, used alternately, so the step
@@ -668,23 +877,27 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
   // Loads and arithmetic run unconditionally: a slot past the end of the row
   // reads edge 0 / node 0 (its ids are 0) and only its stores and its share
   // of dx are masked, which keeps every load out of divergent control flow.
-  auto prefetch = [&](int k, int& e, bool& valid, T (&g)[NL], T (&y)[NL], T (&w)[NT]) {
+  auto prefetch = [&](int k, int& e, bool& valid, In& in) {
     const int r = k & chunk_mask;
     if (r == 0) fetch_ids(k);
     const int q = (r << lgs) + slot;
     e = __shfl(my_e, q, 64);
     const int i = __shfl(my_i, q, 64);
     valid = (k << lgs) + slot < deg;
-    load_edge(e, i, g, y, w);
+    load_edge(e, i, in);
   };
-  auto compute = [&](const int e, const bool valid, const T (&g)[NL], const T (&y)[NL], const T (&w)[NT]) {
+  auto compute = [&](const int e, const bool valid, const In& in) {
     T dya[NV], dxe[NL];
     static_for<NV>([&](auto I) { dya[I] = T(0); });
     // idle lanes (u >= U) aim their dW stores at channel 0 of the same row
     // and store only when chan_ok; for a power-of-two U every lane is active
     const bool store_dw = DW != nullptr;
     T* dwr = store_dw ? DW + (int64_t)e * wstride + uc : nullptr;
-    B::edge(a, __builtin_amdgcn_readfirstlane(e), x, y, g, w, dxe, dya, store_dw && chan_ok && valid, dwr);
+    const bool st = store_dw && chan_ok && valid;
+    if constexpr (DD)
+      BD::edge(a, __builtin_amdgcn_readfirstlane(e), x, xa, in.y, in.yb, in.g, in.w, in.wc, dxe, dya, st, dwr);
+    else
+      B::edge(a, __builtin_amdgcn_readfirstlane(e), x, in.y, in.g, in.w, dxe, dya, st, dwr);
     static_for<L + 1>([&](auto I) {
       constexpr int l = I;
       if (P::in_l(a, l)) {
@@ -736,25 +949,25 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
     }
   };
 
-  T ga[NL], ya[NL], wa[NT];
+  In ia;
   int ea = 0;
   bool va = false;
-  if constexpr (bwd_pipelined<T, L, P>()) {
-    T gb[NL], yb[NL], wb[NT];
+  if constexpr (bwd_pipelined<T, L, P, DD>()) {
+    In ib;
     int eb = 0;
     bool vb = false;
-    if (n_steps > 0) prefetch(0, ea, va, ga, ya, wa);
+    if (n_steps > 0) prefetch(0, ea, va, ia);
     for (int k = 0; k < n_steps; k += 2) {  // wave-uniform trip count
-      prefetch(k + 1, eb, vb, gb, yb, wb);
-      compute(ea, va, ga, ya, wa);
+      prefetch(k + 1, eb, vb, ib);
+      compute(ea, va, ia);
       if (k + 1 >= n_steps) break;
-      prefetch(k + 2, ea, va, ga, ya, wa);
-      compute(eb, vb, gb, yb, wb);
+      prefetch(k + 2, ea, va, ia);
+      compute(eb, vb, ib);
     }
   } else {
     for (int k = 0; k < n_steps; ++k) {
-      prefetch(k, ea, va, ga, ya, wa);
-      compute(ea, va, ga, ya, wa);
+      prefetch(k, ea, va, ia);
+      compute(ea, va, ia);
     }
   }
 
@@ -776,12 +989,14 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
 }
 
 // ---------------------------------------------------------------- launchers
+constexpr bool kDD = TPCONV_DD != 0;
+
 template <typename T, class P>
 hipError_t launch_fwd(const KernelArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
   const int waves_per_block = 4;
   const int blocks = (a.n_rows + waves_per_block - 1) / waves_per_block;
-  hipLaunchKernelGGL((fwd_kernel<T, TPCONV_L, P>), dim3(blocks), dim3(64 * waves_per_block), 0, s, a);
+  hipLaunchKernelGGL((fwd_kernel<T, TPCONV_L, P, kDD>), dim3(blocks), dim3(64 * waves_per_block), 0, s, a);
   return hipGetLastError();
 }
 
@@ -790,7 +1005,7 @@ hipError_t launch_bwd(const KernelArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
   const int waves_per_block = 4;
   const int blocks = (a.n_rows + waves_per_block - 1) / waves_per_block;
-  hipLaunchKernelGGL((bwd_kernel<T, TPCONV_L, P>), dim3(blocks), dim3(64 * waves_per_block), 0, s, a);
+  hipLaunchKernelGGL((bwd_kernel<T, TPCONV_L, P, kDD>), dim3(blocks), dim3(64 * waves_per_block), 0, s, a);
   return hipGetLastError();
 }
 
@@ -842,12 +1057,22 @@ hipError_t dispatch(const KernelArgs& a, hipStream_t s) {
 #define TPCONV_CAT(a, b) TPCONV_CAT2(a, b)
 #define TPCONV_LNAME(stem, ty) TPCONV_CAT(TPCONV_CAT(stem, TPCONV_L), ty)
 
+#if TPCONV_DD
+#if TPCONV_DOUBLE
+hipError_t TPCONV_LNAME(launch_ddf_l, _f64)(const KernelArgs& a, hipStream_t s) { return dispatch<double, true>(a, s); }
+hipError_t TPCONV_LNAME(launch_ddb_l, _f64)(const KernelArgs& a, hipStream_t s) { return dispatch<double, false>(a, s); }
+#else
+hipError_t TPCONV_LNAME(launch_ddf_l, _f32)(const KernelArgs& a, hipStream_t s) { return dispatch<float, true>(a, s); }
+hipError_t TPCONV_LNAME(launch_ddb_l, _f32)(const KernelArgs& a, hipStream_t s) { return dispatch<float, false>(a, s); }
+#endif
+#else
 #if TPCONV_DOUBLE
 hipError_t TPCONV_LNAME(launch_fwd_l, _f64)(const KernelArgs& a, hipStream_t s) { return dispatch<double, true>(a, s); }
 hipError_t TPCONV_LNAME(launch_bwd_l, _f64)(const KernelArgs& a, hipStream_t s) { return dispatch<double, false>(a, s); }
 #else
 hipError_t TPCONV_LNAME(launch_fwd_l, _f32)(const KernelArgs& a, hipStream_t s) { return dispatch<float, true>(a, s); }
 hipError_t TPCONV_LNAME(launch_bwd_l, _f32)(const KernelArgs& a, hipStream_t s) { return dispatch<float, false>(a, s); }
+#endif
 #endif
 
 }  // namespace tpconv

@@ -28,7 +28,7 @@ STATUS = {0: "TPCONV_OK", 1: "TPCONV_E_INVALID_ARG", 2: "TPCONV_E_IRREPS", 3: "T
 
 EXPORTS = ("tpconv_plan", "tpconv_plan_query", "tpconv_plan_paths", "tpconv_plan_table", "tpconv_plan_destroy",
            "tpconv_graph_workspace_bytes", "tpconv_graph_create", "tpconv_graph_export", "tpconv_graph_destroy",
-           "tpconv_forward", "tpconv_backward", "tpconv_last_error")
+           "tpconv_forward", "tpconv_backward", "tpconv_double_backward", "tpconv_last_error")
 
 
 class TPConvError(RuntimeError):
@@ -63,6 +63,7 @@ def _load():
         "tpconv_graph_destroy": (None, [vp]),
         "tpconv_forward": (i32, [vp, vp, vp, vp, vp, vp, vp]),
         "tpconv_backward": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "tpconv_double_backward": (i32, [vp] * 14),
         "tpconv_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -241,3 +242,35 @@ def tpconv_backward(plan: Plan, graph: Graph, x, Y, W, grad_out, grad_x=None, gr
     _check(_lib.tpconv_backward(plan.handle, graph.handle, _ptr(x), _ptr(Y), _ptr(W), _ptr(grad_out),
                                 _ptr(grad_x), _ptr(grad_Y), _ptr(grad_W), _stream_handle(stream)))
     return grad_x, grad_Y, grad_W
+
+
+def tpconv_double_backward(plan: Plan, graph: Graph, x, Y, W, grad_out, ggx=None, ggY=None, ggW=None,
+                           grad_x=None, grad_Y=None, grad_W=None, grad_G=None,
+                           need=(True, True, True, True), stream=None) -> Tuple[Optional[torch.Tensor], ...]:
+    """Gradients of <ggx, dx> + <ggY, dY> + <ggW, dW> (dx, dY, dW = the backward
+    of x, Y, W, grad_out) with respect to x, Y, W and grad_out.
+
+    ggx / ggY / ggW may be None (zero).  Returns (grad_x, grad_Y, grad_W,
+    grad_G); an output is None when `need` turns it off."""
+    N, E, dt = graph.n_nodes, graph.n_edges, plan.torch_dtype
+    _need(x, (N, plan.dim_in), dt, "x")
+    _need(Y, (E, plan.dim_sh), dt, "Y")
+    _need(W, (E, plan.weight_numel), dt, "W")
+    if grad_out is not None:
+        _need(grad_out, (N, plan.dim_out), dt, "grad_out")
+    for t, shp, nm in ((ggx, (N, plan.dim_in), "ggx"), (ggY, (E, plan.dim_sh), "ggY"),
+                       (ggW, (E, plan.weight_numel), "ggW")):
+        if t is not None:
+            _need(t, shp, dt, nm)
+    dev = x.device
+    shapes = ((N, plan.dim_in), (E, plan.dim_sh), (E, plan.weight_numel), (N, plan.dim_out))
+    outs = [grad_x, grad_Y, grad_W, grad_G]
+    for k in range(4):
+        if need[k] and outs[k] is None:
+            outs[k] = torch.empty(shapes[k], dtype=dt, device=dev)
+        if outs[k] is not None:
+            _need(outs[k], shapes[k], dt, ("grad_x", "grad_Y", "grad_W", "grad_G")[k])
+    _check(_lib.tpconv_double_backward(plan.handle, graph.handle, _ptr(x), _ptr(Y), _ptr(W), _ptr(grad_out),
+                                       _ptr(ggx), _ptr(ggY), _ptr(ggW), _ptr(outs[0]), _ptr(outs[1]),
+                                       _ptr(outs[2]), _ptr(outs[3]), _stream_handle(stream)))
+    return tuple(outs)

@@ -185,6 +185,34 @@ tpconv_status tpconv_backward(tpconv_plan_t plan, tpconv_graph_t g, const void* 
                               const void* W, const void* grad_out, void* grad_x, void* grad_Y,
                               void* grad_W, hipStream_t stream);
 
+/* tpconv_double_backward: the backward of tpconv_backward -- second
+ * derivatives for force-trained potentials (the FlashTP page lists an fp64
+ * l_max = 4 double-backward kernel among its key results; the LunaTP and
+ * TrimSO(2) abstracts count higher-order derivatives / double backward as
+ * part of training).
+ * With (dx, dY, dW) = tpconv_backward(x, Y, W, G) and their cotangents
+ *   ggx [N][D_in], ggY [E][D_sh], ggW [E][weight_numel]
+ * (any may be NULL, meaning zero), it returns the gradients of
+ *   L2 = <ggx, dx> + <ggY, dY> + <ggW, dW>
+ * with respect to the four inputs:
+ *   grad_x [N][D_in], grad_Y [E][D_sh], grad_W [E][weight_numel],
+ *   grad_G [N][D_out]  (G = grad_out of the backward).
+ * Because the convolution is linear in each input separately, each is the
+ * forward or backward with one input replaced by a cotangent, summed:
+ *   grad_G = out(ggx, Y, W) + out(x, ggY, W) + out(x, Y, ggW)
+ *   grad_x = dx(Y -> ggY) + dx(W -> ggW),  grad_Y = dY(x -> ggx) + dY(W -> ggW),
+ *   grad_W = dW(x -> ggx) + dW(Y -> ggY).
+ * Two fused kernels: grad_G over the destination-sorted CSR (the forward's
+ * structure), the other three over the source-sorted CSR (the backward's).
+ * Layouts as tpconv_forward / tpconv_backward.  Each output is overwritten;
+ * pass NULL to skip one (grad_G alone skips the second kernel, and the
+ * other three alone skip the first).  grad_out may be NULL only when grad_x,
+ * grad_Y and grad_W are all NULL.  Errors as tpconv_forward. */
+tpconv_status tpconv_double_backward(tpconv_plan_t plan, tpconv_graph_t g, const void* x, const void* Y,
+                                     const void* W, const void* grad_out, const void* ggx, const void* ggY,
+                                     const void* ggW, void* grad_x, void* grad_Y, void* grad_W, void* grad_G,
+                                     hipStream_t stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* tpconv_last_error(void);
 

@@ -193,6 +193,19 @@ def make_inputs(w: Workload, n_paths: int, weight_numel: int):
     return g
 
 
+def make_cotangents(w: Workload, n_edges: int, weight_numel: int):
+    """Cotangents of the backward's outputs, the double backward's extra inputs:
+    ggx [N, D_in], ggY [E, (L+1)^2], ggW [E, weight_numel], standard normal in
+    the workload's dtype, from their own seeded stream (make_inputs' draws are
+    unchanged by it)."""
+    rng = rng_for(w.key, stream=2)
+    dt = w.np_dtype
+    ggx = rng.standard_normal((w.n_atoms, dim_of(w.irreps_in)), dtype=dt)
+    ggY = rng.standard_normal((n_edges, (w.sh_lmax + 1) ** 2), dtype=dt)
+    ggW = rng.standard_normal((n_edges, weight_numel), dtype=dt)
+    return dict(ggx=ggx, ggY=ggY, ggW=ggW)
+
+
 def random_rotation(rng: np.random.Generator) -> np.ndarray:
     """Uniform random proper rotation (QR of a Gaussian matrix, sign-fixed)."""
     q, r = np.linalg.qr(rng.standard_normal((3, 3)))
