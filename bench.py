@@ -8,7 +8,9 @@ parity-allowed paths, fp32, seeded synthetic inputs resident in HBM.
 
 Prints one JSON line: edges/s (value), per-kernel times, the dominant
 kernel's roofline point, and the fp64 CPU oracle timed on a bounded sample
-of the same workload.
+of the same workload.  Outside the timed steps it also reports cold-cache
+kernel times (1 GiB read before each step) and the double backward's two
+kernels (tpconv_double_backward with seeded cotangents).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -41,6 +43,8 @@ def parse():
     p.add_argument("--cold-reps", type=int, default=20,
                    help="after the timed steps, this many extra steps each preceded by reading a 1 GiB buffer "
                         "(evicts the 256 MB Infinity Cache); kernel medians reported as kernels_ms_cold")
+    p.add_argument("--dd-reps", type=int, default=20,
+                   help="timed double-backward calls after the fwd+bwd steps (0 skips); reported as double_backward")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="also run one plain device copy of this many MiB (scales rocprofv3 FETCH/WRITE_SIZE)")
     return p.parse_args()
@@ -52,6 +56,17 @@ def algorithmic_bytes(plan, n_nodes, n_edges, b):
     fwd = n_edges * ((PU + Dsh) * b + 4) + n_nodes * ((plan.dim_in + plan.dim_out) * b + 4)
     bwd = n_edges * ((2 * PU + 2 * Dsh) * b + 8) + n_nodes * ((2 * plan.dim_in + plan.dim_out) * b + 4)
     return fwd, bwd
+
+
+def dd_algorithmic_bytes(plan, n_nodes, n_edges, b):
+    """Double backward, compulsory bytes of its two kernels: grad_G pass (reads W, ggW,
+    Y, ggY per edge; x, ggx per node; writes grad_G) and the grad_x / grad_Y / grad_W
+    pass (reads W, ggW, Y, ggY and writes grad_W, grad_Y per edge; reads x, ggx, G and
+    writes grad_x per node)."""
+    PU, Dsh, Din, Dout = plan.weight_numel, plan.dim_sh, plan.dim_in, plan.dim_out
+    ddf = n_edges * ((2 * PU + 2 * Dsh) * b + 4) + n_nodes * ((2 * Din + Dout) * b + 4)
+    ddb = n_edges * ((3 * PU + 3 * Dsh) * b + 8) + n_nodes * ((3 * Din + Dout) * b + 4)
+    return ddf, ddb
 
 
 def kernel_source_hash():
@@ -189,6 +204,42 @@ def main():
                 "evict": "1 GiB device read (torch.sum) before each step"}
         del evict
 
+    dd = None
+    if args.dd_reps > 0:
+        # double backward: the grad_G kernel and the grad_x / grad_Y / grad_W
+        # kernel timed separately (two calls, each asking for its outputs)
+        ct = workloads.make_cotangents(w, E, plan.weight_numel)
+        ga, gb, gc = T(ct["ggx"]), T(ct["ggY"]), T(ct["ggW"])
+        del ct
+        gx_, gY_, gW_ = torch.empty_like(dx), torch.empty_like(dY), torch.empty_like(dW)
+        gG_ = torch.empty((N, plan.dim_out), dtype=plan.torch_dtype, device=dev)
+
+        def dd_call(ev0, ev1, ev2):
+            ev0.record(stream)
+            tp.tpconv_double_backward(plan, graph, x, Y, W, G, ga, gb, gc, grad_G=gG_,
+                                      need=(False, False, False, True))
+            ev1.record(stream)
+            tp.tpconv_double_backward(plan, graph, x, Y, W, G, ga, gb, gc, gx_, gY_, gW_,
+                                      need=(True, True, True, False))
+            ev2.record(stream)
+
+        dev_ = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.dd_reps + 2)]
+        for k in range(args.dd_reps + 2):   # the first two are warm-up
+            dd_call(*dev_[k])
+        torch.cuda.synchronize()
+        f_ms = np.array([e[0].elapsed_time(e[1]) for e in dev_[2:]])
+        b_ms = np.array([e[1].elapsed_time(e[2]) for e in dev_[2:]])
+        ddf_bytes, ddb_bytes = dd_algorithmic_bytes(plan, N, E, 4 if w.dtype == "f32" else 8)
+        tot = float(np.median(f_ms + b_ms))
+        dd = {"grad_G_kernel_ms_median": round(float(np.median(f_ms)), 4),
+              "grad_xYW_kernel_ms_median": round(float(np.median(b_ms)), 4),
+              "total_ms_median": round(tot, 4), "reps": args.dd_reps,
+              "edges_per_s": round(E / (tot * 1e-3), 1),
+              "algorithmic_bytes": {"grad_G_kernel": int(ddf_bytes), "grad_xYW_kernel": int(ddb_bytes)},
+              "algorithmic_GBps": round((ddf_bytes + ddb_bytes) / (tot * 1e-3) / 1e9, 1),
+              "frac_of_peak": round((ddf_bytes + ddb_bytes) / (tot * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del ga, gb, gc, gx_, gY_, gW_, gG_
+
     b = 4 if w.dtype == "f32" else 8
     fwd_bytes, bwd_bytes = algorithmic_bytes(plan, N, E, b)
     f_avg, b_avg = float(fwd_ms.mean()), float(bwd_ms.mean())
@@ -216,6 +267,7 @@ def main():
                        "backward_avg": round(b_avg, 4), "backward_median": round(float(np.median(bwd_ms)), 4),
                        "backward_min": round(float(bwd_ms.min()), 4)},
         "kernels_ms_cold": cold,
+        "double_backward": dd,
         "hbm": {"fwd_bwd_algorithmic_GBps": round(hbm_fwdbwd, 1), "frac_of_peak": round(hbm_fwdbwd / HBM_PEAK_GBS, 4),
                 "fwd_bytes": int(fwd_bytes), "bwd_bytes": int(bwd_bytes)},
         "roofline": roofline,
