@@ -25,6 +25,7 @@ Modules:
   cg      -- complex CG by Racah's closed form, real-basis CG.
   sh      -- real spherical harmonics built from scipy's complex ones.
   tp      -- dense per-edge forward, backward and double backward.
+  forces  -- edge SH with their gradient, and the position gradient.
 
 Every function here is pinned by a test in ``tests/test_oracle_*.py`` against
 mathematics it does not itself use (library routines, closed forms,
@@ -35,3 +36,4 @@ from .irreps import Irreps, parse_irreps, enumerate_paths  # noqa: F401
 from .cg import cg_complex, real_basis_U, cg_real  # noqa: F401
 from .sh import sh_complex, sh_real  # noqa: F401
 from .tp import TPProblem, tp_forward, tp_backward, tp_double_backward  # noqa: F401
+from .forces import sh_and_jacobian, sh_edges, sh_backward, positions_backward  # noqa: F401
