@@ -47,6 +47,7 @@ def _jobs():
                               os.path.join(BUILD, f"{stem}_l{L}_{'f64' if dbl else 'f32'}.o"),
                               [f"-DTPCONV_L={L}", f"-DTPCONV_DOUBLE={dbl}", f"-DTPCONV_DD={dd}"]))
     units.append((os.path.join(CSRC, "graph.hip"), os.path.join(BUILD, "graph.o"), []))
+    units.append((os.path.join(CSRC, "sh.hip"), os.path.join(BUILD, "sh.o"), []))
     # the host CG builder runs without FMA contraction so its run-time values
     # are bit-identical to the kernels' compile-time evaluation
     units.append((os.path.join(CSRC, "plan.cpp"), os.path.join(BUILD, "plan.o"), ["-ffp-contract=off"]))

@@ -208,3 +208,38 @@ extern "C" tpconv_status tpconv_double_backward(tpconv_plan_t hp, tpconv_graph_t
   }
   return TPCONV_OK;
 }
+
+extern "C" tpconv_status tpconv_sh(tpconv_plan_t hp, int64_t n_edges, const void* vec, void* Y, hipStream_t stream) {
+  if (hp == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL plan");
+  if (n_edges < 0) return fail(TPCONV_E_INVALID_ARG, "n_edges < 0");
+  if (n_edges > 0 && (vec == nullptr || Y == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL vec or Y");
+  const Plan& p = *reinterpret_cast<const Plan*>(hp);
+  const hipError_t he = launch_sh(p.sh_lmax, p.dtype == TPCONV_F64, n_edges, vec, Y, stream);
+  if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("sh launch: ") + hipGetErrorString(he));
+  return TPCONV_OK;
+}
+
+extern "C" tpconv_status tpconv_sh_backward(tpconv_plan_t hp, int64_t n_edges, const void* vec, const void* grad_Y,
+                                            void* grad_vec, hipStream_t stream) {
+  if (hp == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL plan");
+  if (n_edges < 0) return fail(TPCONV_E_INVALID_ARG, "n_edges < 0");
+  if (n_edges > 0 && (vec == nullptr || grad_Y == nullptr || grad_vec == nullptr))
+    return fail(TPCONV_E_INVALID_ARG, "NULL vec, grad_Y or grad_vec");
+  const Plan& p = *reinterpret_cast<const Plan*>(hp);
+  const hipError_t he = launch_sh_backward(p.sh_lmax, p.dtype == TPCONV_F64, n_edges, vec, grad_Y, grad_vec, stream);
+  if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("sh backward launch: ") + hipGetErrorString(he));
+  return TPCONV_OK;
+}
+
+extern "C" tpconv_status tpconv_positions_backward(tpconv_plan_t hp, tpconv_graph_t hg, const void* grad_vec,
+                                                   void* grad_pos, hipStream_t stream) {
+  if (hp == nullptr || hg == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL plan or graph");
+  const Plan& p = *reinterpret_cast<const Plan*>(hp);
+  const Graph& g = *reinterpret_cast<const Graph*>(hg);
+  if (g.n_nodes > 0 && grad_pos == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL grad_pos");
+  if (g.n_edges > 0 && grad_vec == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL grad_vec");
+  const hipError_t he = launch_pos_backward(p.dtype == TPCONV_F64, g.n_nodes, g.src_row, g.src_eid, g.dst_row,
+                                            g.dst_eid, grad_vec, grad_pos, stream);
+  if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("positions backward launch: ") + hipGetErrorString(he));
+  return TPCONV_OK;
+}

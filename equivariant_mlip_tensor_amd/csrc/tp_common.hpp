@@ -99,4 +99,12 @@ TPCONV_DECLARE_LAUNCHERS(2)
 TPCONV_DECLARE_LAUNCHERS(3)
 TPCONV_DECLARE_LAUNCHERS(4)
 
+// Edge harmonics, their gradient and the position gradient (sh.hip).
+hipError_t launch_sh(int L, bool f64, int64_t n_edges, const void* vec, void* Y, hipStream_t s);
+hipError_t launch_sh_backward(int L, bool f64, int64_t n_edges, const void* vec, const void* grad_Y, void* grad_vec,
+                              hipStream_t s);
+hipError_t launch_pos_backward(bool f64, int64_t n_nodes, const int32_t* src_row, const int32_t* src_eid,
+                               const int32_t* dst_row, const int32_t* dst_eid, const void* grad_vec, void* grad_pos,
+                               hipStream_t s);
+
 }  // namespace tpconv

@@ -28,7 +28,8 @@ STATUS = {0: "TPCONV_OK", 1: "TPCONV_E_INVALID_ARG", 2: "TPCONV_E_IRREPS", 3: "T
 
 EXPORTS = ("tpconv_plan", "tpconv_plan_query", "tpconv_plan_paths", "tpconv_plan_table", "tpconv_plan_destroy",
            "tpconv_graph_workspace_bytes", "tpconv_graph_create", "tpconv_graph_export", "tpconv_graph_destroy",
-           "tpconv_forward", "tpconv_backward", "tpconv_double_backward", "tpconv_last_error")
+           "tpconv_forward", "tpconv_backward", "tpconv_double_backward", "tpconv_sh", "tpconv_sh_backward",
+           "tpconv_positions_backward", "tpconv_last_error")
 
 
 class TPConvError(RuntimeError):
@@ -64,6 +65,9 @@ def _load():
         "tpconv_forward": (i32, [vp, vp, vp, vp, vp, vp, vp]),
         "tpconv_backward": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "tpconv_double_backward": (i32, [vp] * 14),
+        "tpconv_sh": (i32, [vp, i64, vp, vp, vp]),
+        "tpconv_sh_backward": (i32, [vp, i64, vp, vp, vp, vp]),
+        "tpconv_positions_backward": (i32, [vp, vp, vp, vp, vp]),
         "tpconv_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -274,3 +278,39 @@ def tpconv_double_backward(plan: Plan, graph: Graph, x, Y, W, grad_out, ggx=None
                                        _ptr(ggx), _ptr(ggY), _ptr(ggW), _ptr(outs[0]), _ptr(outs[1]),
                                        _ptr(outs[2]), _ptr(outs[3]), _stream_handle(stream)))
     return tuple(outs)
+
+
+# ------------------------------------------------- upstream: harmonics, forces
+def tpconv_sh(plan: Plan, vec, Y=None, stream=None) -> torch.Tensor:
+    """Y [E, (sh_lmax+1)^2] of the edge vectors vec [E, 3] (plan dtype)."""
+    E = vec.shape[0] if vec.dim() == 2 else -1
+    _need(vec, (E, 3), plan.torch_dtype, "vec")
+    if Y is None:
+        Y = torch.empty((E, plan.dim_sh), dtype=plan.torch_dtype, device=vec.device)
+    _need(Y, (E, plan.dim_sh), plan.torch_dtype, "Y")
+    _check(_lib.tpconv_sh(plan.handle, E, _ptr(vec), _ptr(Y), _stream_handle(stream)))
+    return Y
+
+
+def tpconv_sh_backward(plan: Plan, vec, grad_Y, grad_vec=None, stream=None) -> torch.Tensor:
+    """grad_vec [E, 3] from grad_Y [E, (sh_lmax+1)^2]."""
+    E = vec.shape[0] if vec.dim() == 2 else -1
+    _need(vec, (E, 3), plan.torch_dtype, "vec")
+    _need(grad_Y, (E, plan.dim_sh), plan.torch_dtype, "grad_Y")
+    if grad_vec is None:
+        grad_vec = torch.empty((E, 3), dtype=plan.torch_dtype, device=vec.device)
+    _need(grad_vec, (E, 3), plan.torch_dtype, "grad_vec")
+    _check(_lib.tpconv_sh_backward(plan.handle, E, _ptr(vec), _ptr(grad_Y), _ptr(grad_vec), _stream_handle(stream)))
+    return grad_vec
+
+
+def tpconv_positions_backward(plan: Plan, graph: Graph, grad_vec, grad_pos=None, stream=None) -> torch.Tensor:
+    """grad_pos [N, 3] for vec[e] = pos[src[e]] - pos[dst[e]] (+ constant shift)."""
+    N, E = graph.n_nodes, graph.n_edges
+    _need(grad_vec, (E, 3), plan.torch_dtype, "grad_vec")
+    if grad_pos is None:
+        grad_pos = torch.empty((N, 3), dtype=plan.torch_dtype, device=grad_vec.device)
+    _need(grad_pos, (N, 3), plan.torch_dtype, "grad_pos")
+    _check(_lib.tpconv_positions_backward(plan.handle, graph.handle, _ptr(grad_vec), _ptr(grad_pos),
+                                          _stream_handle(stream)))
+    return grad_pos

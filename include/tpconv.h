@@ -213,6 +213,38 @@ tpconv_status tpconv_double_backward(tpconv_plan_t plan, tpconv_graph_t g, const
                                      const void* ggW, void* grad_x, void* grad_Y, void* grad_W, void* grad_G,
                                      hipStream_t stream);
 
+/* ------------------------------------------- upstream: harmonics, forces --
+ * The step before the convolution in a force field: the edge harmonics Y
+ * from the edge vectors, and the chain rule from grad_Y back to the edge
+ * vectors and the atom positions (forces are -dE/dpos).  The LunaTP and
+ * TrimSO(2) abstracts place the operator in force-field training; the pages
+ * give no formula for this step, which follows from the harmonics'
+ * definition.  Separate streaming kernels (not fused into the convolution,
+ * whose kernels are bound by arithmetic issue).
+ *
+ * tpconv_sh: Y[E][(L+1)^2] (L = the plan's sh_lmax, plan dtype) =
+ * component-normalised real harmonics of vec[e] / |vec[e]|, (l, m) at column
+ * l*l + l + m, the convention of the plan's CG tables (Y_0 = 1,
+ * Y_1 = sqrt(3) (y, z, x)).  vec: device [E][3] in the plan's dtype.  A zero
+ * vector gets Y = (1, 0, ..., 0).  Errors: TPCONV_E_INVALID_ARG (NULL plan,
+ * NULL pointer with n_edges > 0, n_edges < 0), TPCONV_E_HIP. */
+tpconv_status tpconv_sh(tpconv_plan_t plan, int64_t n_edges, const void* vec, void* Y, hipStream_t stream);
+
+/* tpconv_sh_backward: grad_vec[E][3] = sum over (l, m) of
+ * grad_Y[e][lm] * dY_lm/dvec at vec[e] (zero for a zero vector).  grad_Y
+ * [E][(L+1)^2].  Errors as tpconv_sh. */
+tpconv_status tpconv_sh_backward(tpconv_plan_t plan, int64_t n_edges, const void* vec, const void* grad_Y,
+                                 void* grad_vec, hipStream_t stream);
+
+/* tpconv_positions_backward: grad_pos[N][3] for edge vectors
+ * vec[e] = pos[src[e]] - pos[dst[e]] (+ any shift that does not depend on
+ * pos): grad_pos[j] = sum of grad_vec over the edges leaving j minus the sum
+ * over the edges entering j, over the graph's two CSR views (one wavefront
+ * per node, fixed order, deterministic; fp64 sums for fp32 data).
+ * grad_vec: [E][3]; grad_pos is overwritten.  Errors as tpconv_sh. */
+tpconv_status tpconv_positions_backward(tpconv_plan_t plan, tpconv_graph_t g, const void* grad_vec, void* grad_pos,
+                                        hipStream_t stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* tpconv_last_error(void);
 

@@ -36,7 +36,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(tp):
     declared = header_functions()
-    assert len(declared) == 13
+    assert len(declared) == 16
     assert sorted(tp.EXPORTS) == declared
     lib = ctypes.CDLL(LIB)
     for name in declared:
@@ -126,6 +126,9 @@ def test_null_and_size_errors_need_no_gpu(tp):
     assert lib.tpconv_forward(None, None, None, None, None, None, None) == 1
     assert lib.tpconv_backward(None, None, None, None, None, None, None, None, None, None) == 1
     assert lib.tpconv_double_backward(*([None] * 14)) == 1
+    assert lib.tpconv_sh(None, 0, None, None, None) == 1
+    assert lib.tpconv_sh_backward(None, 0, None, None, None, None) == 1
+    assert lib.tpconv_positions_backward(None, None, None, None, None) == 1
     assert lib.tpconv_graph_workspace_bytes(-1, 5) == 0
     ws = tp.tpconv_graph_workspace_bytes(10, 100)
     assert ws >= 4 * (2 * 11 + 4 * 100 + 2 * 10 + 1)
