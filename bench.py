@@ -9,8 +9,9 @@ parity-allowed paths, fp32, seeded synthetic inputs resident in HBM.
 Prints one JSON line: edges/s (value), per-kernel times, the dominant
 kernel's roofline point, and the fp64 CPU oracle timed on a bounded sample
 of the same workload.  Outside the timed steps it also reports cold-cache
-kernel times (1 GiB read before each step) and the double backward's two
-kernels (tpconv_double_backward with seeded cotangents).
+kernel times (1 GiB read before each step), the double backward's two
+kernels (tpconv_double_backward with seeded cotangents) and the upstream
+kernels (edge harmonics, their gradient, the position gradient).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -45,6 +46,8 @@ def parse():
                         "(evicts the 256 MB Infinity Cache); kernel medians reported as kernels_ms_cold")
     p.add_argument("--dd-reps", type=int, default=20,
                    help="timed double-backward calls after the fwd+bwd steps (0 skips); reported as double_backward")
+    p.add_argument("--upstream-reps", type=int, default=20,
+                   help="timed calls of the edge-harmonics / position-gradient kernels (0 skips); reported as upstream")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="also run one plain device copy of this many MiB (scales rocprofv3 FETCH/WRITE_SIZE)")
     return p.parse_args()
@@ -204,6 +207,34 @@ def main():
                 "evict": "1 GiB device read (torch.sum) before each step"}
         del evict
 
+    up = None
+    if args.upstream_reps > 0:
+        # the step upstream of the convolution on the same graph: Y from the
+        # edge vectors, grad_vec from dY, grad_pos from grad_vec
+        b_ = 4 if w.dtype == "f32" else 8
+        vec_t = T(d["vec"].astype(w.np_dtype))
+        Y_t = torch.empty_like(Y)
+        gv_t = torch.empty_like(vec_t)
+        gp_t = torch.empty((N, 3), dtype=plan.torch_dtype, device=dev)
+        uev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.upstream_reps + 2)]
+        for k in range(args.upstream_reps + 2):   # the first two are warm-up
+            uev[k][0].record(stream)
+            tp.tpconv_sh(plan, vec_t, Y_t)
+            uev[k][1].record(stream)
+            tp.tpconv_sh_backward(plan, vec_t, dY, gv_t)
+            uev[k][2].record(stream)
+            tp.tpconv_positions_backward(plan, graph, gv_t, gp_t)
+            uev[k][3].record(stream)
+        torch.cuda.synchronize()
+        med = [float(np.median([e[i].elapsed_time(e[i + 1]) for e in uev[2:]])) for i in range(3)]
+        Dsh = plan.dim_sh
+        ub = [E * (3 + Dsh) * b_, E * (6 + Dsh) * b_, E * (3 * b_ + 8) + N * (3 * b_ + 8)]
+        up = {name: {"ms_median": round(m, 4), "algorithmic_bytes": int(bb),
+                     "algorithmic_GBps": round(bb / (m * 1e-3) / 1e9, 1)}
+              for name, m, bb in zip(("tpconv_sh", "tpconv_sh_backward", "tpconv_positions_backward"), med, ub)}
+        up["reps"] = args.upstream_reps
+        del vec_t, Y_t, gv_t, gp_t
+
     dd = None
     if args.dd_reps > 0:
         # double backward: the grad_G kernel and the grad_x / grad_Y / grad_W
@@ -268,6 +299,7 @@ def main():
                        "backward_min": round(float(bwd_ms.min()), 4)},
         "kernels_ms_cold": cold,
         "double_backward": dd,
+        "upstream": up,
         "hbm": {"fwd_bwd_algorithmic_GBps": round(hbm_fwdbwd, 1), "frac_of_peak": round(hbm_fwdbwd / HBM_PEAK_GBS, 4),
                 "fwd_bytes": int(fwd_bytes), "bwd_bytes": int(bwd_bytes)},
         "roofline": roofline,
