@@ -438,19 +438,44 @@ struct FwdDD {
   }
 };
 
+// Rows of a small graph are split over R waves of one block (R = 1: one
+// wave per row).  Part p of a row takes a contiguous, slot-aligned range of
+// its edges; the parts' fp64 row sums meet in LDS after a block barrier and
+// part 0 finishes the row.  Returns this part's [beg, end).
+template <int R>
+__device__ __forceinline__ void row_part(int beg, int end, int nsl, int part, int& pb, int& pe) {
+  if constexpr (R == 1) {
+    pb = beg;
+    pe = end;
+  } else {
+    const int steps = (end - beg + nsl - 1) / nsl;
+    const int per = (steps + R - 1) / R;
+    const int s0 = min(steps, part * per);
+    const int s1 = min(steps, s0 + per);
+    pb = beg + s0 * nsl;
+    pe = min(end, beg + s1 * nsl);
+  }
+}
+
 // Forward (DD = false): out = the convolution.  Double backward's first pass
 // (DD = true): out = grad_G, from the cotangents a (gathered like x), b (like
 // Y) and c (like W); a null cotangent reads as zeros.
-template <typename T, int L, class P, bool DD>
+template <typename T, int L, class P, bool DD, int R>
 __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
   using F = Fwd<T, L, P>;
   using FD = FwdDD<T, L, P>;
   using A = typename RowAcc<T>::type;
   constexpr int NL = F::NL, NT = F::NT;
+  static_assert(R == 1 || R == 2 || R == 4, "row split must divide the block's 4 waves");
   const int lane = threadIdx.x & 63;
-  const int wid = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (wid >= a.n_rows) return;  // wave-uniform
-  const int node = __builtin_amdgcn_readfirstlane(a.order[wid]);
+  const int wave = threadIdx.x >> 6;
+  const int part = wave % R;
+  const int wid = blockIdx.x * (4 / R) + wave / R;
+  const bool has_row = wid < a.n_rows;
+  if constexpr (R == 1) {
+    if (!has_row) return;  // wave-uniform
+  }
+  const int node = has_row ? __builtin_amdgcn_readfirstlane(a.order[wid]) : 0;
   const int lg = P::lps_log2(a);
   const int slot = lane >> lg;
   const int u = lane & ((1 << lg) - 1);
@@ -472,9 +497,10 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
   // added into an fp64 row sum kept in LDS (one slab per wave, lane-major),
   // which costs no VGPRs.
   constexpr bool kLdsRow = !std::is_same<T, A>::value;
+  constexpr bool kSlab = kLdsRow || R > 1;  // per-wave fp64 row slabs in LDS
   constexpr int kFlush = 4;
-  __shared__ A s_row[kLdsRow ? 4 : 1][kLdsRow ? NL : 1][64];
-  A* my_row = &s_row[kLdsRow ? (threadIdx.x >> 6) : 0][0][lane];
+  __shared__ A s_row[kSlab ? 4 : 1][kSlab ? NL : 1][64];
+  A* my_row = &s_row[kSlab ? wave : 0][0][lane];
   T acc[NL];
   static_for<NL>([&](auto I) { acc[I] = T(0); });
   if constexpr (kLdsRow) {
@@ -494,9 +520,9 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
     }
   };
 
-  const int beg = a.row_ptr[node];
-  const int end = a.row_ptr[node + 1];
   const int nsl = P::nslots(a);
+  int beg, end;
+  row_part<R>(has_row ? a.row_ptr[node] : 0, has_row ? a.row_ptr[node + 1] : 0, nsl, part, beg, end);
   // the row's edge ids and neighbours are loaded 64 at a time, one per lane,
   // and handed to the slots with lane shuffles while the wave is converged
   for (int cb = beg; cb < end; cb += 64) {
@@ -555,12 +581,24 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
   }
   flush();
 
-  // sum the slots' partial rows: slots sit at lane offsets 2^lg .. 32
   A tot[NL];
   static_for<NL>([&](auto I) {
     if constexpr (kLdsRow) tot[I] = my_row[I * 64];
     else tot[I] = acc[I];
   });
+  if constexpr (R > 1) {
+    // the row's parts meet in LDS; part 0 finishes the row
+    if constexpr (!kLdsRow) {
+      static_for<NL>([&](auto I) { my_row[I * 64] = tot[I]; });
+    }
+    __syncthreads();
+    if (part != 0 || !has_row) return;
+    static_for<R - 1>([&](auto Q) {
+      static_for<NL>([&](auto I) { tot[I] += my_row[(int(Q) + 1) * NL * 64 + I * 64]; });
+    });
+  }
+
+  // sum the slots' partial rows: slots sit at lane offsets 2^lg .. 32
   for (int off = 1 << lg; off < 64; off <<= 1) {
     static_for<NL>([&](auto I) { tot[I] += __shfl_xor(tot[I], off, 64); });
   }
@@ -759,7 +797,7 @@ constexpr bool bwd_pipelined() {
 // Double backward's second pass (DD = true): the same three outputs of
 // <a, dx> + <b, dY> + <c, dW>, with the cotangents a (row-resident like x),
 // b and c; a null cotangent reads as zeros.
-template <typename T, int L, class P, bool DD>
+template <typename T, int L, class P, bool DD, int R>
 __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
   using B = Bwd<T, L, P>;
   using BD = BwdDD<T, L, P>;
@@ -767,10 +805,16 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
   using A = typename RowAcc<T>::type;
   constexpr int NL = B::NL, NT = B::NT;
   constexpr int NV = pow2_ceil(NL);  // dY values, padded to a power of two for the reduce-scatter
+  static_assert(R == 1 || R == 2 || R == 4, "row split must divide the block's 4 waves");
   const int lane = threadIdx.x & 63;
-  const int wid = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (wid >= a.n_rows) return;  // wave-uniform
-  const int node = __builtin_amdgcn_readfirstlane(a.order[wid]);
+  const int wave = threadIdx.x >> 6;
+  const int part = wave % R;
+  const int wid = blockIdx.x * (4 / R) + wave / R;
+  const bool has_row = wid < a.n_rows;
+  if constexpr (R == 1) {
+    if (!has_row) return;  // wave-uniform
+  }
+  const int node = has_row ? __builtin_amdgcn_readfirstlane(a.order[wid]) : 0;
   const int lg = P::lps_log2(a);
   const int lps = 1 << lg;
   const int slot = lane >> lg;
@@ -820,8 +864,9 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
   // step k + 1 are requested before step k computes and stores, so their
   // latency hides behind step k and the in-order memory counter never has to
   // wait for this step's dW / dY stores before the next step can start.
-  const int beg = a.row_ptr[node];
-  const int deg = a.row_ptr[node + 1] - beg;
+  int beg, pend;
+  row_part<R>(has_row ? a.row_ptr[node] : 0, has_row ? a.row_ptr[node + 1] : 0, 64 >> lg, part, beg, pend);
+  const int deg = pend - beg;                   // this part's edges of the row
   const int lgs = 6 - lg;                       // log2(slots per wave)
   const int n_steps = (deg + (1 << lgs) - 1) >> lgs;
   const int chunk_mask = (64 >> lgs) - 1;       // steps per chunk of 64 ids, minus one
@@ -971,6 +1016,20 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
     }
   }
 
+  if constexpr (R > 1) {
+    // the row's parts meet in LDS; part 0 finishes dx
+    __shared__ A s_dx[4][NL][64];
+    if (DX != nullptr) {
+      static_for<NL>([&](auto I) { s_dx[wave][I][lane] = dxa[I]; });
+    }
+    __syncthreads();
+    if (part != 0 || !has_row) return;
+    if (DX != nullptr) {
+      static_for<R - 1>([&](auto Q) {
+        static_for<NL>([&](auto I) { dxa[I] += s_dx[wave + int(Q) + 1][I][lane]; });
+      });
+    }
+  }
   if (DX != nullptr) {
     for (int off = lps; off < 64; off <<= 1) {
       static_for<NL>([&](auto I) { dxa[I] += __shfl_xor(dxa[I], off, 64); });
@@ -991,21 +1050,26 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
 // ---------------------------------------------------------------- launchers
 constexpr bool kDD = TPCONV_DD != 0;
 
-template <typename T, class P>
+// Graphs with at most this many rows split each row over 4 waves: one wave
+// per row would leave most SIMDs with a single wavefront and nothing to hide
+// its memory latency behind.
+constexpr int kSplitRows = 1024;
+
+template <typename T, class P, int R = 1>
 hipError_t launch_fwd(const KernelArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
-  const int waves_per_block = 4;
-  const int blocks = (a.n_rows + waves_per_block - 1) / waves_per_block;
-  hipLaunchKernelGGL((fwd_kernel<T, TPCONV_L, P, kDD>), dim3(blocks), dim3(64 * waves_per_block), 0, s, a);
+  const int rows_per_block = 4 / R;
+  const int blocks = (a.n_rows + rows_per_block - 1) / rows_per_block;
+  hipLaunchKernelGGL((fwd_kernel<T, TPCONV_L, P, kDD, R>), dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <typename T, class P>
+template <typename T, class P, int R = 1>
 hipError_t launch_bwd(const KernelArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
-  const int waves_per_block = 4;
-  const int blocks = (a.n_rows + waves_per_block - 1) / waves_per_block;
-  hipLaunchKernelGGL((bwd_kernel<T, TPCONV_L, P, kDD>), dim3(blocks), dim3(64 * waves_per_block), 0, s, a);
+  const int rows_per_block = 4 / R;
+  const int blocks = (a.n_rows + rows_per_block - 1) / rows_per_block;
+  hipLaunchKernelGGL((bwd_kernel<T, TPCONV_L, P, kDD, R>), dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1032,7 +1096,11 @@ using FullMuls = UList<16, 32, 64>;
 template <typename T, bool FWD, int U0, int... Us>
 bool launch_full(const KernelArgs& a, hipStream_t s, hipError_t& err, UList<U0, Us...>) {
   if (a.mul == U0) {
-    err = FWD ? launch_fwd<T, FullPlan<TPCONV_L, U0>>(a, s) : launch_bwd<T, FullPlan<TPCONV_L, U0>>(a, s);
+    using FP = FullPlan<TPCONV_L, U0>;
+    if (!kDD && a.n_rows <= kSplitRows)
+      err = FWD ? launch_fwd<T, FP, 4>(a, s) : launch_bwd<T, FP, 4>(a, s);
+    else
+      err = FWD ? launch_fwd<T, FP>(a, s) : launch_bwd<T, FP>(a, s);
     return true;
   }
   if constexpr (sizeof...(Us) > 0) {

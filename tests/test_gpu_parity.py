@@ -273,3 +273,23 @@ def test_out_of_range_indices_are_reported(tp):
         tp.tpconv_graph_create(4, src, dst)
     assert ei.value.name == "TPCONV_E_INDEX"
     assert "2 edge(s)" in tp.tpconv_last_error()
+
+
+@pytest.mark.parametrize("spec", [
+    ("32x0e+32x1o+32x2e+32x3o", 3, "32x0e+32x1o+32x2e+32x3o", "f32"),
+    ("16x0e+16x1o+16x2e", 2, "16x0e+16x1o+16x2e", "f64"),
+    ("64x0e+64x1o", 1, "64x0e+64x1o", "f32"),
+])
+def test_small_graph_rows_split_over_waves(tp, spec):
+    """At most 1024 rows: each row is split over four waves whose partial sums
+    meet in LDS.  Uneven parts (a hub), rows shorter than four steps, rows
+    with no edges, and a node count that does not fill the last block."""
+    rng = np.random.default_rng(zlib.crc32(repr(spec).encode()) + 1)
+    n = 301
+    src, dst = small_graph(rng, n, 0.02)
+    src = np.concatenate([src, rng.integers(0, n, 700).astype(np.int32), np.full(500, 3, np.int32)])
+    dst = np.concatenate([dst, np.full(700, 5, np.int32), rng.integers(0, n, 500).astype(np.int32)])
+    keep = (dst != 11) & (src != 12)
+    src, dst = src[keep], dst[keep]
+    out, dx, _, _, _ = check_full(tp, spec, n, src, dst, seed=7, label="row split")
+    assert np.all(out[11] == 0) and np.all(dx[12] == 0)
