@@ -1097,7 +1097,7 @@ template <typename T, bool FWD, int U0, int... Us>
 bool launch_full(const KernelArgs& a, hipStream_t s, hipError_t& err, UList<U0, Us...>) {
   if (a.mul == U0) {
     using FP = FullPlan<TPCONV_L, U0>;
-    if (!kDD && a.n_rows <= kSplitRows)
+    if (a.n_rows <= kSplitRows)
       err = FWD ? launch_fwd<T, FP, 4>(a, s) : launch_bwd<T, FP, 4>(a, s);
     else
       err = FWD ? launch_fwd<T, FP>(a, s) : launch_bwd<T, FP>(a, s);
