@@ -684,11 +684,12 @@ struct Bwd {
 
 // Double backward, second pass (source-sorted rows).  With a, b, c the
 // cotangents of grad_x, grad_Y, grad_W, per path:
-//   dxp = CG(., Y, G), dxq = CG(., b, G), dyp = CG(x, ., G), dyq = CG(a, ., G)
+//   dxp = CG(., Y, G), dxq = CG(., b, G), xt = W a + c x, dyt = CG(xt, ., G)
 //   grad_W[p,u]   = a . dxp + x . dxq            (stored at once)
 //   grad_x (row) += W dxq + c dxp
-//   grad_Y (lane)+= W dyq + c dyp                (summed over channels later)
-// Each nonzero costs four FMAs sharing one product |c| * G[m3].
+//   grad_Y (lane)+= dyt                          (summed over channels later)
+// Each nonzero costs three FMAs sharing one product |c| * G[m3]; folding the
+// weights into xt first saves the fourth (grad_Y = CG(W a + c x, ., G)).
 template <typename T, int L, class P>
 struct BwdDD {
   static constexpr int NL = (L + 1) * (L + 1);
@@ -711,14 +712,16 @@ struct BwdDD {
             if (P::template on<t>(a) && P::template run<t>(a, tok)) {
               using TI = TabInfo<l1, l2, l3>;
               constexpr int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1;
-              T dxp[n1], dxq[n1], dyp[n2], dyq[n2];
+              T dxp[n1], dxq[n1], xt[n1], dyt[n2];
+              static_for<n1>([&](auto M1) {
+                if constexpr (TI::has_m1(M1)) xt[M1] = fmaT(w[t], xa[l1 * l1 + M1], wc[t] * x[l1 * l1 + M1]);
+              });
               static_for<TI::tab.n>([&](auto K) {
                 constexpr cg::Entry en = TI::tab.e[K];
                 constexpr T mag = T(en.mag);
                 const T cgm = mag * g[l3 * l3 + en.m3];
                 const T cgs = en.neg ? -cgm : cgm;
                 const T yv = y[l2 * l2 + en.m2], bv = yb[l2 * l2 + en.m2];
-                const T xv = x[l1 * l1 + en.m1], av = xa[l1 * l1 + en.m1];
                 if constexpr (TI::first_m1(K)) {
                   dxp[en.m1] = cgs * yv;
                   dxq[en.m1] = cgs * bv;
@@ -726,13 +729,10 @@ struct BwdDD {
                   dxp[en.m1] = fmaT(cgs, yv, dxp[en.m1]);
                   dxq[en.m1] = fmaT(cgs, bv, dxq[en.m1]);
                 }
-                if constexpr (TI::first_m2(K)) {
-                  dyp[en.m2] = cgs * xv;
-                  dyq[en.m2] = cgs * av;
-                } else {
-                  dyp[en.m2] = fmaT(cgs, xv, dyp[en.m2]);
-                  dyq[en.m2] = fmaT(cgs, av, dyq[en.m2]);
-                }
+                if constexpr (TI::first_m2(K))
+                  dyt[en.m2] = cgs * xt[en.m1];
+                else
+                  dyt[en.m2] = fmaT(cgs, xt[en.m1], dyt[en.m2]);
               });
               T s = T(0);
               static_for<n1>([&](auto M1) {
@@ -756,8 +756,7 @@ struct BwdDD {
                 });
               }
               static_for<n2>([&](auto M2) {
-                if constexpr (TI::has_m2(M2))
-                  dya[l2 * l2 + M2] = fmaT(w[t], dyq[M2], fmaT(wc[t], dyp[M2], dya[l2 * l2 + M2]));
+                if constexpr (TI::has_m2(M2)) dya[l2 * l2 + M2] += dyt[M2];
               });
             }
           }
