@@ -280,6 +280,55 @@ struct TabInfo {
   }
 };
 
+// The table's entries grouped by (m3, |c|), for fp64 kernels: an fp64
+// coefficient is no inline literal, so every use costs two scalar moves; in
+// z[m3] += c (+-p1 +- p2 ...) each distinct coefficient is used once per
+// group.  Inside a group a positive entry comes first (no negation needed);
+// a group with only negative entries sums magnitudes and uses -c.
+template <int L1, int L2, int L3>
+struct Grouped {
+  static constexpr const cg::Table& tab = cg::TableOf<L1, L2, L3>::value;
+  struct Order {
+    int n = 0;
+    int idx[cg::kEntriesMax] = {};      // entry at this position
+    bool open[cg::kEntriesMax] = {};    // first of its group
+    bool close[cg::kEntriesMax] = {};   // last of its group
+    bool first_m3[cg::kEntriesMax] = {};// the group is the first one of its m3
+    bool flip[cg::kEntriesMax] = {};    // group of negative entries only (at close)
+    bool sub[cg::kEntriesMax] = {};     // subtract this entry (not at open)
+  };
+  static constexpr Order build() {
+    Order o;
+    bool used[cg::kEntriesMax] = {};
+    bool seen_m3[2 * cg::kLMax + 1] = {};
+    for (int a = 0; a < tab.n; ++a) {
+      if (used[a]) continue;
+      // members of a's group, positive ones first
+      int mem[cg::kEntriesMax] = {};
+      int k = 0;
+      for (int pass = 0; pass < 2; ++pass)
+        for (int b = a; b < tab.n; ++b)
+          if (!used[b] && tab.e[b].m3 == tab.e[a].m3 && tab.e[b].mag == tab.e[a].mag &&
+              (tab.e[b].neg != 0) == (pass == 1))
+            mem[k++] = b;
+      const bool all_neg = tab.e[mem[0]].neg != 0;
+      for (int j = 0; j < k; ++j) {
+        const int pos = o.n++;
+        used[mem[j]] = true;
+        o.idx[pos] = mem[j];
+        o.open[pos] = j == 0;
+        o.close[pos] = j == k - 1;
+        o.sub[pos] = j > 0 && !all_neg && tab.e[mem[j]].neg != 0;
+        o.flip[pos] = all_neg;
+        o.first_m3[pos] = !seen_m3[tab.e[mem[j]].m3];
+      }
+      seen_m3[tab.e[a].m3] = true;
+    }
+    return o;
+  }
+  static constexpr Order ord = build();
+};
+
 // Is product x[m1]*Y[m2] used by some table of group (l1, l2) in parity class PAR?
 template <int L, int PAR, int L1, int L2, int L3 = 0>
 constexpr bool group_uses(int m1, int m2) {
@@ -323,6 +372,15 @@ __device__ __forceinline__ void load_w(const KernelArgs& a, const T* __restrict_
   });
 }
 
+// The double backward's grad_G kernel for l = 4 holds more per-edge state
+// than the register file (it spills to scratch): it keeps the row sum in an
+// LDS slab for fp64 data too.  (For the plain forward the per-edge slab
+// update costs more than the registers it frees.)
+template <typename T, int L, bool DD>
+constexpr bool row_sum_in_lds() {
+  return DD && L >= 4;
+}
+
 // ------------------------------------------------------------------ forward
 template <typename T, int L, class P>
 struct Fwd {
@@ -353,15 +411,34 @@ struct Fwd {
               using TI = TabInfo<l1, l2, l3>;
               constexpr int n3 = 2 * l3 + 1;
               T z[n3];
-              static_for<TI::tab.n>([&](auto K) {
-                constexpr cg::Entry en = TI::tab.e[K];
-                constexpr T c = en.neg ? T(-en.mag) : T(en.mag);
-                const T p = pr[en.m1 * n2 + en.m2];
-                if constexpr (TI::first_m3(K))
-                  z[en.m3] = c * p;
-                else
-                  z[en.m3] = fmaT(c, p, z[en.m3]);
-              });
+              if constexpr (sizeof(T) == 8) {
+                using GR = Grouped<l1, l2, l3>;
+                T acc_g = T(0);
+                static_for<GR::ord.n>([&](auto K) {
+                  constexpr cg::Entry en = TI::tab.e[GR::ord.idx[K]];
+                  const T p = pr[en.m1 * n2 + en.m2];
+                  if constexpr (GR::ord.open[K]) acc_g = p;
+                  else if constexpr (GR::ord.sub[K]) acc_g = acc_g - p;
+                  else acc_g = acc_g + p;
+                  if constexpr (GR::ord.close[K]) {
+                    constexpr T c = GR::ord.flip[K] ? T(-en.mag) : T(en.mag);
+                    if constexpr (GR::ord.first_m3[K])
+                      z[en.m3] = c * acc_g;
+                    else
+                      z[en.m3] = fmaT(c, acc_g, z[en.m3]);
+                  }
+                });
+              } else {
+                static_for<TI::tab.n>([&](auto K) {
+                  constexpr cg::Entry en = TI::tab.e[K];
+                  constexpr T c = en.neg ? T(-en.mag) : T(en.mag);
+                  const T p = pr[en.m1 * n2 + en.m2];
+                  if constexpr (TI::first_m3(K))
+                    z[en.m3] = c * p;
+                  else
+                    z[en.m3] = fmaT(c, p, z[en.m3]);
+                });
+              }
               if (P::template first3<t>(a)) {
                 static_for<n3>([&](auto M3) { te[l3 * l3 + M3] = w[t] * z[M3]; });
               } else {
@@ -411,18 +488,47 @@ struct FwdDD {
               using TI = TabInfo<l1, l2, l3>;
               constexpr int n3 = 2 * l3 + 1;
               T z1[n3], z2[n3];
-              static_for<TI::tab.n>([&](auto K) {
-                constexpr cg::Entry en = TI::tab.e[K];
-                constexpr T c = en.neg ? T(-en.mag) : T(en.mag);
-                constexpr int pi = en.m1 * n2 + en.m2;
-                if constexpr (TI::first_m3(K)) {
-                  z1[en.m3] = c * p1[pi];
-                  z2[en.m3] = c * p2[pi];
-                } else {
-                  z1[en.m3] = fmaT(c, p1[pi], z1[en.m3]);
-                  z2[en.m3] = fmaT(c, p2[pi], z2[en.m3]);
-                }
-              });
+              if constexpr (sizeof(T) == 8) {
+                using GR = Grouped<l1, l2, l3>;  // one coefficient per (m3, |c|) group
+                T g1 = T(0), g2 = T(0);
+                static_for<GR::ord.n>([&](auto K) {
+                  constexpr cg::Entry en = TI::tab.e[GR::ord.idx[K]];
+                  constexpr int pi = en.m1 * n2 + en.m2;
+                  if constexpr (GR::ord.open[K]) {
+                    g1 = p1[pi];
+                    g2 = p2[pi];
+                  } else if constexpr (GR::ord.sub[K]) {
+                    g1 = g1 - p1[pi];
+                    g2 = g2 - p2[pi];
+                  } else {
+                    g1 = g1 + p1[pi];
+                    g2 = g2 + p2[pi];
+                  }
+                  if constexpr (GR::ord.close[K]) {
+                    constexpr T c = GR::ord.flip[K] ? T(-en.mag) : T(en.mag);
+                    if constexpr (GR::ord.first_m3[K]) {
+                      z1[en.m3] = c * g1;
+                      z2[en.m3] = c * g2;
+                    } else {
+                      z1[en.m3] = fmaT(c, g1, z1[en.m3]);
+                      z2[en.m3] = fmaT(c, g2, z2[en.m3]);
+                    }
+                  }
+                });
+              } else {
+                static_for<TI::tab.n>([&](auto K) {
+                  constexpr cg::Entry en = TI::tab.e[K];
+                  constexpr T c = en.neg ? T(-en.mag) : T(en.mag);
+                  constexpr int pi = en.m1 * n2 + en.m2;
+                  if constexpr (TI::first_m3(K)) {
+                    z1[en.m3] = c * p1[pi];
+                    z2[en.m3] = c * p2[pi];
+                  } else {
+                    z1[en.m3] = fmaT(c, p1[pi], z1[en.m3]);
+                    z2[en.m3] = fmaT(c, p2[pi], z2[en.m3]);
+                  }
+                });
+              }
               if (P::template first3<t>(a)) {
                 static_for<n3>([&](auto M3) { te[l3 * l3 + M3] = fmaT(w[t], z2[M3], wc[t] * z1[M3]); });
               } else {
@@ -496,9 +602,9 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
   // te is added in fp32 into acc for kFlush edges at a time, and acc is then
   // added into an fp64 row sum kept in LDS (one slab per wave, lane-major),
   // which costs no VGPRs.
-  constexpr bool kLdsRow = !std::is_same<T, A>::value;
+  constexpr bool kLdsRow = !std::is_same<T, A>::value || row_sum_in_lds<T, L, DD>();
   constexpr bool kSlab = kLdsRow || R > 1;  // per-wave fp64 row slabs in LDS
-  constexpr int kFlush = 4;
+  constexpr int kFlush = std::is_same<T, A>::value ? 1 : 4;  // fp64 data: straight into the slab
   __shared__ A s_row[kSlab ? 4 : 1][kSlab ? NL : 1][64];
   A* my_row = &s_row[kSlab ? wave : 0][0][lane];
   T acc[NL];
