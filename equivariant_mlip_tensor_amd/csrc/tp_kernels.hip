@@ -960,8 +960,17 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
   T xa[DD ? NL : 1];
   load_row(X, true, x);
   if constexpr (DD) load_row(XA, XA != nullptr, xa);
+  // dx row sum: registers, or for the fp64 l = 4 double backward (whose
+  // per-edge state spills to scratch) a per-wave LDS slab, lane-major.  (The
+  // plain fp64 l = 4 backward measured slower with the slab.)
+  constexpr bool kDxLds = DD && sizeof(T) == 8 && L >= 4;
+  __shared__ A s_dxrow[kDxLds ? 4 : 1][kDxLds ? NL : 1][64];
+  A* const my_dx = &s_dxrow[kDxLds ? wave : 0][0][lane];
   A dxa[NL];
-  static_for<NL>([&](auto I) { dxa[I] = A(0); });
+  static_for<NL>([&](auto I) {
+    if constexpr (kDxLds) my_dx[I * 64] = A(0);
+    else dxa[I] = A(0);
+  });
 
   // The wave walks the row in steps of nslots edges: step k gives slot s the
   // edge at row position k * nslots + s.  Edge ids arrive 64 at a time (one
@@ -1052,7 +1061,9 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
       constexpr int l = I;
       if (P::in_l(a, l)) {
         static_for<2 * l + 1>([&](auto M) {
-          dxa[l * l + M] += valid ? static_cast<A>(dxe[l * l + M]) : A(0);
+          const A v = valid ? static_cast<A>(dxe[l * l + M]) : A(0);
+          if constexpr (kDxLds) my_dx[(l * l + M) * 64] += v;
+          else dxa[l * l + M] += v;
         });
       }
     });
@@ -1121,6 +1132,9 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
     }
   }
 
+  if constexpr (kDxLds) {
+    static_for<NL>([&](auto I) { dxa[I] = my_dx[I * 64]; });
+  }
   if constexpr (R > 1) {
     // the row's parts meet in LDS; part 0 finishes dx
     __shared__ A s_dx[4][NL][64];
