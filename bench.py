@@ -149,6 +149,11 @@ def main():
     graph = tp.tpconv_graph_create(N, src, dst)
     torch.cuda.synchronize()
     graph_ms = (time.perf_counter() - t0) * 1e3
+    # a rebuild (what a changed neighbour list costs), into the same workspace
+    t0 = time.perf_counter()
+    graph = tp.tpconv_graph_create(N, src, dst, workspace=graph.workspace)
+    torch.cuda.synchronize()
+    graph_rebuild_ms = (time.perf_counter() - t0) * 1e3
     out = torch.empty((N, plan.dim_out), dtype=plan.torch_dtype, device=dev)
     dx = torch.empty((N, plan.dim_in), dtype=plan.torch_dtype, device=dev)
     dY = torch.empty((E, plan.dim_sh), dtype=plan.torch_dtype, device=dev)
@@ -304,6 +309,7 @@ def main():
                 "fwd_bytes": int(fwd_bytes), "bwd_bytes": int(bwd_bytes)},
         "roofline": roofline,
         "graph_build_ms": round(graph_ms, 3),
+        "graph_rebuild_ms": round(graph_rebuild_ms, 3),
         "peak_device_GiB": round(peak_gib, 3),
         "kernel_source": kernel_source_hash(),
         "cpu_baseline": None,

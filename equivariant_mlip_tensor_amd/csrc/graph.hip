@@ -4,8 +4,10 @@
 // each destination's in-edges, the backward each source's out-edges, so
 // both reductions happen in registers of one wavefront.  The layout is a
 // counting sort done on the device -- histogram, scan, scatter -- followed by
-// a per-row sort on the edge id, so every row lists its edges in the
-// caller's order and the layout (and every sum over a row) is deterministic.
+// a per-row sort on the edge id (one wavefront per row ranks each edge by
+// the number of the row's edges with a smaller id), so every row lists its
+// edges in the caller's order and the layout (and every sum over a row) is
+// deterministic.
 // Each view also gets a row order, longest rows first, in which the kernels
 // hand rows to wavefronts: the long rows start early and the short ones fill
 // the tail of the dispatch.  Rows of equal degree may come in any order; a
@@ -32,7 +34,7 @@ constexpr int kDegBuckets = 1024;
 
 struct Layout {
   size_t dst_row, dst_col, dst_eid, src_row, src_col, src_eid, dst_order, src_order, cur_dst, cur_src, hist,
-      hcur, err, total;
+      hcur, err, tmp_dcol, tmp_deid, tmp_scol, tmp_seid, total;
 };
 
 Layout layout(int64_t n, int64_t e) {
@@ -56,6 +58,11 @@ Layout layout(int64_t n, int64_t e) {
   L.hist = take(sizeof(int32_t) * 2 * kDegBuckets);
   L.hcur = take(sizeof(int32_t) * 2 * kDegBuckets);
   L.err = take(sizeof(int32_t));
+  // the scatter's unsorted rows, read once by the per-row sort
+  L.tmp_dcol = take(sizeof(int32_t) * e);
+  L.tmp_deid = take(sizeof(int32_t) * e);
+  L.tmp_scol = take(sizeof(int32_t) * e);
+  L.tmp_seid = take(sizeof(int32_t) * e);
   L.total = o;
   return L;
 }
@@ -121,21 +128,34 @@ __global__ void k_scatter(const int32_t* __restrict__ src, const int32_t* __rest
   }
 }
 
-// One thread per row: insertion sort of the row's (eid, col) pairs by eid.
-__global__ void k_sort_rows(const int32_t* __restrict__ row, int32_t* __restrict__ col, int32_t* __restrict__ eid,
-                            int64_t N) {
-  for (int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; r < N; r += (int64_t)gridDim.x * blockDim.x) {
-    const int32_t a = row[r], b = row[r + 1];
-    for (int32_t i = a + 1; i < b; ++i) {
-      const int32_t ke = eid[i], kc = col[i];
-      int32_t j = i - 1;
-      while (j >= a && eid[j] > ke) {
-        eid[j + 1] = eid[j];
-        col[j + 1] = col[j];
-        --j;
+// One wavefront per row: each of the row's (eid, col) pairs goes to the
+// position given by the number of the row's edges with a smaller eid (eids
+// in a row are distinct, so these ranks are a permutation).  Lanes take the
+// row 64 edges at a time and compare against it 64 at a time through lane
+// shuffles; the loop bounds are the same for the whole wave.
+__global__ __launch_bounds__(256) void k_rank_rows(const int32_t* __restrict__ row, const int32_t* __restrict__ col_in,
+                                                   const int32_t* __restrict__ eid_in, int32_t* __restrict__ col_out,
+                                                   int32_t* __restrict__ eid_out, int64_t N) {
+  const int lane = threadIdx.x & 63;
+  for (int64_t r = blockIdx.x * 4 + (threadIdx.x >> 6); r < N; r += (int64_t)gridDim.x * 4) {
+    const int32_t a = row[r];
+    const int32_t d = row[r + 1] - a;
+    for (int32_t base = 0; base < d; base += 64) {
+      const int32_t i = base + lane;
+      const bool mine = i < d;
+      const int32_t me = mine ? eid_in[a + i] : 0;
+      const int32_t mc = mine ? col_in[a + i] : 0;
+      int32_t rank = 0;
+      for (int32_t cb = 0; cb < d; cb += 64) {
+        const int32_t j = cb + lane;
+        const int32_t other = j < d ? eid_in[a + j] : 0;
+        const int32_t lim = d - cb < 64 ? d - cb : 64;
+        for (int32_t k = 0; k < lim; ++k) rank += __shfl(other, k, 64) < me ? 1 : 0;
       }
-      eid[j + 1] = ke;
-      col[j + 1] = kc;
+      if (mine) {
+        eid_out[a + rank] = me;
+        col_out[a + rank] = mc;
+      }
     }
   }
 }
@@ -215,6 +235,10 @@ extern "C" tpconv_status tpconv_graph_create(int64_t n_nodes, int64_t n_edges, c
   int32_t* cur_dst = at(L.cur_dst);
   int32_t* cur_src = at(L.cur_src);
   int32_t* err = at(L.err);
+  int32_t* tmp_dcol = at(L.tmp_dcol);
+  int32_t* tmp_deid = at(L.tmp_deid);
+  int32_t* tmp_scol = at(L.tmp_scol);
+  int32_t* tmp_seid = at(L.tmp_seid);
 
   const int B = 256;
   hipLaunchKernelGGL(k_fill, dim3(grid_for(n_nodes + 1, B)), dim3(B), 0, stream, g.dst_row, n_nodes + 1, 0);
@@ -236,11 +260,11 @@ extern "C" tpconv_status tpconv_graph_create(int64_t n_nodes, int64_t n_edges, c
   }
   if (n_edges > 0) {
     hipLaunchKernelGGL(k_scatter, dim3(grid_for(n_edges, B)), dim3(B), 0, stream, src, dst, n_edges, n_nodes,
-                       g.dst_row, cur_dst, g.dst_col, g.dst_eid, g.src_row, cur_src, g.src_col, g.src_eid);
-    hipLaunchKernelGGL(k_sort_rows, dim3(grid_for(n_nodes, 64)), dim3(64), 0, stream, g.dst_row, g.dst_col,
-                       g.dst_eid, n_nodes);
-    hipLaunchKernelGGL(k_sort_rows, dim3(grid_for(n_nodes, 64)), dim3(64), 0, stream, g.src_row, g.src_col,
-                       g.src_eid, n_nodes);
+                       g.dst_row, cur_dst, tmp_dcol, tmp_deid, g.src_row, cur_src, tmp_scol, tmp_seid);
+    hipLaunchKernelGGL(k_rank_rows, dim3(grid_for((n_nodes + 3) / 4, 1)), dim3(256), 0, stream, g.dst_row, tmp_dcol,
+                       tmp_deid, g.dst_col, g.dst_eid, n_nodes);
+    hipLaunchKernelGGL(k_rank_rows, dim3(grid_for((n_nodes + 3) / 4, 1)), dim3(256), 0, stream, g.src_row, tmp_scol,
+                       tmp_seid, g.src_col, g.src_eid, n_nodes);
   }
   if (n_nodes > 0) {
     const int32_t* rows[2] = {g.dst_row, g.src_row};
