@@ -26,6 +26,17 @@
 // lane mapping a compile-time constant, no branch inside an edge), and
 // RtPlan<L, PAR> for any other plan (path set, offsets and U read from the
 // launch arguments, one uniform branch per path).
+//
+// With TPCONV_DD=1 the same two row kernels compute the double backward
+// (FwdDD: grad_G over destination rows; BwdDD: grad_x, grad_Y, grad_W over
+// source rows).  Beyond the scheme above:
+//  * the fp32 backward issues the next edge's loads before this edge's
+//    stores, into a second register set (bwd_pipelined);
+//  * graphs with at most 1024 rows split each row over the 4 waves of a
+//    block, which meet in LDS (row_part, template parameter R);
+//  * fp64 contractions sum the products that share an (m3, |c|) pair before
+//    one multiply by the coefficient (Grouped), because an fp64 coefficient
+//    is no inline literal.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
