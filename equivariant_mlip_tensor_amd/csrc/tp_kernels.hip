@@ -166,6 +166,7 @@ __device__ __forceinline__ bool bit(uint64_t lo, uint64_t hi, int t) {
 template <int L, int PAR>
 struct RtPlan {
   static constexpr int kPar = PAR;
+  static constexpr bool kFull = false;
   static __device__ __forceinline__ int lps_log2(const KernelArgs& a) { return a.lps_log2; }
   static __device__ __forceinline__ int nslots(const KernelArgs& a) { return a.nslots; }
   static __device__ __forceinline__ int mul(const KernelArgs& a) { return a.mul; }
@@ -204,6 +205,7 @@ template <int L, int U>
 struct FullPlan {
   static_assert(U >= 1 && U <= 64, "one wave holds at most 64 channels");
   static constexpr int kPar = kEvenOnly;
+  static constexpr bool kFull = true;
   static constexpr int kLg = log2_ceil(U);
   static constexpr int kD = U * (L + 1) * (L + 1);
   static __device__ __forceinline__ constexpr int lps_log2(const KernelArgs&) { return kLg; }
@@ -802,7 +804,8 @@ struct Bwd {
 // Double backward, second pass (source-sorted rows).  With a, b, c the
 // cotangents of grad_x, grad_Y, grad_W, per path:
 //   dxp = CG(., Y, G), dxq = CG(., b, G), xt = W a + c x, dyt = CG(xt, ., G)
-//   grad_W[p,u]   = a . dxp + x . dxq            (stored at once)
+//   grad_W[p,u]   = a . dxp + x . dxq            (stored at once, or with kLate
+//                                                 returned and stored by the caller)
 //   grad_x (row) += W dxq + c dxp
 //   grad_Y (lane)+= dyt                          (summed over channels later)
 // Each nonzero costs three FMAs sharing one product |c| * G[m3]; folding the
@@ -812,11 +815,11 @@ struct BwdDD {
   static constexpr int NL = (L + 1) * (L + 1);
   static constexpr int NT = triple_count(L);
 
-  template <int NV>
+  template <bool kLate, int NV>
   static __device__ __forceinline__ void edge(const KernelArgs& a, int tok, const T (&x)[NL], const T (&xa)[NL],
                                               const T (&y)[NL], const T (&yb)[NL], const T (&g)[NL],
                                               const T (&w)[NT], const T (&wc)[NT], T (&dxe)[NL], T (&dya)[NV],
-                                              bool store_dw, T* dwr) {
+                                              bool store_dw, T* dwr, T (&dwv)[NT]) {
     static_assert(NV >= NL, "dY accumulator too short");
     static_for<L + 1>([&](auto I3) {
       constexpr int l3 = I3;
@@ -858,7 +861,10 @@ struct BwdDD {
                   s = fmaT(x[l1 * l1 + M1], dxq[M1], s);
                 }
               });
-              if (store_dw) __builtin_nontemporal_store(s, dwr + P::template woff<t>(a));
+              if constexpr (kLate)
+                dwv[t] = s;
+              else if (store_dw)
+                __builtin_nontemporal_store(s, dwr + P::template woff<t>(a));
               if (P::template first1<t>(a)) {
                 static_for<n1>([&](auto M1) {
                   if constexpr (TI::has_m1(M1))
@@ -971,10 +977,20 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
   T xa[DD ? NL : 1];
   load_row(X, true, x);
   if constexpr (DD) load_row(XA, XA != nullptr, xa);
-  // dx row sum: registers, or for the fp64 l = 4 double backward (whose
-  // per-edge state spills to scratch) a per-wave LDS slab, lane-major.  (The
-  // plain fp64 l = 4 backward measured slower with the slab.)
-  constexpr bool kDxLds = DD && sizeof(T) == 8 && L >= 4;
+  // The fp32 l = 3 double backward over whole rows with a compile-time
+  // table (kLate) keeps an edge's grad_W and grad_Y values until the next
+  // edge's loads are issued (store_pending below): those loads then sit
+  // ahead of the stores in the in-order memory counter, and waiting for them
+  // does not wait for this edge's stores.  Everything else stores at once:
+  // fp64 l = 4 measured slower (twice the registers held), the split-row
+  // and run-time-table kernels drop to one wave per SIMD, and at other l the
+  // compiler waits for all stores more often, not less.
+  constexpr bool kLate = DD && sizeof(T) == 4 && L == 3 && P::kFull && R == 1;
+  // dx row sum: registers, or a per-wave LDS slab, lane-major, for kLate
+  // (room for the held values) and for the fp64 l = 4 double backward (whose
+  // per-edge state spills to scratch otherwise).  The plain backward,
+  // fp64 l = 4 included, measured slower with the slab.
+  constexpr bool kDxLds = kLate || (DD && sizeof(T) == 8 && L >= 4);
   __shared__ A s_dxrow[kDxLds ? 4 : 1][kDxLds ? NL : 1][64];
   A* const my_dx = &s_dxrow[kDxLds ? wave : 0][0][lane];
   A dxa[NL];
@@ -1056,7 +1072,12 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
     valid = (k << lgs) + slot < deg;
     load_edge(e, i, in);
   };
-  auto compute = [&](const int e, const bool valid, const In& in) {
+  struct Pending {
+    T dw[NT];  // unused, and removed, unless kLate
+    T dy[kLate ? NV : 1];
+    int base, nv;
+  };
+  auto compute = [&](const int e, const bool valid, const In& in, Pending& pd) {
     T dya[NV], dxe[NL];
     static_for<NV>([&](auto I) { dya[I] = T(0); });
     // idle lanes (u >= U) aim their dW stores at channel 0 of the same row
@@ -1065,7 +1086,8 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
     T* dwr = store_dw ? DW + (int64_t)e * wstride + uc : nullptr;
     const bool st = store_dw && chan_ok && valid;
     if constexpr (DD)
-      BD::edge(a, __builtin_amdgcn_readfirstlane(e), x, xa, in.y, in.yb, in.g, in.w, in.wc, dxe, dya, st, dwr);
+      BD::template edge<kLate>(a, __builtin_amdgcn_readfirstlane(e), x, xa, in.y, in.yb, in.g, in.w, in.wc, dxe,
+                               dya, st, dwr, pd.dw);
     else
       B::edge(a, __builtin_amdgcn_readfirstlane(e), x, in.y, in.g, in.w, dxe, dya, st, dwr);
     static_for<L + 1>([&](auto I) {
@@ -1110,13 +1132,41 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
           }
         }
       });
-      // bits below lps/NV were plain sums: one lane of each such group stores
-      const int plain_mask = lps > NV ? lps / NV - 1 : 0;
-      if ((u & plain_mask) == 0 && valid) {
-        T* dyr = DY + (int64_t)e * d_sh;
-        static_for<NV>([&](auto V) {
-          if (V < nv && base + V < d_sh) dyr[base + V] = dya[V];
+      if constexpr (kLate) {
+        static_for<NV>([&](auto V) { pd.dy[V] = dya[V]; });
+        pd.base = base;
+        pd.nv = nv;
+      } else {
+        // bits below lps/NV were plain sums: one lane of each such group stores
+        const int plain_mask = lps > NV ? lps / NV - 1 : 0;
+        if ((u & plain_mask) == 0 && valid) {
+          T* dyr = DY + (int64_t)e * d_sh;
+          static_for<NV>([&](auto V) {
+            if (V < nv && base + V < d_sh) dyr[base + V] = dya[V];
+          });
+        }
+      }
+    }
+  };
+  auto store_pending = [&](const int e, const bool valid, const Pending& pd) {
+    if constexpr (kLate) {
+      if (DW != nullptr && chan_ok && valid) {
+        T* dwr = DW + (int64_t)e * wstride + uc;
+        static_for<NT>([&](auto I) {
+          constexpr TripleInfo ti = triple_at(L, I);
+          if constexpr (triple_in_class(ti.l1, ti.l2, ti.l3, P::kPar)) {
+            if (P::template on<I>(a)) __builtin_nontemporal_store(pd.dw[I], dwr + P::template woff<I>(a));
+          }
         });
+      }
+      if (DY != nullptr) {
+        const int plain_mask = lps > NV ? lps / NV - 1 : 0;
+        if ((u & plain_mask) == 0 && valid) {
+          T* dyr = DY + (int64_t)e * d_sh;
+          static_for<NV>([&](auto V) {
+            if (V < pd.nv && pd.base + V < d_sh) dyr[pd.base + V] = pd.dy[V];
+          });
+        }
       }
     }
   };
@@ -1124,6 +1174,7 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
   In ia;
   int ea = 0;
   bool va = false;
+  Pending pd;
   if constexpr (bwd_pipelined<T, L, P, DD>()) {
     In ib;
     int eb = 0;
@@ -1131,15 +1182,24 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
     if (n_steps > 0) prefetch(0, ea, va, ia);
     for (int k = 0; k < n_steps; k += 2) {  // wave-uniform trip count
       prefetch(k + 1, eb, vb, ib);
-      compute(ea, va, ia);
+      compute(ea, va, ia, pd);
       if (k + 1 >= n_steps) break;
       prefetch(k + 2, ea, va, ia);
-      compute(eb, vb, ib);
+      compute(eb, vb, ib, pd);
+    }
+  } else if constexpr (kLate) {
+    if (n_steps > 0) prefetch(0, ea, va, ia);
+    for (int k = 0; k < n_steps; ++k) {  // wave-uniform trip count
+      compute(ea, va, ia, pd);
+      const int e_done = ea;
+      const bool v_done = va;
+      if (k + 1 < n_steps) prefetch(k + 1, ea, va, ia);
+      store_pending(e_done, v_done, pd);
     }
   } else {
     for (int k = 0; k < n_steps; ++k) {
       prefetch(k, ea, va, ia);
-      compute(ea, va, ia);
+      compute(ea, va, ia, pd);
     }
   }
 
