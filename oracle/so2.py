@@ -1,0 +1,232 @@
+"""SO(2) convolution (oracle; test infrastructure).
+
+The TrimSO(2) page (Abstract) describes SO(2)-convolution interatomic
+potentials: a representation transformation around dense matrix
+multiplications, which TrimSO(2) fuses as rotation on gather and inverse
+rotation on reduction.  The page prints no formula; the plainest reading, the
+one written out here, is:
+
+  * every edge e (src j, dst i, vector r_e = pos[j] - pos[i]) has a frame
+    rotation R_e, a proper rotation with R_e r_hat_e = z_hat;
+  * the neighbour's features are rotated into that frame block by block,
+    x~[l] = D^l(R_e) x[j, l] (per channel), D^l the real Wigner matrix with
+    Y_l(R v) = D^l(R) Y_l(v) for the real harmonics of sh.py;
+  * in the edge frame a linear map that commutes with rotations about z mixes
+    degrees and channels at each |m| separately:
+        m = 0:  y~_0  = A_0 X_0
+        m > 0:  y~_+m = A_m X_+m - B_m X_-m,   y~_-m = B_m X_+m + A_m X_-m
+    with X_+-m the vector of x~[l][c][+-m] over l = m..L (l major) and
+    channels c, and A_m, B_m shared by all edges (the dense matmuls);
+  * the result is rotated back and summed into the destination,
+        out[i, l] += D^l(R_e)^T y~[l].
+
+The map at |m| > 0 is complex multiplication by (A_m + i B_m) on
+X_+m + i X_-m, which commutes with the 2x2 rotation by m*alpha that a z
+rotation applies to each (+m, -m) pair, so the output does not depend on
+which R_e is chosen among those taking r_hat to z_hat.  Activations, radial
+modulation of the maps and a truncation of m are left out (the abstract
+names no such detail for the convolution itself).
+
+Layouts (all row-major, fp64 here):
+  x, out  [N][C (L+1)^2]   degree l at offset C l^2, stored [C][2l+1]
+  D       [E][sum_l (2l+1)^2]   block l at offset sum_{k<l} (2k+1)^2, [m][n]
+  weights A_0, A_1, B_1, ..., A_L, B_L, each [K_m][K_m] (out, in) with
+          K_m = (L+1-m) C and index (l-m) C + c.
+
+R_e (the Rodrigues rotation about r_hat x z_hat by the angle between them;
+identity for a zero vector or r_hat = z_hat, diag(1,-1,-1) for r_hat = -z_hat)
+and D^l are fixed definitions so that D itself can be compared; the
+convolution's output does not depend on that choice.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .sh import sh_real
+
+
+# ------------------------------------------------------------------ frames
+def edge_rotation(vec: np.ndarray) -> np.ndarray:
+    """[E,3,3] proper rotations with R r_hat = z_hat (Rodrigues' formula)."""
+    vec = np.asarray(vec, dtype=np.float64).reshape(-1, 3)
+    R = np.zeros((len(vec), 3, 3))
+    for e, v in enumerate(vec):
+        r = np.linalg.norm(v)
+        if r == 0.0:
+            R[e] = np.eye(3)
+            continue
+        u = v / r
+        axis = np.cross(u, [0.0, 0.0, 1.0])          # (u_y, -u_x, 0)
+        s = np.linalg.norm(axis)
+        c = u[2]
+        if s == 0.0:
+            R[e] = np.eye(3) if c > 0 else np.diag([1.0, -1.0, -1.0])
+            continue
+        k = axis / s
+        K = np.array([[0.0, -k[2], k[1]], [k[2], 0.0, -k[0]], [-k[1], k[0], 0.0]])
+        R[e] = np.eye(3) + s * K + (1.0 - c) * (K @ K)  # angle theta: sin = s, cos = c
+    return R
+
+
+def sphere_quadrature(degree: int):
+    """Points [K,3] and weights [K] (summing to 4 pi) that integrate every
+    polynomial of total degree <= `degree` over the unit sphere exactly:
+    Gauss-Legendre in z times equispaced azimuths."""
+    nz = degree // 2 + 1
+    nphi = degree + 1
+    z, wz = np.polynomial.legendre.leggauss(nz)
+    phi = 2.0 * np.pi * np.arange(nphi) / nphi
+    zz, pp = np.meshgrid(z, phi, indexing="ij")
+    rho = np.sqrt(1.0 - zz ** 2)
+    pts = np.stack([rho * np.cos(pp), rho * np.sin(pp), zz], axis=-1).reshape(-1, 3)
+    w = (wz[:, None] * np.full(nphi, 2.0 * np.pi / nphi)[None, :]).reshape(-1)
+    return pts, w
+
+
+def wigner_D(lmax: int, R: np.ndarray) -> list:
+    """Real Wigner matrices D^l(R), l = 0..lmax, each [E, 2l+1, 2l+1], from
+    their definition as the matrix of v -> Y_l(R v) in the basis Y_l:
+        D^l[m, n] = (1/4 pi) integral over the sphere of Y_lm(R v) Y_ln(v)
+    (the component-normalised harmonics are orthonormal under (1/4 pi) dOmega),
+    evaluated with a quadrature exact for the degree-2l integrand."""
+    R = np.asarray(R, dtype=np.float64).reshape(-1, 3, 3)
+    pts, w = sphere_quadrature(2 * lmax)
+    Yv = sh_real(lmax, pts)                                   # [K, (L+1)^2]
+    out = []
+    RY = sh_real(lmax, np.einsum("eab,kb->eka", R, pts))      # Y(R v_k)  [E, K, (L+1)^2]
+    for l in range(lmax + 1):
+        sl = slice(l * l, (l + 1) ** 2)
+        out.append(np.einsum("k,ekm,kn->emn", w, RY[:, :, sl], Yv[:, sl]) / (4.0 * np.pi))
+    return out
+
+
+def pack_D(blocks: list) -> np.ndarray:
+    """[E, sum (2l+1)^2] from the per-l blocks (row-major [m][n])."""
+    return np.concatenate([b.reshape(b.shape[0], int(np.prod(b.shape[1:]))) for b in blocks], axis=1)
+
+
+def unpack_D(D: np.ndarray, lmax: int) -> list:
+    D = np.asarray(D, dtype=np.float64)
+    out, off = [], 0
+    for l in range(lmax + 1):
+        n = 2 * l + 1
+        out.append(D[:, off:off + n * n].reshape(-1, n, n))
+        off += n * n
+    return out
+
+
+def edge_wigner(lmax: int, vec: np.ndarray) -> np.ndarray:
+    """Packed D(R_e) for every edge vector: [E, sum (2l+1)^2]."""
+    return pack_D(wigner_D(lmax, edge_rotation(vec)))
+
+
+# ------------------------------------------------------------------ layout
+def weight_blocks(lmax: int, C: int):
+    """[(name, m, offset, K_m)] in storage order A_0, A_1, B_1, ..., A_L, B_L."""
+    out, off = [], 0
+    for m in range(lmax + 1):
+        K = (lmax + 1 - m) * C
+        out.append(("A", m, off, K))
+        off += K * K
+        if m > 0:
+            out.append(("B", m, off, K))
+            off += K * K
+    return out
+
+
+def weight_numel(lmax: int, C: int) -> int:
+    return sum(K * K for _, _, _, K in weight_blocks(lmax, C))
+
+
+def _maps(lmax, C, weights):
+    weights = np.asarray(weights, dtype=np.float64)
+    A, B = {}, {}
+    for name, m, off, K in weight_blocks(lmax, C):
+        (A if name == "A" else B)[m] = weights[off:off + K * K].reshape(K, K)
+    return A, B
+
+
+def _split(x, lmax, C):
+    """[n, C (L+1)^2] -> list over l of [n, C, 2l+1]."""
+    return [x[:, C * l * l:C * (l + 1) ** 2].reshape(len(x), C, 2 * l + 1) for l in range(lmax + 1)]
+
+
+def _join(blocks):
+    return np.concatenate([b.reshape(b.shape[0], int(np.prod(b.shape[1:]))) for b in blocks], axis=1)
+
+
+def _gather_m(xt, lmax, m, sign):
+    """X_{sign*m}: [n, K_m] over (l = m..L, c) of the rotated blocks."""
+    return np.concatenate([xt[l][:, :, l + sign * m] for l in range(m, lmax + 1)], axis=1)
+
+
+def _scatter_m(yt, lmax, C, m, sign, vals):
+    for l in range(m, lmax + 1):
+        yt[l][:, :, l + sign * m] = vals[:, (l - m) * C:(l - m + 1) * C]
+
+
+def _so2_apply(xt, lmax, C, A, B, adjoint=False):
+    """The per-|m| maps on rotated blocks (list over l of [n, C, 2l+1])."""
+    n = len(xt[0])
+    yt = [np.zeros((n, C, 2 * l + 1)) for l in range(lmax + 1)]
+    for m in range(lmax + 1):
+        a = A[m].T if adjoint else A[m]
+        if m == 0:
+            _scatter_m(yt, lmax, C, 0, 0, _gather_m(xt, lmax, 0, 0) @ a.T)
+            continue
+        b = -B[m].T if adjoint else B[m]           # adjoint of [[A,-B],[B,A]] is [[A^T,B^T],[-B^T,A^T]]
+        xp, xm = _gather_m(xt, lmax, m, +1), _gather_m(xt, lmax, m, -1)
+        _scatter_m(yt, lmax, C, m, +1, xp @ a.T - xm @ b.T)
+        _scatter_m(yt, lmax, C, m, -1, xp @ b.T + xm @ a.T)
+    return yt
+
+
+def _rotate(blocks, Dl, transpose=False):
+    """Per edge and channel: D^l v (or D^l^T v)."""
+    spec = "emn,ecm->ecn" if transpose else "emn,ecn->ecm"
+    return [np.einsum(spec, Dl[l], blocks[l]) for l in range(len(blocks))]
+
+
+# ------------------------------------------------------------------ operator
+def so2_forward(lmax, C, x, D, weights, src, dst, n_nodes):
+    """out[i] = sum_{e: dst=i} D_e^T SO2(D_e x[src e])."""
+    x = np.asarray(x, dtype=np.float64)
+    src, dst = np.asarray(src, np.int64), np.asarray(dst, np.int64)
+    A, B = _maps(lmax, C, weights)
+    Dl = unpack_D(D, lmax)
+    xt = _rotate(_split(x[src], lmax, C), Dl)
+    yt = _so2_apply(xt, lmax, C, A, B)
+    msg = _join(_rotate(yt, Dl, transpose=True))
+    out = np.zeros((n_nodes, C * (lmax + 1) ** 2))
+    np.add.at(out, dst, msg)
+    return out
+
+
+def so2_backward(lmax, C, x, D, weights, G, src, dst, n_nodes):
+    """Gradients of <G, so2_forward(...)>: (grad_x [N, C(L+1)^2], grad_weights
+    in the weights' layout).  With g~ = D_e G[dst e] and x~ = D_e x[src e]:
+        grad_x[j]  = sum_{e: src=j} D_e^T SO2^T(g~)
+        grad_A_0   = sum_e g~_0 X_0^T
+        grad_A_m   = sum_e g~_+m X_+m^T + g~_-m X_-m^T
+        grad_B_m   = sum_e g~_-m X_+m^T - g~_+m X_-m^T."""
+    x = np.asarray(x, dtype=np.float64)
+    G = np.asarray(G, dtype=np.float64)
+    src, dst = np.asarray(src, np.int64), np.asarray(dst, np.int64)
+    A, B = _maps(lmax, C, weights)
+    Dl = unpack_D(D, lmax)
+    xt = _rotate(_split(x[src], lmax, C), Dl)
+    gt = _rotate(_split(G[dst], lmax, C), Dl)
+    dxt = _so2_apply(gt, lmax, C, A, B, adjoint=True)
+    grad_x = np.zeros((n_nodes, C * (lmax + 1) ** 2))
+    np.add.at(grad_x, src, _join(_rotate(dxt, Dl, transpose=True)))
+    gw = np.zeros(weight_numel(lmax, C))
+    for name, m, off, K in weight_blocks(lmax, C):
+        if m == 0:
+            blk = _gather_m(gt, lmax, 0, 0).T @ _gather_m(xt, lmax, 0, 0)
+        else:
+            gp, gm = _gather_m(gt, lmax, m, +1), _gather_m(gt, lmax, m, -1)
+            xp, xm = _gather_m(xt, lmax, m, +1), _gather_m(xt, lmax, m, -1)
+            blk = gp.T @ xp + gm.T @ xm if name == "A" else gm.T @ xp - gp.T @ xm
+        gw[off:off + K * K] = blk.reshape(-1)
+    return grad_x, gw

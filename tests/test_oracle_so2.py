@@ -1,0 +1,288 @@
+"""Pins for the oracle's SO(2) convolution (CPU only).
+
+Each function of oracle/so2.py is checked against something it does not use
+itself:
+  * the frame rotation: orthogonality, determinant, R r_hat = z_hat;
+  * the sphere quadrature: closed-form moments of x^a y^b z^c;
+  * the Wigner matrices: the defining identity D Y(v) = Y(R v) at points
+    outside the quadrature, the l = 1 closed form (a permutation of R), the
+    least-squares fit of the tensor-product tests, D(R1 R2) = D(R1) D(R2);
+  * the convolution: rotation equivariance, independence of the roll about
+    the edge axis, a loop-by-loop evaluation of the definition, and -- the
+    strongest pin -- equality with the (separately pinned) tensor-product
+    oracle when A_m, B_m are built from the real CG coefficients at m2 = 0,
+    which is what a tensor product with Y(r_hat) becomes in the edge frame;
+  * the backward: the operator is linear in x and in the weights, so
+    <G, f(dx)> = <grad_x, dx> and <G, f(x; dw)> = <grad_w, dw> exactly.
+"""
+
+from math import gamma
+
+import numpy as np
+import pytest
+
+from oracle import TPProblem, cg_real, sh_real, tp_forward
+from oracle.so2 import (edge_rotation, edge_wigner, pack_D, so2_backward, so2_forward, sphere_quadrature,
+                        unpack_D, weight_blocks, weight_numel, wigner_D)
+
+from test_oracle_tp import fitted_D
+
+
+def random_rotation(rng):
+    q, r = np.linalg.qr(rng.standard_normal((3, 3)))
+    q = q * np.sign(np.diag(r))
+    if np.linalg.det(q) < 0:
+        q[:, 0] *= -1
+    return q
+
+
+def rot_z(g):
+    c, s = np.cos(g), np.sin(g)
+    return np.array([[c, -s, 0.0], [s, c, 0.0], [0.0, 0.0, 1.0]])
+
+
+def test_edge_rotation():
+    rng = np.random.default_rng(80)
+    v = rng.standard_normal((50, 3)) * rng.uniform(0.1, 5.0, (50, 1))
+    v = np.concatenate([v, [[0, 0, 2.0], [0, 0, -3.0], [0, 0, 0], [1e-3, 0, -1.0], [0, 1e-9, -1.0]]])
+    R = edge_rotation(v)
+    for e in range(len(v)):
+        np.testing.assert_allclose(R[e] @ R[e].T, np.eye(3), atol=1e-13)
+        assert np.linalg.det(R[e]) == pytest.approx(1.0, abs=1e-13)
+        r = np.linalg.norm(v[e])
+        if r > 0:
+            np.testing.assert_allclose(R[e] @ (v[e] / r), [0, 0, 1.0], atol=1e-12)
+    np.testing.assert_array_equal(R[-3], np.eye(3))
+    np.testing.assert_array_equal(R[-4], np.diag([1.0, -1.0, -1.0]))
+
+
+@pytest.mark.parametrize("degree", [0, 2, 6, 8])
+def test_quadrature_moments(degree):
+    pts, w = sphere_quadrature(degree)
+    assert w.sum() == pytest.approx(4 * np.pi, rel=1e-14)
+    for a in range(degree + 1):
+        for b in range(degree + 1 - a):
+            for c in range(degree + 1 - a - b):
+                q = np.sum(w * pts[:, 0] ** a * pts[:, 1] ** b * pts[:, 2] ** c)
+                if a % 2 or b % 2 or c % 2:
+                    exact = 0.0
+                else:   # integral of x^a y^b z^c over the unit sphere
+                    exact = 2 * gamma((a + 1) / 2) * gamma((b + 1) / 2) * gamma((c + 1) / 2) / gamma((a + b + c + 3) / 2)
+                assert q == pytest.approx(exact, abs=1e-13), (a, b, c)
+
+
+@pytest.mark.parametrize("lmax", [1, 3, 4])
+def test_wigner_defining_identity(lmax):
+    rng = np.random.default_rng(81 + lmax)
+    Rs = np.stack([random_rotation(rng) for _ in range(6)])
+    Ds = wigner_D(lmax, Rs)
+    v = rng.standard_normal((30, 3))
+    for e in range(len(Rs)):
+        for l in range(lmax + 1):
+            sl = slice(l * l, (l + 1) ** 2)
+            np.testing.assert_allclose(sh_real(lmax, v @ Rs[e].T)[:, sl], sh_real(lmax, v)[:, sl] @ Ds[l][e].T,
+                                       atol=1e-12)
+            np.testing.assert_allclose(Ds[l][e] @ Ds[l][e].T, np.eye(2 * l + 1), atol=1e-12)
+            np.testing.assert_allclose(Ds[l][e], fitted_D(l, Rs[e], rng), atol=1e-11)
+
+
+def test_wigner_l1_closed_form_and_homomorphism():
+    rng = np.random.default_rng(85)
+    R1, R2 = random_rotation(rng), random_rotation(rng)
+    P = np.zeros((3, 3))
+    P[0, 1] = P[1, 2] = P[2, 0] = 1.0            # Y_1 = sqrt(3) (y, z, x)
+    D1 = wigner_D(1, R1[None])[1][0]
+    np.testing.assert_allclose(D1, P @ R1 @ P.T, atol=1e-13)
+    a, b, ab = wigner_D(4, np.stack([R1, R2, R1 @ R2]))[4]
+    np.testing.assert_allclose(ab, a @ b, atol=1e-12)
+
+
+def test_edge_frame_aligns_harmonics():
+    rng = np.random.default_rng(86)
+    v = rng.standard_normal((40, 3))
+    Dl = unpack_D(edge_wigner(3, v), 3)
+    Y = sh_real(3, v)
+    for l in range(4):
+        rot = np.einsum("emn,en->em", Dl[l], Y[:, l * l:(l + 1) ** 2])
+        want = np.zeros_like(rot)
+        want[:, l] = np.sqrt(2 * l + 1)           # Y_l(z_hat): only m = 0
+        np.testing.assert_allclose(rot, want, atol=1e-12)
+
+
+def make_graph(rng, n, E):
+    src = rng.integers(0, n, E)
+    dst = rng.integers(0, n, E)
+    vec = rng.standard_normal((E, 3)) * rng.uniform(0.5, 4.0, (E, 1))
+    return src, dst, vec
+
+
+def rotate_feats(x, lmax, C, Ds):
+    out = x.copy()
+    for l in range(lmax + 1):
+        sl = slice(C * l * l, C * (l + 1) ** 2)
+        out[:, sl] = (x[:, sl].reshape(len(x), C, 2 * l + 1) @ Ds[l].T).reshape(len(x), -1)
+    return out
+
+
+@pytest.mark.parametrize("lmax,C", [(1, 3), (2, 2), (3, 2)])
+def test_equivariance(lmax, C):
+    rng = np.random.default_rng(90 + lmax)
+    n, E = 7, 40
+    src, dst, vec = make_graph(rng, n, E)
+    x = rng.standard_normal((n, C * (lmax + 1) ** 2))
+    w = rng.standard_normal(weight_numel(lmax, C))
+    out = so2_forward(lmax, C, x, edge_wigner(lmax, vec), w, src, dst, n)
+    Q = random_rotation(rng)
+    DQ = [d[0] for d in wigner_D(lmax, Q[None])]
+    out_r = so2_forward(lmax, C, rotate_feats(x, lmax, C, DQ), edge_wigner(lmax, vec @ Q.T), w, src, dst, n)
+    np.testing.assert_allclose(out_r, rotate_feats(out, lmax, C, DQ), atol=1e-11)
+
+
+def test_roll_invariance():
+    rng = np.random.default_rng(95)
+    lmax, C, n, E = 3, 3, 6, 30
+    src, dst, vec = make_graph(rng, n, E)
+    x = rng.standard_normal((n, C * 16))
+    w = rng.standard_normal(weight_numel(lmax, C))
+    R = edge_rotation(vec)
+    rolled = np.stack([rot_z(g) @ R[e] for e, g in enumerate(rng.uniform(0, 2 * np.pi, E))])
+    a = so2_forward(lmax, C, x, pack_D(wigner_D(lmax, R)), w, src, dst, n)
+    b = so2_forward(lmax, C, x, pack_D(wigner_D(lmax, rolled)), w, src, dst, n)
+    np.testing.assert_allclose(a, b, atol=1e-11)
+
+
+def brute_forward(lmax, C, x, D, w, src, dst, n):
+    """The definition, one scalar at a time."""
+    Dl = unpack_D(D, lmax)
+    blocks = {b[0] + str(b[1]): (b[2], b[3]) for b in weight_blocks(lmax, C)}
+
+    def Wm(name, m, o, i):
+        off, K = blocks[name + str(m)]
+        return w[off + o * K + i]
+
+    out = np.zeros((n, C * (lmax + 1) ** 2))
+    for e in range(len(src)):
+        xt = {}
+        for l in range(lmax + 1):
+            for c in range(C):
+                for mi in range(-l, l + 1):
+                    xt[l, c, mi] = sum(Dl[l][e, mi + l, ni + l] * x[src[e], C * l * l + c * (2 * l + 1) + ni + l]
+                                       for ni in range(-l, l + 1))
+        yt = {}
+        for l3 in range(lmax + 1):
+            for c3 in range(C):
+                for m3 in range(-l3, l3 + 1):
+                    m = abs(m3)
+                    o = (l3 - m) * C + c3
+                    s = 0.0
+                    for l1 in range(m, lmax + 1):
+                        for c1 in range(C):
+                            i = (l1 - m) * C + c1
+                            if m == 0:
+                                s += Wm("A", 0, o, i) * xt[l1, c1, 0]
+                            elif m3 > 0:
+                                s += Wm("A", m, o, i) * xt[l1, c1, m] - Wm("B", m, o, i) * xt[l1, c1, -m]
+                            else:
+                                s += Wm("B", m, o, i) * xt[l1, c1, m] + Wm("A", m, o, i) * xt[l1, c1, -m]
+                    yt[l3, c3, m3] = s
+        for l in range(lmax + 1):
+            for c in range(C):
+                for ni in range(-l, l + 1):
+                    out[dst[e], C * l * l + c * (2 * l + 1) + ni + l] += sum(
+                        Dl[l][e, mi + l, ni + l] * yt[l, c, mi] for mi in range(-l, l + 1))
+    return out
+
+
+def test_matches_brute_force():
+    rng = np.random.default_rng(96)
+    lmax, C, n, E = 2, 2, 5, 12
+    src, dst, vec = make_graph(rng, n, E)
+    x = rng.standard_normal((n, C * 9))
+    w = rng.standard_normal(weight_numel(lmax, C))
+    D = edge_wigner(lmax, vec)
+    np.testing.assert_allclose(so2_forward(lmax, C, x, D, w, src, dst, n), brute_forward(lmax, C, x, D, w, src, dst, n),
+                               atol=1e-12)
+
+
+def escn_weights(prob, lmax, C, w_path):
+    """A_m, B_m of the tensor product with Y(r_hat) seen in the edge frame:
+    Y_l2(z_hat) = sqrt(2 l2 + 1) at m2 = 0 only, so path p = (l1, l2, l3)
+    maps x~[l1][u][m1] to y~[l3][u][m3] with coefficient
+    w[p,u] sqrt(2 l2 + 1) C_p[m1, 0, m3], nonzero only for |m1| = |m3|."""
+    W = np.zeros(weight_numel(lmax, C))
+    blocks = {b[0] + str(b[1]): (b[2], b[3]) for b in weight_blocks(lmax, C)}
+    for p, (s1, l2, s3) in enumerate(prob.paths):
+        l1, l3 = prob.irreps_in[s1].l, prob.irreps_out[s3].l
+        cg = cg_real(l1, l2, l3)[:, l2, :] * np.sqrt(2 * l2 + 1)      # [m1 + l1, m3 + l3]
+        for m1 in range(-l1, l1 + 1):
+            for m3 in range(-l3, l3 + 1):
+                if abs(m1) != abs(m3):
+                    assert cg[m1 + l1, m3 + l3] == 0.0
+        for m in range(0, min(l1, l3) + 1):
+            a = cg[l1 + m, l3 + m]
+            if m > 0:
+                b = cg[l1 + m, l3 - m]
+                # the complex-multiplication form the SO(2) map assumes
+                assert cg[l1 - m, l3 - m] == pytest.approx(a, abs=1e-14)
+                assert cg[l1 - m, l3 + m] == pytest.approx(-b, abs=1e-14)
+            for u in range(C):
+                o, i = (l3 - m) * C + u, (l1 - m) * C + u
+                offA, K = blocks["A" + str(m)]
+                W[offA + o * K + i] += w_path[p, u] * a
+                if m > 0:
+                    offB, _ = blocks["B" + str(m)]
+                    W[offB + o * K + i] += w_path[p, u] * b
+    return W
+
+
+@pytest.mark.parametrize("case", [("3x0e+3x1o+3x2e", 2, "3x0e+3x1o+3x2e"),
+                                  ("2x0e+2x1o+2x2e+2x3o", 3, "2x0e+2x1o+2x2e+2x3o"),
+                                  ("2x0e+2x1o+2x2e", 2, "2x0o+2x1e+2x2o"),        # odd paths: B_m only
+                                  ("2x0e+2x1e+2x2e+2x3e", 3, "2x0e+2x1e+2x2e+2x3e")])  # both parities
+def test_equals_tensor_product_in_edge_frame(case):
+    rng = np.random.default_rng(97)
+    prob = TPProblem.build(*case)
+    lmax, C = prob.sh_lmax, prob.irreps_in[0].mul
+    n, E = 8, 50
+    src, dst, vec = make_graph(rng, n, E)
+    x = rng.standard_normal((n, prob.dim_in))
+    w_path = rng.standard_normal((len(prob.paths), C))
+    W_edges = np.concatenate([np.tile(w_path[p], (E, 1)) for p in range(len(prob.paths))], axis=1)
+    ref = tp_forward(prob, x, sh_real(lmax, vec), W_edges, src, dst, n)
+    got = so2_forward(lmax, C, x, edge_wigner(lmax, vec), escn_weights(prob, lmax, C, w_path), src, dst, n)
+    np.testing.assert_allclose(got, ref, atol=1e-11 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("lmax,C", [(1, 2), (3, 3)])
+def test_backward_by_linearity(lmax, C):
+    rng = np.random.default_rng(98 + lmax)
+    n, E = 9, 60
+    src, dst, vec = make_graph(rng, n, E)
+    D = edge_wigner(lmax, vec)
+    d = C * (lmax + 1) ** 2
+    x = rng.standard_normal((n, d))
+    w = rng.standard_normal(weight_numel(lmax, C))
+    G = rng.standard_normal((n, d))
+    gx, gw = so2_backward(lmax, C, x, D, w, G, src, dst, n)
+    for _ in range(3):
+        dx = rng.standard_normal((n, d))
+        dw = rng.standard_normal(len(w))
+        lhs_x = np.vdot(G, so2_forward(lmax, C, dx, D, w, src, dst, n))
+        lhs_w = np.vdot(G, so2_forward(lmax, C, x, D, dw, src, dst, n))
+        assert np.vdot(gx, dx) == pytest.approx(lhs_x, rel=1e-11)
+        assert np.vdot(gw, dw) == pytest.approx(lhs_w, rel=1e-11)
+    # every weight block is reached
+    for _, _, off, K in weight_blocks(lmax, C):
+        assert np.abs(gw[off:off + K * K]).max() > 0
+
+
+def test_isolated_nodes_and_no_edges():
+    rng = np.random.default_rng(99)
+    lmax, C, n = 2, 2, 4
+    w = rng.standard_normal(weight_numel(lmax, C))
+    x = rng.standard_normal((n, C * 9))
+    e = np.zeros(0, np.int64)
+    out = so2_forward(lmax, C, x, np.zeros((0, 35)), w, e, e, n)
+    assert out.shape == (n, 18) and np.all(out == 0)
+    gx, gw = so2_backward(lmax, C, x, np.zeros((0, 35)), w, x, e, e, n)
+    assert np.all(gx == 0) and np.all(gw == 0)
