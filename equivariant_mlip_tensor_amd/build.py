@@ -48,6 +48,7 @@ def _jobs():
                               [f"-DTPCONV_L={L}", f"-DTPCONV_DOUBLE={dbl}", f"-DTPCONV_DD={dd}"]))
     units.append((os.path.join(CSRC, "graph.hip"), os.path.join(BUILD, "graph.o"), []))
     units.append((os.path.join(CSRC, "sh.hip"), os.path.join(BUILD, "sh.o"), []))
+    units.append((os.path.join(CSRC, "so2.hip"), os.path.join(BUILD, "so2.o"), []))
     # the host CG builder runs without FMA contraction so its run-time values
     # are bit-identical to the kernels' compile-time evaluation
     units.append((os.path.join(CSRC, "plan.cpp"), os.path.join(BUILD, "plan.o"), ["-ffp-contract=off"]))

@@ -243,3 +243,80 @@ extern "C" tpconv_status tpconv_positions_backward(tpconv_plan_t hp, tpconv_grap
   if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("positions backward launch: ") + hipGetErrorString(he));
   return TPCONV_OK;
 }
+
+namespace {
+bool so2_supported(int L, int C) { return L >= 1 && L <= 3 && (C == 16 || C == 32); }
+}  // namespace
+
+extern "C" int64_t tpconv_so2_weight_numel(int lmax, int channels) {
+  return so2_supported(lmax, channels) ? so2_weight_numel(lmax, channels) : 0;
+}
+
+extern "C" tpconv_status tpconv_so2_rotations(int lmax, tpconv_dtype dtype, int64_t n_edges, const void* vec,
+                                              void* D, hipStream_t stream) {
+  if (n_edges < 0) return fail(TPCONV_E_INVALID_ARG, "n_edges < 0");
+  if (lmax < 0 || lmax > 4) return fail(TPCONV_E_UNSUPPORTED, "SO(2) rotations: lmax must be 0..4");
+  if (dtype != TPCONV_F32 && dtype != TPCONV_F64) return fail(TPCONV_E_INVALID_ARG, "unknown dtype");
+  if (n_edges > 0 && (vec == nullptr || D == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL vec or D");
+  const hipError_t he = launch_so2_wigner(lmax, dtype == TPCONV_F64, n_edges, vec, D, stream);
+  if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("SO(2) rotations launch: ") + hipGetErrorString(he));
+  return TPCONV_OK;
+}
+
+extern "C" tpconv_status tpconv_so2_forward(tpconv_graph_t hg, int lmax, int channels, tpconv_dtype dtype,
+                                            const void* x, const void* D, const void* weights, void* out,
+                                            hipStream_t stream) {
+  if (hg == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL graph");
+  if (!so2_supported(lmax, channels) || dtype != TPCONV_F32)
+    return fail(TPCONV_E_UNSUPPORTED, "SO(2) convolution: lmax 1..3, channels 16 or 32, fp32");
+  const Graph& g = *reinterpret_cast<const Graph*>(hg);
+  if (g.n_nodes == 0) return TPCONV_OK;
+  if (out == nullptr || weights == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL out or weights");
+  if (g.n_edges > 0 && (x == nullptr || D == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL x or D");
+  const hipError_t he = launch_so2_conv(lmax, channels, false, (int)g.n_nodes, g.dst_row, g.dst_col, g.dst_eid,
+                                        g.dst_order, static_cast<const float*>(x), static_cast<const float*>(D),
+                                        static_cast<const float*>(weights), static_cast<float*>(out), stream);
+  if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("SO(2) forward launch: ") + hipGetErrorString(he));
+  return TPCONV_OK;
+}
+
+extern "C" size_t tpconv_so2_workspace_bytes(int lmax, int channels, int64_t n_edges) {
+  if (!so2_supported(lmax, channels) || n_edges < 0) return 0;
+  return (size_t)so2_wgrad_blocks(n_edges) * (size_t)so2_weight_numel(lmax, channels) * sizeof(float);
+}
+
+extern "C" tpconv_status tpconv_so2_backward(tpconv_graph_t hg, int lmax, int channels, tpconv_dtype dtype,
+                                             const void* x, const void* D, const void* weights, const void* grad_out,
+                                             void* grad_x, void* grad_weights, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream) {
+  if (hg == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL graph");
+  if (!so2_supported(lmax, channels) || dtype != TPCONV_F32)
+    return fail(TPCONV_E_UNSUPPORTED, "SO(2) convolution: lmax 1..3, channels 16 or 32, fp32");
+  const Graph& g = *reinterpret_cast<const Graph*>(hg);
+  if (grad_x == nullptr && grad_weights == nullptr) return TPCONV_OK;
+  if (grad_weights != nullptr) {
+    const size_t need = tpconv_so2_workspace_bytes(lmax, channels, g.n_edges);
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(TPCONV_E_WORKSPACE, "SO(2) backward: workspace smaller than tpconv_so2_workspace_bytes()");
+  }
+  if (g.n_nodes > 0 && grad_out == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL grad_out");
+  if (grad_x != nullptr && weights == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL weights");
+  if (g.n_edges > 0 && (x == nullptr || D == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL x or D");
+  if (grad_x != nullptr && g.n_nodes > 0) {
+    const hipError_t he = launch_so2_conv(lmax, channels, true, (int)g.n_nodes, g.src_row, g.src_col, g.src_eid,
+                                          g.src_order, static_cast<const float*>(grad_out),
+                                          static_cast<const float*>(D), static_cast<const float*>(weights),
+                                          static_cast<float*>(grad_x), stream);
+    if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("SO(2) backward launch: ") + hipGetErrorString(he));
+  }
+  if (grad_weights != nullptr) {
+    const hipError_t he = launch_so2_wgrad(lmax, channels, (int)g.n_nodes, g.n_edges, g.dst_row, g.dst_col,
+                                           g.dst_eid, static_cast<const float*>(x), static_cast<const float*>(grad_out),
+                                           static_cast<const float*>(D), static_cast<float*>(workspace),
+                                           static_cast<float*>(grad_weights), stream);
+    if (he != hipSuccess)
+      return fail(TPCONV_E_HIP, std::string("SO(2) weight-gradient launch: ") + hipGetErrorString(he));
+  }
+  return TPCONV_OK;
+}
+

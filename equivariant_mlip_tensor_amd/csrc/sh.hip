@@ -224,6 +224,122 @@ __global__ __launch_bounds__(256) void k_pos_backward(int64_t n_nodes, const int
   }
 }
 
+// Edge frames for the SO(2) convolution.  R_e is the proper rotation about
+// u x z_hat through the angle between u = r / |r| and z_hat (Rodrigues'
+// formula), so R_e u = z_hat; the identity for a zero vector or u = z_hat and
+// diag(1, -1, -1) for u = -z_hat.  Its real Wigner blocks,
+//   D^l[m][n] = (1 / 4 pi) integral over the sphere of Y_lm(R v) Y_ln(v),
+// the matrix of v -> Y_l(R v) in the basis Y_l, come from a product rule
+// that is exact for the degree-2l integrand: L + 1 Gauss-Legendre nodes in z
+// (closed forms) times 2L + 1 equispaced azimuths.  fp64 throughout.
+__device__ __forceinline__ void gauss_legendre(int n, int i, double& x, double& w) {
+  // nodes ascending; the closed forms for n <= 5
+  switch (n) {
+    case 1: x = 0.0; w = 2.0; return;
+    case 2: x = (i == 0 ? -1.0 : 1.0) / sqrt(3.0); w = 1.0; return;
+    case 3: {
+      const double a = sqrt(0.6);
+      x = i == 0 ? -a : (i == 1 ? 0.0 : a);
+      w = i == 1 ? 8.0 / 9.0 : 5.0 / 9.0;
+      return;
+    }
+    case 4: {
+      const double t = 2.0 / 7.0 * sqrt(6.0 / 5.0);
+      const double inner = sqrt(3.0 / 7.0 - t), outer = sqrt(3.0 / 7.0 + t);
+      const double wi = (18.0 + sqrt(30.0)) / 36.0, wo = (18.0 - sqrt(30.0)) / 36.0;
+      const double xs[4] = {-outer, -inner, inner, outer}, ws[4] = {wo, wi, wi, wo};
+      x = xs[i];
+      w = ws[i];
+      return;
+    }
+    default: {
+      const double t = 2.0 * sqrt(10.0 / 7.0);
+      const double inner = sqrt(5.0 - t) / 3.0, outer = sqrt(5.0 + t) / 3.0;
+      const double wi = (322.0 + 13.0 * sqrt(70.0)) / 900.0, wo = (322.0 - 13.0 * sqrt(70.0)) / 900.0;
+      const double xs[5] = {-outer, -inner, 0.0, inner, outer}, ws[5] = {wo, wi, 128.0 / 225.0, wi, wo};
+      x = xs[i];
+      w = ws[i];
+      return;
+    }
+  }
+}
+
+template <typename T, int L>
+__global__ __launch_bounds__(64) void k_so2_wigner(int64_t n, const T* __restrict__ vec, T* __restrict__ D) {
+  constexpr int NS = (L + 1) * (L + 1);
+  constexpr int ND = (L + 1) * (2 * L + 1) * (2 * L + 3) / 3;
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  double ux, uy, uz;
+  const double r = load_unit(vec + 3 * e, ux, uy, uz);
+  double R[3][3] = {{1.0, 0.0, 0.0}, {0.0, 1.0, 0.0}, {0.0, 0.0, 1.0}};
+  if (r > 0.0) {
+    const double sn = sqrt(ux * ux + uy * uy), cs = uz;
+    if (sn == 0.0) {
+      if (cs < 0.0) R[1][1] = R[2][2] = -1.0;
+    } else {
+      const double kx = uy / sn, ky = -ux / sn;  // unit axis u x z_hat / |u x z_hat|, kz = 0
+      const double K[3][3] = {{0.0, 0.0, ky}, {0.0, 0.0, -kx}, {-ky, kx, 0.0}};
+      for (int a = 0; a < 3; ++a)
+        for (int b = 0; b < 3; ++b) {
+          double k2 = 0.0;
+          for (int q = 0; q < 3; ++q) k2 += K[a][q] * K[q][b];
+          R[a][b] += sn * K[a][b] + (1.0 - cs) * k2;
+        }
+    }
+  }
+  double acc[ND];
+  for (int q = 0; q < ND; ++q) acc[q] = 0.0;
+  constexpr int NZ = L + 1, NP = 2 * L + 1;
+  for (int iz = 0; iz < NZ; ++iz) {
+    double z, wz;
+    gauss_legendre(NZ, iz, z, wz);
+    const double rho = sqrt(fmax(0.0, 1.0 - z * z));
+    for (int ip = 0; ip < NP; ++ip) {
+      double sp, cp;
+      sincos(2.0 * M_PI * ip / NP, &sp, &cp);
+      const double px = rho * cp, py = rho * sp;
+      const double qx = R[0][0] * px + R[0][1] * py + R[0][2] * z;
+      const double qy = R[1][0] * px + R[1][1] * py + R[1][2] * z;
+      const double qz = R[2][0] * px + R[2][1] * py + R[2][2] * z;
+      double Sp[NS], Sq[NS];
+      solid_harmonics<L, double, PlainOps<double>>(px, py, z, 1.0, 1.0, Sp);
+      solid_harmonics<L, double, PlainOps<double>>(qx, qy, qz, 1.0, 1.0, Sq);
+      const double w = wz / (2.0 * NP);  // (wz * 2 pi / NP) / (4 pi)
+      sh_for<L + 1>([&](auto IL) {
+        constexpr int l = IL, n2 = 2 * l + 1, off = l * (2 * l - 1) * (2 * l + 1) / 3;
+        const double wl = w * n2;  // Y = sqrt(2l+1) S on the unit sphere
+        sh_for<n2>([&](auto M) {
+          const double a = wl * Sq[l * l + M];
+          sh_for<n2>([&](auto N) { acc[off + M * n2 + N] += a * Sp[l * l + N]; });
+        });
+      });
+    }
+  }
+  T* out = D + e * ND;
+  for (int q = 0; q < ND; ++q) out[q] = T(acc[q]);
+}
+
+template <typename T, int L>
+hipError_t wigner_T(int64_t n, const void* vec, void* D, hipStream_t s) {
+  const int64_t blocks = (n + 63) / 64;
+  hipLaunchKernelGGL((k_so2_wigner<T, L>), dim3((unsigned)blocks), dim3(64), 0, s, n, static_cast<const T*>(vec),
+                     static_cast<T*>(D));
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t wigner_dispatch(int L, int64_t n, const void* vec, void* D, hipStream_t s) {
+  switch (L) {
+    case 0: return wigner_T<T, 0>(n, vec, D, s);
+    case 1: return wigner_T<T, 1>(n, vec, D, s);
+    case 2: return wigner_T<T, 2>(n, vec, D, s);
+    case 3: return wigner_T<T, 3>(n, vec, D, s);
+    case 4: return wigner_T<T, 4>(n, vec, D, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename T, int L>
 hipError_t sh_fwd_T(int64_t n, const void* vec, void* Y, hipStream_t s) {
   const int64_t blocks = (n + 255) / 256;
@@ -264,6 +380,11 @@ hipError_t launch_sh_backward(int L, bool f64, int64_t n_edges, const void* vec,
   if (n_edges <= 0) return hipSuccess;
   return f64 ? sh_dispatch<double>(false, L, n_edges, vec, grad_Y, grad_vec, s)
              : sh_dispatch<float>(false, L, n_edges, vec, grad_Y, grad_vec, s);
+}
+
+hipError_t launch_so2_wigner(int L, bool f64, int64_t n_edges, const void* vec, void* D, hipStream_t s) {
+  if (n_edges <= 0) return hipSuccess;
+  return f64 ? wigner_dispatch<double>(L, n_edges, vec, D, s) : wigner_dispatch<float>(L, n_edges, vec, D, s);
 }
 
 hipError_t launch_pos_backward(bool f64, int64_t n_nodes, const int32_t* src_row, const int32_t* src_eid,

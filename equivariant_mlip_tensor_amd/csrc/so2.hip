@@ -1,0 +1,418 @@
+// so2.hip -- SO(2) convolution on gfx950 (fp32).
+//
+// The operation (TrimSO(2), Abstract: rotation on gather, dense matrix
+// multiplications in the edge frame, inverse rotation on reduction), per edge
+// e with neighbour j and centre i:
+//   x~[l][c][m]  = sum_n D_e^l[m][n] x[j][l][c][n]          (rotation on gather)
+//   m = 0:  y~_0  = A_0 X_0
+//   m > 0:  y~_+m = A_m X_+m - B_m X_-m,  y~_-m = B_m X_+m + A_m X_-m
+//           (X_+-m: x~[l][c][+-m] over l = m..L, c, index (l - m) C + c)
+//   out[i][l][c][n] += sum_m D_e^l[m][n] y~[l][c][m]      (inverse rotation on reduction)
+// with A_m, B_m shared by all edges.  The backward needs grad_x, which is the
+// same operator with the adjoint maps (A^T, and B^T with the opposite sign)
+// run over the source-sorted rows on grad_out, and the map gradients, sums
+// over all edges of outer products of the rotated grad_out and x.
+//
+// Kernels (one wavefront = 64 lanes):
+//  * k_so2_conv<L, C, ADJ>: one wavefront per CSR row, edges in chunks of 16.
+//    Per chunk: the 16 Wigner rows go to LDS; each neighbour row is rotated
+//    in registers (lane = channel c and a share of the m) and written to an
+//    LDS tile [edge][node layout]; per |m| the maps run on the matrix cores
+//    (v_mfma_f32_16x16x4f32: M = the 16 edges, N = output (l, c), K = input
+//    (l, c)), their A and B fragments shared by the four products of a
+//    (+m, -m) pair, weights streamed from L2; the results overwrite the
+//    tile at the same (+-m) places; the inverse rotation then adds each
+//    edge's message into per-lane row sums.  Nothing per edge reaches HBM.
+//    The tile's edge stride is 2 mod 32 floats, which keeps the fragment
+//    reads (16 edges x 4 consecutive k) free of LDS bank conflicts.
+//  * k_so2_wgrad<L, C>: four wavefronts share one LDS copy of the rotated x
+//    and grad_out of 16 edges; each wavefront owns a fixed set of 16 x 16
+//    output tiles of the map gradients (compile-time list, its accumulators
+//    stay in registers over all of the block's edges) and runs them on the
+//    matrix cores with K = edges.  Per-block partial sums go to a caller
+//    workspace; k_so2_wsum adds them in block order (deterministic, no
+//    atomics).
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+#include <utility>
+
+#include "tp_common.hpp"
+
+namespace tpconv {
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+template <typename F, int... I>
+__device__ __forceinline__ void so2_sf(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void so2_for(F&& f) {
+  if constexpr (N > 0) so2_sf(f, std::make_integer_sequence<int, N>{});
+}
+
+__device__ __forceinline__ v4f mfma(float a, float b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int L, int C>
+struct So2Shape {
+  static_assert(C == 16 || C == 32, "channels: 16 or 32");
+  static constexpr int NC = (L + 1) * (L + 1);
+  static constexpr int DN = C * NC;                        // node row, floats
+  static constexpr int NSPLIT = 64 / C;                    // lanes per channel
+  static constexpr int PAD = (DN + 31) / 32 * 32 + 2;      // LDS tile edge stride
+  static constexpr int ND = (L + 1) * (2 * L + 1) * (2 * L + 3) / 3;  // Wigner floats per edge
+  static constexpr int NDP = ND + 1;                       // LDS stride of a Wigner row
+  static constexpr int kEdges = 16;
+  static constexpr int K(int m) { return (L + 1 - m) * C; }
+  static constexpr int doff(int l) { return l * (2 * l - 1) * (2 * l + 1) / 3; }
+  static constexpr int xoff(int l) { return C * l * l; }
+  static constexpr int woffA(int m) {
+    int o = 0;
+    for (int k = 0; k < m; ++k) o += (k ? 2 : 1) * K(k) * K(k);
+    return o;
+  }
+  static constexpr int woffB(int m) { return woffA(m) + K(m) * K(m); }
+  static constexpr int NW = woffA(L + 1);
+  static constexpr int J(int l) { return (2 * l + 1 + NSPLIT - 1) / NSPLIT; }  // components per lane, degree l
+  static constexpr int jbase(int l) {
+    int b = 0;
+    for (int k = 0; k < l; ++k) b += J(k);
+    return b;
+  }
+  static constexpr int NACC = jbase(L + 1);
+  // map-gradient jobs: one 16 x 16 tile (m, ot, it) of A_m (and of B_m when m > 0)
+  static constexpr int njobs() {
+    int n = 0;
+    for (int m = 0; m <= L; ++m) n += (K(m) / 16) * (K(m) / 16);
+    return n;
+  }
+  struct Job {
+    int m, ot, it;
+  };
+  static constexpr Job job(int j) {
+    for (int m = 0; m <= L; ++m) {
+      const int t = K(m) / 16;
+      if (j < t * t) return Job{m, j / t, j % t};
+      j -= t * t;
+    }
+    return Job{-1, 0, 0};
+  }
+};
+
+// Rotates neighbour row `xr` of one edge into the tile (rotation on gather):
+// lane (c, h) writes x~[l][c][m] for m = h, h + NSPLIT, ...
+template <int L, int C>
+__device__ __forceinline__ void rotate_in(const float* __restrict__ xr, const float* dle, float* te, int c, int h) {
+  using S = So2Shape<L, C>;
+  so2_for<L + 1>([&](auto IL) {
+    constexpr int l = IL, n2 = 2 * l + 1;
+    float xv[n2];
+    so2_for<n2>([&](auto N) { xv[N] = xr[S::xoff(l) + c * n2 + N]; });
+    so2_for<S::J(l)>([&](auto JJ) {
+      const int m = h + S::NSPLIT * int(JJ);
+      if (m < n2) {
+        const float* dr = dle + S::doff(l) + m * n2;
+        float s = 0.f;
+        so2_for<n2>([&](auto N) { s = fmaf(dr[N], xv[N], s); });
+        te[S::xoff(l) + c * n2 + m] = s;
+      }
+    });
+  });
+}
+
+template <int L, int C, bool ADJ>
+__global__ __launch_bounds__(64) void k_so2_conv(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
+                                                 const int32_t* __restrict__ eid, const int32_t* __restrict__ order,
+                                                 const float* __restrict__ X, const float* __restrict__ Dm,
+                                                 const float* __restrict__ W, float* __restrict__ out) {
+  using S = So2Shape<L, C>;
+  __shared__ float tile[S::kEdges * S::PAD];
+  __shared__ float dl[S::kEdges * S::NDP];
+  const int lane = threadIdx.x;
+  const int c = lane % C, h = lane / C;
+  const int row = order[blockIdx.x];
+  const int beg = row_ptr[row], end = row_ptr[row + 1];
+  float acc[S::NACC];
+  so2_for<S::NACC>([&](auto I) { acc[I] = 0.f; });
+
+  for (int k0 = beg; k0 < end; k0 += S::kEdges) {
+    const int ne = min(S::kEdges, end - k0);
+    const int my_n = lane < ne ? col[k0 + lane] : 0;
+    // the chunk's Wigner rows (zeros past the row end, so those edges rotate to zero)
+    for (int q = lane; q < S::kEdges * S::ND; q += 64) {
+      const int e = q / S::ND, r = q - e * S::ND;
+      dl[e * S::NDP + r] = e < ne ? Dm[(int64_t)eid[k0 + e] * S::ND + r] : 0.f;
+    }
+    __syncthreads();
+    for (int e = 0; e < S::kEdges; ++e) {  // wave-uniform
+      const int nb = __builtin_amdgcn_readlane(my_n, e);
+      rotate_in<L, C>(X + (int64_t)nb * S::DN, &dl[e * S::NDP], &tile[e * S::PAD], c, h);
+    }
+    __syncthreads();
+
+    // the per-|m| maps on the matrix cores
+    const int er = lane & 15;  // A fragment: edge row; B fragment and result: column
+    const int kq = lane >> 4;  // A/B fragment: k within the step; result: rows 4 kq .. 4 kq + 3
+    so2_for<L + 1>([&](auto IM) {
+      constexpr int m = IM;
+      constexpr int K = S::K(m), NT = K / 16, KS = K / 4;
+      const float* WA = W + S::woffA(m);
+      const float* WB = W + (m > 0 ? S::woffB(m) : 0);
+      v4f yp[NT], ym[m > 0 ? NT : 1];
+      so2_for<NT>([&](auto T) {
+        yp[T] = v4f{0.f, 0.f, 0.f, 0.f};
+        if constexpr (m > 0) ym[T] = v4f{0.f, 0.f, 0.f, 0.f};
+      });
+#pragma unroll 2
+      for (int ks = 0; ks < KS; ++ks) {
+        const int kk = 4 * ks + kq;
+        const int l1 = m + kk / C, c1 = kk % C;
+        const float* t1 = &tile[er * S::PAD + C * l1 * l1 + c1 * (2 * l1 + 1) + l1];
+        const float ap = t1[m];
+        const float am = m > 0 ? t1[-m] : 0.f;
+        so2_for<NT>([&](auto T) {
+          const int n = int(T) * 16 + er;
+          const float wa = ADJ ? WA[kk * K + n] : WA[n * K + kk];
+          yp[T] = mfma(ap, wa, yp[T]);
+          if constexpr (m > 0) {
+            const float wb = ADJ ? WB[kk * K + n] : WB[n * K + kk];
+            // forward: y+ += A x+ - B x-, y- += B x+ + A x-
+            // adjoint: y+ += A^T g+ + B^T g-, y- += -B^T g+ + A^T g-
+            yp[T] = mfma(am, ADJ ? wb : -wb, yp[T]);
+            ym[T] = mfma(ap, ADJ ? -wb : wb, ym[T]);
+            ym[T] = mfma(am, wa, ym[T]);
+          }
+        });
+      }
+      // every read of this |m| is done: the results take the same places
+      so2_for<NT>([&](auto T) {
+        const int n = int(T) * 16 + er;
+        const int l3 = m + n / C, c3 = n % C;
+        float* t3 = &tile[C * l3 * l3 + c3 * (2 * l3 + 1) + l3];
+        so2_for<4>([&](auto R) {
+          const int e = 4 * kq + int(R);
+          t3[e * S::PAD + m] = yp[T][int(R)];
+          if constexpr (m > 0) t3[e * S::PAD - m] = ym[T][int(R)];
+        });
+      });
+    });
+    __syncthreads();
+
+    // inverse rotation on reduction: lane (c, h) sums components n = h, h + NSPLIT, ...
+    for (int e = 0; e < ne; ++e) {  // wave-uniform
+      const float* te = &tile[e * S::PAD];
+      const float* dle = &dl[e * S::NDP];
+      so2_for<L + 1>([&](auto IL) {
+        constexpr int l = IL, n2 = 2 * l + 1;
+        float yv[n2];
+        so2_for<n2>([&](auto M) { yv[M] = te[S::xoff(l) + c * n2 + M]; });
+        so2_for<S::J(l)>([&](auto JJ) {
+          const int n = h + S::NSPLIT * int(JJ);
+          if (n < n2) {
+            float s = acc[S::jbase(l) + JJ];
+            so2_for<n2>([&](auto M) { s = fmaf(dle[S::doff(l) + M * n2 + n], yv[M], s); });
+            acc[S::jbase(l) + JJ] = s;
+          }
+        });
+      });
+    }
+    __syncthreads();
+  }
+
+  float* orow = out + (int64_t)row * S::DN;
+  so2_for<L + 1>([&](auto IL) {
+    constexpr int l = IL, n2 = 2 * l + 1;
+    so2_for<S::J(l)>([&](auto JJ) {
+      const int n = h + S::NSPLIT * int(JJ);
+      if (n < n2) orow[S::xoff(l) + c * n2 + n] = acc[S::jbase(l) + JJ];
+    });
+  });
+}
+
+// row of CSR slot k: the last r with row_ptr[r] <= k
+__device__ __forceinline__ int slot_row(const int32_t* __restrict__ row_ptr, int n_rows, int k) {
+  int lo = 0, hi = n_rows - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (row_ptr[mid] <= k)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+template <int L, int C, int WV>
+__device__ __forceinline__ void wgrad_wave(int n_rows, int64_t s0, int64_t s1, const int32_t* __restrict__ row_ptr,
+                                           const int32_t* __restrict__ col, const int32_t* __restrict__ eid,
+                                           const float* __restrict__ X, const float* __restrict__ G,
+                                           const float* __restrict__ Dm, float* __restrict__ part, float* xt,
+                                           float* gt, float* dl) {
+  using S = So2Shape<L, C>;
+  constexpr int NJ = S::njobs();
+  constexpr int NMINE = (NJ - WV + 3) / 4;  // jobs j = WV, WV + 4, ...
+  const int lane = threadIdx.x & 63;
+  const int c = lane % C, h = lane / C;
+  const int er = lane & 15, kq = lane >> 4;
+  v4f accA[NMINE], accB[NMINE];
+  so2_for<NMINE>([&](auto I) {
+    accA[I] = v4f{0.f, 0.f, 0.f, 0.f};
+    accB[I] = v4f{0.f, 0.f, 0.f, 0.f};
+  });
+
+  for (int64_t k0 = s0; k0 < s1; k0 += S::kEdges) {
+    const int ne = (int)min<int64_t>(S::kEdges, s1 - k0);
+    int my_s = 0, my_d = 0;
+    if (er < ne) {
+      const int k = (int)(k0 + er);
+      my_s = col[k];
+      my_d = slot_row(row_ptr, n_rows, k);
+    }
+    for (int q = threadIdx.x; q < S::kEdges * S::ND; q += 256) {
+      const int e = q / S::ND, r = q - e * S::ND;
+      dl[e * S::NDP + r] = e < ne ? Dm[(int64_t)eid[k0 + e] * S::ND + r] : 0.f;
+    }
+    __syncthreads();
+    so2_for<4>([&](auto I) {
+      constexpr int e = WV + 4 * int(I);
+      const int sn = __builtin_amdgcn_readlane(my_s, e);
+      const int dn = __builtin_amdgcn_readlane(my_d, e);
+      rotate_in<L, C>(X + (int64_t)sn * S::DN, &dl[e * S::NDP], &xt[e * S::PAD], c, h);
+      rotate_in<L, C>(G + (int64_t)dn * S::DN, &dl[e * S::NDP], &gt[e * S::PAD], c, h);
+    });
+    __syncthreads();
+    so2_for<NMINE>([&](auto I) {
+      constexpr typename S::Job jb = S::job(WV + 4 * int(I));
+      constexpr int m = jb.m;
+      const int o = jb.ot * 16 + er, i = jb.it * 16 + er;
+      const int lo = m + o / C, co = o % C, li = m + i / C, ci = i % C;
+      const float* go = &gt[C * lo * lo + co * (2 * lo + 1) + lo];
+      const float* xi = &xt[C * li * li + ci * (2 * li + 1) + li];
+      so2_for<4>([&](auto KS) {
+        const int e = 4 * int(KS) + kq;  // K index of both fragments: the edge
+        const float gp = go[e * S::PAD + m], xp = xi[e * S::PAD + m];
+        accA[I] = mfma(gp, xp, accA[I]);
+        if constexpr (m > 0) {
+          const float gm = go[e * S::PAD - m], xm = xi[e * S::PAD - m];
+          accA[I] = mfma(gm, xm, accA[I]);   // dA += g+ x+^T + g- x-^T
+          accB[I] = mfma(gm, xp, accB[I]);   // dB += g- x+^T - g+ x-^T
+          accB[I] = mfma(-gp, xm, accB[I]);
+        }
+      });
+    });
+    __syncthreads();
+  }
+
+  float* pb = part + (int64_t)blockIdx.x * S::NW;
+  so2_for<NMINE>([&](auto I) {
+    constexpr typename S::Job jb = S::job(WV + 4 * int(I));
+    constexpr int m = jb.m, K = S::K(m);
+    const int i = jb.it * 16 + er;
+    so2_for<4>([&](auto R) {
+      const int o = jb.ot * 16 + 4 * kq + int(R);
+      pb[S::woffA(m) + o * K + i] = accA[I][int(R)];
+      if constexpr (m > 0) pb[S::woffB(m) + o * K + i] = accB[I][int(R)];
+    });
+  });
+}
+
+template <int L, int C>
+__global__ __launch_bounds__(256) void k_so2_wgrad(int n_rows, int64_t n_slots, int64_t per_block,
+                                                   const int32_t* __restrict__ row_ptr,
+                                                   const int32_t* __restrict__ col, const int32_t* __restrict__ eid,
+                                                   const float* __restrict__ X, const float* __restrict__ G,
+                                                   const float* __restrict__ Dm, float* __restrict__ part) {
+  using S = So2Shape<L, C>;
+  __shared__ float xt[S::kEdges * S::PAD];
+  __shared__ float gt[S::kEdges * S::PAD];
+  __shared__ float dl[S::kEdges * S::NDP];
+  const int64_t s0 = (int64_t)blockIdx.x * per_block;
+  const int64_t s1 = min(n_slots, s0 + per_block);
+  switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
+    case 0: wgrad_wave<L, C, 0>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, part, xt, gt, dl); break;
+    case 1: wgrad_wave<L, C, 1>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, part, xt, gt, dl); break;
+    case 2: wgrad_wave<L, C, 2>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, part, xt, gt, dl); break;
+    default: wgrad_wave<L, C, 3>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, part, xt, gt, dl); break;
+  }
+}
+
+// grad_w[j] = sum over blocks b (in order) of part[b][j]
+__global__ __launch_bounds__(256) void k_so2_wsum(int nb, int64_t nw, const float* __restrict__ part,
+                                                  float* __restrict__ gw) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= nw) return;
+  double s = 0.0;
+  for (int b = 0; b < nb; ++b) s += part[(int64_t)b * nw + j];
+  gw[j] = (float)s;
+}
+
+template <int L, int C>
+hipError_t conv_LC(bool adjoint, int n_rows, const int32_t* row_ptr, const int32_t* col, const int32_t* eid,
+                   const int32_t* order, const float* X, const float* D, const float* W, float* out, hipStream_t s) {
+  if (adjoint)
+    hipLaunchKernelGGL((k_so2_conv<L, C, true>), dim3((unsigned)n_rows), dim3(64), 0, s, row_ptr, col, eid, order, X,
+                       D, W, out);
+  else
+    hipLaunchKernelGGL((k_so2_conv<L, C, false>), dim3((unsigned)n_rows), dim3(64), 0, s, row_ptr, col, eid, order,
+                       X, D, W, out);
+  return hipGetLastError();
+}
+
+template <int L, int C>
+hipError_t wgrad_LC(int n_rows, int64_t n_slots, int nb, const int32_t* row_ptr, const int32_t* col,
+                    const int32_t* eid, const float* X, const float* G, const float* D, float* part, float* gw,
+                    hipStream_t s) {
+  using S = So2Shape<L, C>;
+  const int64_t per_block = (n_slots + nb - 1) / nb;
+  hipLaunchKernelGGL((k_so2_wgrad<L, C>), dim3((unsigned)nb), dim3(256), 0, s, n_rows, n_slots, per_block, row_ptr,
+                     col, eid, X, G, D, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_so2_wsum, dim3((unsigned)((S::NW + 255) / 256)), dim3(256), 0, s, nb, (int64_t)S::NW, part,
+                     gw);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t so2_weight_numel(int L, int C) {
+  int64_t n = 0;
+  for (int m = 0; m <= L; ++m) n += (m ? 2 : 1) * int64_t((L + 1 - m) * C) * ((L + 1 - m) * C);
+  return n;
+}
+
+int so2_wgrad_blocks(int64_t n_edges) {
+  const int64_t nb = (n_edges + 63) / 64;
+  return (int)(nb < 1 ? 1 : (nb > 512 ? 512 : nb));
+}
+
+#define SO2_CASES(F, ...)                                   \
+  switch (L * 100 + C) {                                    \
+    case 116: return F<1, 16>(__VA_ARGS__);                 \
+    case 132: return F<1, 32>(__VA_ARGS__);                 \
+    case 216: return F<2, 16>(__VA_ARGS__);                 \
+    case 232: return F<2, 32>(__VA_ARGS__);                 \
+    case 316: return F<3, 16>(__VA_ARGS__);                 \
+    case 332: return F<3, 32>(__VA_ARGS__);                 \
+    default: return hipErrorInvalidValue;                   \
+  }
+
+hipError_t launch_so2_conv(int L, int C, bool adjoint, int n_rows, const int32_t* row_ptr, const int32_t* col,
+                           const int32_t* eid, const int32_t* order, const float* X, const float* D, const float* W,
+                           float* out, hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  SO2_CASES(conv_LC, adjoint, n_rows, row_ptr, col, eid, order, X, D, W, out, s)
+}
+
+hipError_t launch_so2_wgrad(int L, int C, int n_rows, int64_t n_edges, const int32_t* row_ptr, const int32_t* col,
+                            const int32_t* eid, const float* X, const float* G, const float* D, float* part,
+                            float* grad_w, hipStream_t s) {
+  const int nb = so2_wgrad_blocks(n_edges);
+  SO2_CASES(wgrad_LC, n_rows, n_edges, nb, row_ptr, col, eid, X, G, D, part, grad_w, s)
+}
+
+}  // namespace tpconv

@@ -100,6 +100,16 @@ TPCONV_DECLARE_LAUNCHERS(3)
 TPCONV_DECLARE_LAUNCHERS(4)
 
 // Edge harmonics, their gradient and the position gradient (sh.hip).
+// SO(2) convolution (so2.hip, sh.hip)
+hipError_t launch_so2_wigner(int L, bool f64, int64_t n_edges, const void* vec, void* D, hipStream_t s);
+int64_t so2_weight_numel(int L, int C);
+int so2_wgrad_blocks(int64_t n_edges);
+hipError_t launch_so2_conv(int L, int C, bool adjoint, int n_rows, const int32_t* row_ptr, const int32_t* col,
+                           const int32_t* eid, const int32_t* order, const float* X, const float* D, const float* W,
+                           float* out, hipStream_t s);
+hipError_t launch_so2_wgrad(int L, int C, int n_rows, int64_t n_edges, const int32_t* row_ptr, const int32_t* col,
+                            const int32_t* eid, const float* X, const float* G, const float* D, float* part,
+                            float* grad_w, hipStream_t s);
 hipError_t launch_sh(int L, bool f64, int64_t n_edges, const void* vec, void* Y, hipStream_t s);
 hipError_t launch_sh_backward(int L, bool f64, int64_t n_edges, const void* vec, const void* grad_Y, void* grad_vec,
                               hipStream_t s);

@@ -29,7 +29,8 @@ STATUS = {0: "TPCONV_OK", 1: "TPCONV_E_INVALID_ARG", 2: "TPCONV_E_IRREPS", 3: "T
 EXPORTS = ("tpconv_plan", "tpconv_plan_query", "tpconv_plan_paths", "tpconv_plan_table", "tpconv_plan_destroy",
            "tpconv_graph_workspace_bytes", "tpconv_graph_create", "tpconv_graph_export", "tpconv_graph_destroy",
            "tpconv_forward", "tpconv_backward", "tpconv_double_backward", "tpconv_sh", "tpconv_sh_backward",
-           "tpconv_positions_backward", "tpconv_last_error")
+           "tpconv_positions_backward", "tpconv_so2_weight_numel", "tpconv_so2_rotations", "tpconv_so2_forward",
+           "tpconv_so2_workspace_bytes", "tpconv_so2_backward", "tpconv_last_error")
 
 
 class TPConvError(RuntimeError):
@@ -68,6 +69,12 @@ def _load():
         "tpconv_sh": (i32, [vp, i64, vp, vp, vp]),
         "tpconv_sh_backward": (i32, [vp, i64, vp, vp, vp, vp]),
         "tpconv_positions_backward": (i32, [vp, vp, vp, vp, vp]),
+        "tpconv_so2_weight_numel": (i64, [ctypes.c_int, ctypes.c_int]),
+        "tpconv_so2_rotations": (i32, [ctypes.c_int, ctypes.c_int, i64, vp, vp, vp]),
+        "tpconv_so2_forward": (i32, [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp]),
+        "tpconv_so2_workspace_bytes": (sz, [ctypes.c_int, ctypes.c_int, i64]),
+        "tpconv_so2_backward": (i32, [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, sz,
+                                      vp]),
         "tpconv_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -314,3 +321,83 @@ def tpconv_positions_backward(plan: Plan, graph: Graph, grad_vec, grad_pos=None,
     _check(_lib.tpconv_positions_backward(plan.handle, graph.handle, _ptr(grad_vec), _ptr(grad_pos),
                                           _stream_handle(stream)))
     return grad_pos
+
+
+# ---------------------------------------------------------- SO(2) convolution
+def tpconv_so2_weight_numel(lmax: int, channels: int) -> int:
+    """Length of the map weights A_0, A_1, B_1, ..., A_L, B_L (0: unsupported)."""
+    return int(_lib.tpconv_so2_weight_numel(int(lmax), int(channels)))
+
+
+def _so2_sizes(lmax, channels):
+    nw = tpconv_so2_weight_numel(lmax, channels)
+    if nw == 0:
+        raise TPConvError(3, f"SO(2) convolution: unsupported lmax={lmax}, channels={channels}")
+    return channels * (lmax + 1) ** 2, (lmax + 1) * (2 * lmax + 1) * (2 * lmax + 3) // 3, nw
+
+
+def tpconv_so2_rotations(lmax: int, vec, D=None, stream=None) -> torch.Tensor:
+    """D [E, sum_l (2l+1)^2]: real Wigner blocks of each edge's frame rotation
+    (dtype of vec, float32 or float64)."""
+    E = vec.shape[0] if vec.dim() == 2 else -1
+    dt = vec.dtype
+    _need(vec, (E, 3), dt, "vec")
+    nd = (lmax + 1) * (2 * lmax + 1) * (2 * lmax + 3) // 3
+    if D is None:
+        D = torch.empty((E, nd), dtype=dt, device=vec.device)
+    _need(D, (E, nd), dt, "D")
+    _check(_lib.tpconv_so2_rotations(int(lmax), F64 if dt == torch.float64 else F32, E, _ptr(vec), _ptr(D),
+                                     _stream_handle(stream)))
+    return D
+
+
+def tpconv_so2_forward(graph: Graph, lmax: int, channels: int, x, D, weights, out=None, stream=None) -> torch.Tensor:
+    """out [N, C (L+1)^2] = sum over in-edges of D^T SO2(D x[src])."""
+    N, E = graph.n_nodes, graph.n_edges
+    dn, nd, nw = _so2_sizes(lmax, channels)
+    f = torch.float32
+    _need(x, (N, dn), f, "x")
+    _need(D, (E, nd), f, "D")
+    _need(weights, (nw,), f, "weights")
+    if out is None:
+        out = torch.empty((N, dn), dtype=f, device=x.device)
+    _need(out, (N, dn), f, "out")
+    _check(_lib.tpconv_so2_forward(graph.handle, int(lmax), int(channels), F32, _ptr(x), _ptr(D), _ptr(weights),
+                                   _ptr(out), _stream_handle(stream)))
+    return out
+
+
+def tpconv_so2_workspace_bytes(lmax: int, channels: int, n_edges: int) -> int:
+    return int(_lib.tpconv_so2_workspace_bytes(int(lmax), int(channels), int(n_edges)))
+
+
+def tpconv_so2_backward(graph: Graph, lmax: int, channels: int, x, D, weights, grad_out, grad_x=None,
+                        grad_weights=None, workspace=None, need=(True, True),
+                        stream=None) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
+    """(grad_x, grad_weights) of <grad_out, out>; an output is None when `need` turns it off."""
+    N, E = graph.n_nodes, graph.n_edges
+    dn, nd, nw = _so2_sizes(lmax, channels)
+    f = torch.float32
+    _need(x, (N, dn), f, "x")
+    _need(D, (E, nd), f, "D")
+    _need(weights, (nw,), f, "weights")
+    _need(grad_out, (N, dn), f, "grad_out")
+    dev = x.device
+    if need[0] and grad_x is None:
+        grad_x = torch.empty((N, dn), dtype=f, device=dev)
+    if need[1] and grad_weights is None:
+        grad_weights = torch.empty((nw,), dtype=f, device=dev)
+    if grad_x is not None:
+        _need(grad_x, (N, dn), f, "grad_x")
+    if grad_weights is not None:
+        _need(grad_weights, (nw,), f, "grad_weights")
+    ws_bytes = 0
+    if grad_weights is not None:
+        if workspace is None:
+            workspace = torch.empty(max(tpconv_so2_workspace_bytes(lmax, channels, E), 256), dtype=torch.uint8,
+                                    device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.tpconv_so2_backward(graph.handle, int(lmax), int(channels), F32, _ptr(x), _ptr(D), _ptr(weights),
+                                    _ptr(grad_out), _ptr(grad_x), _ptr(grad_weights), _ptr(workspace), ws_bytes,
+                                    _stream_handle(stream)))
+    return grad_x, grad_weights

@@ -245,6 +245,75 @@ tpconv_status tpconv_sh_backward(tpconv_plan_t plan, int64_t n_edges, const void
 tpconv_status tpconv_positions_backward(tpconv_plan_t plan, tpconv_graph_t g, const void* grad_vec, void* grad_pos,
                                         hipStream_t stream);
 
+/* ------------------------------------------------ SO(2) convolution ------
+ * The convolution of SO(2)-based potentials (TrimSO(2), Abstract: rotation
+ * on gather, dense matrix multiplications in the edge frame, inverse
+ * rotation on reduction; the page prints no formula, so the plainest
+ * reading is used).  Per edge e (neighbour j = src, centre i = dst):
+ *   x~[l]  = D_e^l x[j, l]                       (per channel)
+ *   m = 0: y~_0 = A_0 X_0;   m > 0: y~_+m = A_m X_+m - B_m X_-m,
+ *                                   y~_-m = B_m X_+m + A_m X_-m
+ *   out[i, l] += D_e^l^T y~[l]
+ * X_+-m stacks x~[l][c][+-m] over l = m..L and channels c at index
+ * (l - m) C + c; A_m, B_m are shared by all edges.  The output does not
+ * depend on the roll of the edge frame about the edge axis.
+ *
+ * Layouts (row-major, fp32):
+ *   x, out, grad  [N][C (L+1)^2]: degree l at column C l^2, stored [C][2l+1]
+ *                 (the irreps layout "Cx0e+Cx1o+...", every l = 0..L present)
+ *   D             [E][sum_l (2l+1)^2]: block l at sum_{k<l} (2k+1)^2, [m][n]
+ *   weights       A_0, A_1, B_1, ..., A_L, B_L, each [K_m][K_m] (out, in),
+ *                 K_m = (L+1-m) C; tpconv_so2_weight_numel(L, C) floats.
+ * Supported: 1 <= lmax <= 3, channels 16 or 32, TPCONV_F32 (rotations: also
+ * lmax 0 and 4, and TPCONV_F64).  Other values: TPCONV_E_UNSUPPORTED. */
+
+/* Number of map weights (and of grad_weights) for (lmax, channels); 0 when
+ * the pair is unsupported. */
+int64_t tpconv_so2_weight_numel(int lmax, int channels);
+
+/* tpconv_so2_rotations: D[E][sum (2l+1)^2] for edge vectors vec[E][3], both
+ * in `dtype`.  The frame R_e is the proper rotation about u x z_hat through
+ * the angle between u = vec / |vec| and z_hat (Rodrigues), so R_e u = z_hat;
+ * the identity for a zero vector or u = z_hat, diag(1, -1, -1) for
+ * u = -z_hat.  D^l(R) is the real Wigner matrix with Y_l(R v) = D^l(R) Y_l(v)
+ * for the harmonics of tpconv_sh (fp64 arithmetic inside).  Errors:
+ * TPCONV_E_INVALID_ARG (n_edges < 0, NULL pointer with n_edges > 0),
+ * TPCONV_E_UNSUPPORTED (lmax outside 0..4), TPCONV_E_HIP. */
+tpconv_status tpconv_so2_rotations(int lmax, tpconv_dtype dtype, int64_t n_edges, const void* vec, void* D,
+                                   hipStream_t stream);
+
+/* tpconv_so2_forward: out (overwritten, zero rows for nodes without in-edges)
+ * over the graph's destination-sorted rows: one wavefront per row; per chunk
+ * of 16 edges the neighbour rows are rotated into an LDS tile, the per-|m|
+ * maps run on the matrix cores, and the inverse rotations are summed in
+ * registers.  x, D, weights, out: device fp32.  Errors: TPCONV_E_INVALID_ARG
+ * (NULL handle or pointer), TPCONV_E_UNSUPPORTED, TPCONV_E_HIP. */
+tpconv_status tpconv_so2_forward(tpconv_graph_t g, int lmax, int channels, tpconv_dtype dtype, const void* x,
+                                 const void* D, const void* weights, void* out, hipStream_t stream);
+
+/* Workspace bytes tpconv_so2_backward needs for n_edges edges (the partial
+ * sums of the map gradients, one row of weight_numel floats per block of at
+ * most 512 blocks). */
+size_t tpconv_so2_workspace_bytes(int lmax, int channels, int64_t n_edges);
+
+/* tpconv_so2_backward: gradients of <grad_out, out>:
+ *   grad_x[j]     = sum_{e: src = j} D_e^T SO2^T(D_e grad_out[dst e])
+ *                   (the forward's kernel with the adjoint maps, over the
+ *                   source-sorted rows);
+ *   grad_weights  = sum over edges of g~ x~^T per block (g~, x~ the rotated
+ *                   grad_out[dst] and x[src]):  A_0: g~_0 X_0^T;
+ *                   A_m: g~_+m X_+m^T + g~_-m X_-m^T;
+ *                   B_m: g~_-m X_+m^T - g~_+m X_-m^T;
+ *                   partial sums per block of edges in `workspace`
+ *                   (tpconv_so2_workspace_bytes), then added in block order.
+ * Outputs are overwritten; pass NULL to skip one (grad_weights NULL needs no
+ * workspace).  Deterministic (no atomics).  Errors: TPCONV_E_INVALID_ARG,
+ * TPCONV_E_WORKSPACE (workspace too small), TPCONV_E_UNSUPPORTED,
+ * TPCONV_E_HIP. */
+tpconv_status tpconv_so2_backward(tpconv_graph_t g, int lmax, int channels, tpconv_dtype dtype, const void* x,
+                                  const void* D, const void* weights, const void* grad_out, void* grad_x,
+                                  void* grad_weights, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* tpconv_last_error(void);
 

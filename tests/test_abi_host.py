@@ -31,12 +31,12 @@ def tp():
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tpconv_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(tpconv_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(tp):
     declared = header_functions()
-    assert len(declared) == 16
+    assert len(declared) == 21
     assert sorted(tp.EXPORTS) == declared
     lib = ctypes.CDLL(LIB)
     for name in declared:
@@ -140,3 +140,31 @@ def test_null_and_size_errors_need_no_gpu(tp):
     assert lib.tpconv_graph_create(10, 5, None, None, buf, 64, None, ctypes.byref(g)) == 1
     assert lib.tpconv_graph_create(10, 100, buf, buf, buf, 64, None, ctypes.byref(g)) == 5
     assert "workspace" in tp.tpconv_last_error()
+
+
+def test_so2_sizes_and_errors_need_no_gpu(tp):
+    from oracle.so2 import weight_numel
+    lib = tp._lib
+    for L in (1, 2, 3):
+        for C in (16, 32):
+            assert tp.tpconv_so2_weight_numel(L, C) == weight_numel(L, C)
+            nb = min(512, max(1, -(-100000 // 64)))
+            assert tp.tpconv_so2_workspace_bytes(L, C, 100000) == nb * weight_numel(L, C) * 4
+    assert tp.tpconv_so2_weight_numel(3, 32) == 45056
+    for L, C in ((0, 16), (4, 16), (3, 8), (3, 64), (2, 24)):
+        assert tp.tpconv_so2_weight_numel(L, C) == 0
+        assert tp.tpconv_so2_workspace_bytes(L, C, 10) == 0
+    buf = (ctypes.c_uint8 * 64)()
+    assert lib.tpconv_so2_rotations(5, 0, 1, buf, buf, None) == 3
+    assert lib.tpconv_so2_rotations(2, 0, 1, None, None, None) == 1
+    assert lib.tpconv_so2_rotations(2, 7, 1, buf, buf, None) == 1        # unknown dtype
+    assert lib.tpconv_so2_rotations(2, 0, -1, buf, buf, None) == 1
+    assert lib.tpconv_so2_rotations(2, 0, 0, None, None, None) == 0       # nothing to do
+    assert lib.tpconv_so2_forward(None, 2, 16, 0, None, None, None, None, None) == 1
+    assert lib.tpconv_so2_backward(None, 2, 16, 0, *([None] * 7), 0, None) == 1
+    # unsupported shapes and dtypes are refused before the graph is read
+    fake = ctypes.c_void_p(ctypes.addressof(buf))
+    assert lib.tpconv_so2_forward(fake, 4, 16, 0, None, None, None, None, None) == 3
+    assert lib.tpconv_so2_forward(fake, 2, 16, 1, None, None, None, None, None) == 3
+    assert lib.tpconv_so2_backward(fake, 2, 64, 0, *([None] * 7), 0, None) == 3
+

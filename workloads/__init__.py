@@ -23,6 +23,11 @@ graphs stand in for those systems, whose datasets and weights are not used):
   c28k  28000 atoms, density 0.1/A^3, periodic, cutoff 5 A,
         64x0e+64x1o+64x2e+64x3o, SH l<=3, fp32
 
+SO(2) convolution shapes on the same graphs (SO2_SHAPES: degree bound L and
+channels C, every l = 0..L present with C channels): tiny L=1 C=16, c1k L=2
+C=32, c4k L=3 C=32, c2k L=3 C=16, c28k L=3 C=32; x and G N(0,1), the map
+weights N(0,1)/sqrt(2 C (L+1)), fp32, from their own seeded stream.
+
 Edges are ordered pairs (i != j) closer than the cutoff (minimum image when
 periodic), src = j (neighbour), dst = i (centre), edge vector
 r = pos[src] - pos[dst]; they are emitted dst-major, src ascending.  x and G
@@ -79,6 +84,9 @@ WORKLOADS = {
     "c28k": Workload(5, "c28k", 28000, 5.0, "64x0e+64x1o+64x2e+64x3o", 3, "64x0e+64x1o+64x2e+64x3o", "f32",
                      density=0.1),
 }
+
+
+SO2_SHAPES = {"tiny": (1, 16), "c1k": (2, 32), "c4k": (3, 32), "c2k": (3, 16), "c28k": (3, 32)}
 
 
 def rng_for(key: int, stream: int = 0) -> np.random.Generator:
@@ -213,3 +221,21 @@ def random_rotation(rng: np.random.Generator) -> np.ndarray:
     if np.linalg.det(q) < 0:
         q[:, 0] = -q[:, 0]
     return q
+
+
+def make_so2_inputs(w: Workload, weight_numel: int):
+    """Inputs of one SO(2)-convolution forward+backward on workload w's graph
+    (fp32 numpy): dict(n_nodes, src, dst, vec, lmax, channels, x, weights, G)
+    with x, G [N, C (L+1)^2] and weights [weight_numel] (the width comes from
+    the caller)."""
+    lmax, C = SO2_SHAPES[w.name]
+    g = make_graph(w)
+    g.pop("rng")
+    rng = rng_for(w.key, stream=3)
+    d = C * (lmax + 1) ** 2
+    x = rng.standard_normal((w.n_atoms, d), dtype=np.float32)
+    weights = rng.standard_normal(weight_numel, dtype=np.float32) * np.float32(1.0 / sqrt(2.0 * C * (lmax + 1)))
+    G = rng.standard_normal((w.n_atoms, d), dtype=np.float32)
+    g.update(n_nodes=w.n_atoms, lmax=lmax, channels=C, x=x, weights=weights, G=G)
+    return g
+
