@@ -10,8 +10,10 @@ Prints one JSON line: edges/s (value), per-kernel times, the dominant
 kernel's roofline point, and the fp64 CPU oracle timed on a bounded sample
 of the same workload.  Outside the timed steps it also reports cold-cache
 kernel times (1 GiB read before each step), the double backward's two
-kernels (tpconv_double_backward with seeded cotangents) and the upstream
-kernels (edge harmonics, their gradient, the position gradient).
+kernels (tpconv_double_backward with seeded cotangents), the upstream
+kernels (edge harmonics, their gradient, the position gradient) and the SO(2)
+convolution on the same graph (its rotations, forward, grad_x and
+map-gradient passes, against the fp32 matrix-core peak).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -31,6 +33,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 FP32_VALU_PEAK_TFLOPS = 157.3  # 256 CU x 2.4 GHz x 64 lanes x 2 flop x 2 (packed FMA)
 FP32_VALU_PLAIN_TFLOPS = 78.6  # the same without packed FMA, which this build does not emit
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix-core peak
 
 
 def parse():
@@ -48,6 +51,8 @@ def parse():
                    help="timed double-backward calls after the fwd+bwd steps (0 skips); reported as double_backward")
     p.add_argument("--upstream-reps", type=int, default=20,
                    help="timed calls of the edge-harmonics / position-gradient kernels (0 skips); reported as upstream")
+    p.add_argument("--so2-reps", type=int, default=20,
+                   help="timed calls of each SO(2)-convolution pass on the same graph (0 skips); reported as so2")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="also run one plain device copy of this many MiB (scales rocprofv3 FETCH/WRITE_SIZE)")
     return p.parse_args()
@@ -70,6 +75,13 @@ def dd_algorithmic_bytes(plan, n_nodes, n_edges, b):
     ddf = n_edges * ((2 * PU + 2 * Dsh) * b + 4) + n_nodes * ((2 * Din + Dout) * b + 4)
     ddb = n_edges * ((3 * PU + 3 * Dsh) * b + 8) + n_nodes * ((3 * Din + Dout) * b + 4)
     return ddf, ddb
+
+
+def so2_flops_per_edge(lmax, C):
+    """Dense-map flops per edge: 2 K_0^2 + 4 x 2 K_m^2 for m >= 1 (four K_m x K_m
+    products per (+m, -m) pair); the rotations' VALU work is not counted."""
+    ks = [(lmax + 1 - m) * C for m in range(lmax + 1)]
+    return 2 * (ks[0] ** 2 + 4 * sum(k * k for k in ks[1:]))
 
 
 def kernel_source_hash():
@@ -276,6 +288,46 @@ def main():
               "frac_of_peak": round((ddf_bytes + ddb_bytes) / (tot * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del ga, gb, gc, gx_, gY_, gW_, gG_
 
+    so2 = None
+    if args.so2_reps > 0 and w.name in workloads.SO2_SHAPES:
+        # the SO(2) convolution on the same graph, each pass timed alone
+        L2, C2 = workloads.SO2_SHAPES[w.name]
+        s2 = workloads.make_so2_inputs(w, tp.tpconv_so2_weight_numel(L2, C2))
+        vec2, x2, w2, G2 = T(s2["vec"].astype(np.float32)), T(s2["x"]), T(s2["weights"]), T(s2["G"])
+        del s2
+        D2 = tp.tpconv_so2_rotations(L2, vec2)
+        o2, gx2 = torch.empty_like(x2), torch.empty_like(x2)
+        gw2 = torch.empty_like(w2)
+        ws2 = torch.empty(tp.tpconv_so2_workspace_bytes(L2, C2, E), dtype=torch.uint8, device=dev)
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.so2_reps + 2)]
+        for k in range(args.so2_reps + 2):   # the first two are warm-up
+            sev[k][0].record(stream)
+            tp.tpconv_so2_rotations(L2, vec2, D2)
+            sev[k][1].record(stream)
+            tp.tpconv_so2_forward(graph, L2, C2, x2, D2, w2, o2)
+            sev[k][2].record(stream)
+            tp.tpconv_so2_backward(graph, L2, C2, x2, D2, w2, G2, grad_x=gx2, need=(True, False))
+            sev[k][3].record(stream)
+            tp.tpconv_so2_backward(graph, L2, C2, x2, D2, w2, G2, grad_weights=gw2, workspace=ws2,
+                                   need=(False, True))
+            sev[k][4].record(stream)
+        torch.cuda.synchronize()
+        med = [float(np.median([e[i].elapsed_time(e[i + 1]) for e in sev[2:]])) for i in range(4)]
+        fl = so2_flops_per_edge(L2, C2) * E
+        tf = lambda ms: round(fl / (ms * 1e-3) / 1e12, 2)   # noqa: E731
+        so2 = {"shape": f"l<={L2}, {C2} channels, {N} nodes, {E} edges, fp32",
+               "flops_per_pass": int(fl),
+               "rotations_ms_median": round(med[0], 4),
+               "forward_ms_median": round(med[1], 4), "forward_TFLOPs": tf(med[1]),
+               "grad_x_ms_median": round(med[2], 4), "grad_x_TFLOPs": tf(med[2]),
+               "grad_weights_ms_median": round(med[3], 4), "grad_weights_TFLOPs": tf(med[3]),
+               "roofline": {"bound": "mfma", "kernel": "k_so2_conv (forward)", "achieved": tf(med[1]),
+                            "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(fl / (med[1] * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)},
+               "fwd_bwd_edges_per_s": round(E / ((med[1] + med[2] + med[3]) * 1e-3), 1),
+               "reps": args.so2_reps}
+        del vec2, x2, w2, G2, D2, o2, gx2, gw2, ws2
+
     b = 4 if w.dtype == "f32" else 8
     fwd_bytes, bwd_bytes = algorithmic_bytes(plan, N, E, b)
     f_avg, b_avg = float(fwd_ms.mean()), float(bwd_ms.mean())
@@ -305,6 +357,7 @@ def main():
         "kernels_ms_cold": cold,
         "double_backward": dd,
         "upstream": up,
+        "so2": so2,
         "hbm": {"fwd_bwd_algorithmic_GBps": round(hbm_fwdbwd, 1), "frac_of_peak": round(hbm_fwdbwd / HBM_PEAK_GBS, 4),
                 "fwd_bytes": int(fwd_bytes), "bwd_bytes": int(bwd_bytes)},
         "roofline": roofline,

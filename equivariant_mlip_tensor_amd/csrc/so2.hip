@@ -103,24 +103,54 @@ struct So2Shape {
   }
 };
 
-// Rotates neighbour row `xr` of one edge into the tile (rotation on gather):
-// lane (c, h) writes x~[l][c][m] for m = h, h + NSPLIT, ...
+// Channel c of a node row: its (L+1)^2 components, (l, n) at l*l + l + n.
 template <int L, int C>
-__device__ __forceinline__ void rotate_in(const float* __restrict__ xr, const float* dle, float* te, int c, int h) {
+__device__ __forceinline__ void load_channel(const float* __restrict__ xr, int c, float (&xv)[(L + 1) * (L + 1)]) {
   using S = So2Shape<L, C>;
   so2_for<L + 1>([&](auto IL) {
     constexpr int l = IL, n2 = 2 * l + 1;
-    float xv[n2];
-    so2_for<n2>([&](auto N) { xv[N] = xr[S::xoff(l) + c * n2 + N]; });
+    so2_for<n2>([&](auto N) { xv[l * l + N] = xr[S::xoff(l) + c * n2 + N]; });
+  });
+}
+
+// Rotates one edge's channel into the tile (rotation on gather): lane (c, h)
+// writes x~[l][c][m] for m = h, h + NSPLIT, ...
+template <int L, int C>
+__device__ __forceinline__ void rotate_in(const float (&xv)[(L + 1) * (L + 1)], const float* dle, float* te, int c,
+                                          int h) {
+  using S = So2Shape<L, C>;
+  so2_for<L + 1>([&](auto IL) {
+    constexpr int l = IL, n2 = 2 * l + 1;
     so2_for<S::J(l)>([&](auto JJ) {
       const int m = h + S::NSPLIT * int(JJ);
       if (m < n2) {
         const float* dr = dle + S::doff(l) + m * n2;
         float s = 0.f;
-        so2_for<n2>([&](auto N) { s = fmaf(dr[N], xv[N], s); });
+        so2_for<n2>([&](auto N) { s = fmaf(dr[N], xv[l * l + N], s); });
         te[S::xoff(l) + c * n2 + m] = s;
       }
     });
+  });
+}
+
+// The Wigner rows of a chunk's edges into LDS (zeros past the chunk's end, so
+// those edges rotate to zero).  my_id: edge id of chunk edge (lane & 15)
+// (any value for lanes past ne); NTH threads share the copy.
+template <int L, int C, int NTH>
+__device__ __forceinline__ void load_wigner(int tid, int ne, int my_id, const float* __restrict__ Dm, float* dl) {
+  using S = So2Shape<L, C>;
+  constexpr int TOT = S::kEdges * S::ND, IT = (TOT + NTH - 1) / NTH;
+  float v[IT];
+  so2_for<IT>([&](auto I) {
+    const int q = tid + NTH * int(I);
+    const int e = q / S::ND, r = q - e * S::ND;
+    const int id = __shfl(my_id, e & 15);
+    v[I] = (q < TOT && e < ne) ? Dm[(int64_t)id * S::ND + r] : 0.f;
+  });
+  so2_for<IT>([&](auto I) {
+    const int q = tid + NTH * int(I);
+    const int e = q / S::ND, r = q - e * S::ND;
+    if (q < TOT) dl[e * S::NDP + r] = v[I];
   });
 }
 
@@ -143,14 +173,18 @@ __global__ __launch_bounds__(64) void k_so2_conv(const int32_t* __restrict__ row
     const int ne = min(S::kEdges, end - k0);
     const int my_n = lane < ne ? col[k0 + lane] : 0;
     // the chunk's Wigner rows (zeros past the row end, so those edges rotate to zero)
-    for (int q = lane; q < S::kEdges * S::ND; q += 64) {
-      const int e = q / S::ND, r = q - e * S::ND;
-      dl[e * S::NDP + r] = e < ne ? Dm[(int64_t)eid[k0 + e] * S::ND + r] : 0.f;
-    }
+    const int my_id = lane < ne ? eid[k0 + lane] : 0;
+    load_wigner<L, C, 64>(lane, ne, my_id, Dm, dl);
     __syncthreads();
-    for (int e = 0; e < S::kEdges; ++e) {  // wave-uniform
-      const int nb = __builtin_amdgcn_readlane(my_n, e);
-      rotate_in<L, C>(X + (int64_t)nb * S::DN, &dl[e * S::NDP], &tile[e * S::PAD], c, h);
+    for (int e0 = 0; e0 < S::kEdges; e0 += 4) {  // wave-uniform; four edges' loads issued together
+      float xv[4][S::NC];
+      so2_for<4>([&](auto I) {
+        load_channel<L, C>(X + (int64_t)__builtin_amdgcn_readlane(my_n, e0 + int(I)) * S::DN, c, xv[I]);
+      });
+      so2_for<4>([&](auto I) {
+        const int e = e0 + int(I);
+        rotate_in<L, C>(xv[I], &dl[e * S::NDP], &tile[e * S::PAD], c, h);
+      });
     }
     __syncthreads();
 
@@ -167,26 +201,57 @@ __global__ __launch_bounds__(64) void k_so2_conv(const int32_t* __restrict__ row
         yp[T] = v4f{0.f, 0.f, 0.f, 0.f};
         if constexpr (m > 0) ym[T] = v4f{0.f, 0.f, 0.f, 0.f};
       });
-#pragma unroll 2
-      for (int ks = 0; ks < KS; ++ks) {
-        const int kk = 4 * ks + kq;
-        const int l1 = m + kk / C, c1 = kk % C;
-        const float* t1 = &tile[er * S::PAD + C * l1 * l1 + c1 * (2 * l1 + 1) + l1];
-        const float ap = t1[m];
-        const float am = m > 0 ? t1[-m] : 0.f;
+      // K runs in groups of 16: in group g, lane quarter kq supplies
+      // k = 16 g + 4 kq + s at step s = 0..3 (a permutation of K, the same for
+      // both fragments), so a lane's four weights of a group for one n-tile
+      // are W[n][k..k+3], one 16-byte load (forward).  The next group's
+      // weights are in flight while this group's products run.
+      constexpr int NG = K / 16;
+      constexpr int NB = m > 0 ? NT : 1;
+      auto load_w = [&](const int g, v4f (&wa)[NT], v4f (&wb)[NB]) {
+        const int k = 16 * g + 4 * kq;
         so2_for<NT>([&](auto T) {
           const int n = int(T) * 16 + er;
-          const float wa = ADJ ? WA[kk * K + n] : WA[n * K + kk];
-          yp[T] = mfma(ap, wa, yp[T]);
-          if constexpr (m > 0) {
-            const float wb = ADJ ? WB[kk * K + n] : WB[n * K + kk];
-            // forward: y+ += A x+ - B x-, y- += B x+ + A x-
-            // adjoint: y+ += A^T g+ + B^T g-, y- += -B^T g+ + A^T g-
-            yp[T] = mfma(am, ADJ ? wb : -wb, yp[T]);
-            ym[T] = mfma(ap, ADJ ? -wb : wb, ym[T]);
-            ym[T] = mfma(am, wa, ym[T]);
+          if constexpr (!ADJ) {
+            wa[T] = *reinterpret_cast<const v4f*>(WA + n * K + k);
+            if constexpr (m > 0) wb[T] = *reinterpret_cast<const v4f*>(WB + n * K + k);
+          } else {  // the adjoint's B fragment is W^T: W[k + s][n], coalesced over n
+            wa[T] = v4f{WA[(k + 0) * K + n], WA[(k + 1) * K + n], WA[(k + 2) * K + n], WA[(k + 3) * K + n]};
+            if constexpr (m > 0)
+              wb[T] = v4f{WB[(k + 0) * K + n], WB[(k + 1) * K + n], WB[(k + 2) * K + n], WB[(k + 3) * K + n]};
           }
         });
+      };
+      auto run_group = [&](const int g, const v4f (&wa)[NT], const v4f (&wb)[NB]) {
+        so2_for<4>([&](auto SS) {
+          const int k = 16 * g + 4 * kq + int(SS);
+          const int l1 = m + k / C, c1 = k % C;
+          const float* t1 = &tile[er * S::PAD + C * l1 * l1 + c1 * (2 * l1 + 1) + l1];
+          const float ap = t1[m];
+          const float am = m > 0 ? t1[-m] : 0.f;
+          so2_for<NT>([&](auto T) {
+            const float a_w = wa[T][int(SS)];
+            yp[T] = mfma(ap, a_w, yp[T]);
+            if constexpr (m > 0) {
+              const float b_w = wb[T][int(SS)];
+              // forward: y+ += A x+ - B x-, y- += B x+ + A x-
+              // adjoint: y+ += A^T g+ + B^T g-, y- += -B^T g+ + A^T g-
+              yp[T] = mfma(am, ADJ ? b_w : -b_w, yp[T]);
+              ym[T] = mfma(ap, ADJ ? -b_w : b_w, ym[T]);
+              ym[T] = mfma(am, a_w, ym[T]);
+            }
+          });
+        });
+      };
+      v4f wa0[NT], wb0[NB], wa1[NT], wb1[NB];
+      load_w(0, wa0, wb0);
+#pragma unroll 1
+      for (int g = 0; g < NG; g += 2) {
+        if (g + 1 < NG) load_w(g + 1, wa1, wb1);
+        run_group(g, wa0, wb0);
+        if (g + 1 >= NG) break;
+        if (g + 2 < NG) load_w(g + 2, wa0, wb0);
+        run_group(g + 1, wa1, wb1);
       }
       // every read of this |m| is done: the results take the same places
       so2_for<NT>([&](auto T) {
@@ -264,25 +329,34 @@ __device__ __forceinline__ void wgrad_wave(int n_rows, int64_t s0, int64_t s1, c
     accB[I] = v4f{0.f, 0.f, 0.f, 0.f};
   });
 
+  // destination row of the block's current slot: one search, then a cursor
+  int cur = s0 < s1 ? slot_row(row_ptr, n_rows, (int)s0) : 0;
   for (int64_t k0 = s0; k0 < s1; k0 += S::kEdges) {
     const int ne = (int)min<int64_t>(S::kEdges, s1 - k0);
-    int my_s = 0, my_d = 0;
+    int my_s = 0, my_d = 0, my_id = 0;
     if (er < ne) {
       const int k = (int)(k0 + er);
       my_s = col[k];
-      my_d = slot_row(row_ptr, n_rows, k);
+      my_id = eid[k];
+      int r = cur;
+      while (row_ptr[r + 1] <= k) ++r;  // ends: row_ptr[n_rows] = n_slots > k
+      my_d = r;
     }
-    for (int q = threadIdx.x; q < S::kEdges * S::ND; q += 256) {
-      const int e = q / S::ND, r = q - e * S::ND;
-      dl[e * S::NDP + r] = e < ne ? Dm[(int64_t)eid[k0 + e] * S::ND + r] : 0.f;
-    }
+    cur = __builtin_amdgcn_readlane(my_d, ne - 1);
+    load_wigner<L, C, 256>(threadIdx.x, ne, my_id, Dm, dl);
     __syncthreads();
-    so2_for<4>([&](auto I) {
-      constexpr int e = WV + 4 * int(I);
-      const int sn = __builtin_amdgcn_readlane(my_s, e);
-      const int dn = __builtin_amdgcn_readlane(my_d, e);
-      rotate_in<L, C>(X + (int64_t)sn * S::DN, &dl[e * S::NDP], &xt[e * S::PAD], c, h);
-      rotate_in<L, C>(G + (int64_t)dn * S::DN, &dl[e * S::NDP], &gt[e * S::PAD], c, h);
+    so2_for<2>([&](auto P) {   // two edges at a time, x and grad_out rows loaded together
+      float xv[2][S::NC], gv[2][S::NC];
+      so2_for<2>([&](auto I) {
+        constexpr int e = WV + 8 * int(P) + 4 * int(I);
+        load_channel<L, C>(X + (int64_t)__builtin_amdgcn_readlane(my_s, e) * S::DN, c, xv[I]);
+        load_channel<L, C>(G + (int64_t)__builtin_amdgcn_readlane(my_d, e) * S::DN, c, gv[I]);
+      });
+      so2_for<2>([&](auto I) {
+        constexpr int e = WV + 8 * int(P) + 4 * int(I);
+        rotate_in<L, C>(xv[I], &dl[e * S::NDP], &xt[e * S::PAD], c, h);
+        rotate_in<L, C>(gv[I], &dl[e * S::NDP], &gt[e * S::PAD], c, h);
+      });
     });
     __syncthreads();
     so2_for<NMINE>([&](auto I) {
@@ -346,6 +420,7 @@ __global__ __launch_bounds__(256) void k_so2_wsum(int nb, int64_t nw, const floa
   const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (j >= nw) return;
   double s = 0.0;
+#pragma unroll 8
   for (int b = 0; b < nb; ++b) s += part[(int64_t)b * nw + j];
   gw[j] = (float)s;
 }
