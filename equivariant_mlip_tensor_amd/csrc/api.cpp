@@ -272,17 +272,19 @@ extern "C" tpconv_status tpconv_so2_forward(tpconv_graph_t hg, int lmax, int cha
   const Graph& g = *reinterpret_cast<const Graph*>(hg);
   if (g.n_nodes == 0) return TPCONV_OK;
   if (out == nullptr || weights == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL out or weights");
+  if (reinterpret_cast<uintptr_t>(weights) % 16 != 0)
+    return fail(TPCONV_E_INVALID_ARG, "SO(2) weights must be 16-byte aligned");
   if (g.n_edges > 0 && (x == nullptr || D == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL x or D");
   const hipError_t he = launch_so2_conv(lmax, channels, false, (int)g.n_nodes, g.dst_row, g.dst_col, g.dst_eid,
                                         g.dst_order, static_cast<const float*>(x), static_cast<const float*>(D),
-                                        static_cast<const float*>(weights), static_cast<float*>(out), stream);
+                                        static_cast<const float*>(weights), static_cast<float*>(out), nullptr, stream);
   if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("SO(2) forward launch: ") + hipGetErrorString(he));
   return TPCONV_OK;
 }
 
 extern "C" size_t tpconv_so2_workspace_bytes(int lmax, int channels, int64_t n_edges) {
   if (!so2_supported(lmax, channels) || n_edges < 0) return 0;
-  return (size_t)so2_wgrad_blocks(n_edges) * (size_t)so2_weight_numel(lmax, channels) * sizeof(float);
+  return (size_t)(so2_wgrad_blocks(n_edges) + 1) * (size_t)so2_weight_numel(lmax, channels) * sizeof(float);
 }
 
 extern "C" tpconv_status tpconv_so2_backward(tpconv_graph_t hg, int lmax, int channels, tpconv_dtype dtype,
@@ -294,25 +296,27 @@ extern "C" tpconv_status tpconv_so2_backward(tpconv_graph_t hg, int lmax, int ch
     return fail(TPCONV_E_UNSUPPORTED, "SO(2) convolution: lmax 1..3, channels 16 or 32, fp32");
   const Graph& g = *reinterpret_cast<const Graph*>(hg);
   if (grad_x == nullptr && grad_weights == nullptr) return TPCONV_OK;
-  if (grad_weights != nullptr) {
-    const size_t need = tpconv_so2_workspace_bytes(lmax, channels, g.n_edges);
-    if (workspace == nullptr || workspace_bytes < need)
-      return fail(TPCONV_E_WORKSPACE, "SO(2) backward: workspace smaller than tpconv_so2_workspace_bytes()");
-  }
+  const size_t need = tpconv_so2_workspace_bytes(lmax, channels, g.n_edges);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(TPCONV_E_WORKSPACE, "SO(2) backward: workspace smaller than tpconv_so2_workspace_bytes()");
+  float* const ws_maps = static_cast<float*>(workspace);  // the transposed maps, weight_numel floats
+  float* const ws_part = ws_maps + so2_weight_numel(lmax, channels);
   if (g.n_nodes > 0 && grad_out == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL grad_out");
   if (grad_x != nullptr && weights == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL weights");
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(TPCONV_E_INVALID_ARG, "SO(2) workspace must be 16-byte aligned");
   if (g.n_edges > 0 && (x == nullptr || D == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL x or D");
   if (grad_x != nullptr && g.n_nodes > 0) {
     const hipError_t he = launch_so2_conv(lmax, channels, true, (int)g.n_nodes, g.src_row, g.src_col, g.src_eid,
                                           g.src_order, static_cast<const float*>(grad_out),
                                           static_cast<const float*>(D), static_cast<const float*>(weights),
-                                          static_cast<float*>(grad_x), stream);
+                                          static_cast<float*>(grad_x), ws_maps, stream);
     if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("SO(2) backward launch: ") + hipGetErrorString(he));
   }
   if (grad_weights != nullptr) {
     const hipError_t he = launch_so2_wgrad(lmax, channels, (int)g.n_nodes, g.n_edges, g.dst_row, g.dst_col,
                                            g.dst_eid, static_cast<const float*>(x), static_cast<const float*>(grad_out),
-                                           static_cast<const float*>(D), static_cast<float*>(workspace),
+                                           static_cast<const float*>(D), ws_part,
                                            static_cast<float*>(grad_weights), stream);
     if (he != hipSuccess)
       return fail(TPCONV_E_HIP, std::string("SO(2) weight-gradient launch: ") + hipGetErrorString(he));

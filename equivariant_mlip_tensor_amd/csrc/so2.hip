@@ -204,22 +204,17 @@ __global__ __launch_bounds__(64) void k_so2_conv(const int32_t* __restrict__ row
       // K runs in groups of 16: in group g, lane quarter kq supplies
       // k = 16 g + 4 kq + s at step s = 0..3 (a permutation of K, the same for
       // both fragments), so a lane's four weights of a group for one n-tile
-      // are W[n][k..k+3], one 16-byte load (forward).  The next group's
-      // weights are in flight while this group's products run.
+      // are W[n][k..k+3], one 16-byte load.  The adjoint gets the maps
+      // transposed (k_so2_transpose) and reads them the same way.  The next
+      // group's weights are in flight while this group's products run.
       constexpr int NG = K / 16;
       constexpr int NB = m > 0 ? NT : 1;
       auto load_w = [&](const int g, v4f (&wa)[NT], v4f (&wb)[NB]) {
         const int k = 16 * g + 4 * kq;
         so2_for<NT>([&](auto T) {
           const int n = int(T) * 16 + er;
-          if constexpr (!ADJ) {
-            wa[T] = *reinterpret_cast<const v4f*>(WA + n * K + k);
-            if constexpr (m > 0) wb[T] = *reinterpret_cast<const v4f*>(WB + n * K + k);
-          } else {  // the adjoint's B fragment is W^T: W[k + s][n], coalesced over n
-            wa[T] = v4f{WA[(k + 0) * K + n], WA[(k + 1) * K + n], WA[(k + 2) * K + n], WA[(k + 3) * K + n]};
-            if constexpr (m > 0)
-              wb[T] = v4f{WB[(k + 0) * K + n], WB[(k + 1) * K + n], WB[(k + 2) * K + n], WB[(k + 3) * K + n]};
-          }
+          wa[T] = *reinterpret_cast<const v4f*>(WA + n * K + k);
+          if constexpr (m > 0) wb[T] = *reinterpret_cast<const v4f*>(WB + n * K + k);
         });
       };
       auto run_group = [&](const int g, const v4f (&wa)[NT], const v4f (&wb)[NB]) {
@@ -296,6 +291,27 @@ __global__ __launch_bounds__(64) void k_so2_conv(const int32_t* __restrict__ row
       if (n < n2) orow[S::xoff(l) + c * n2 + n] = acc[S::jbase(l) + JJ];
     });
   });
+}
+
+// Each map block of W transposed in place of itself: Wt[off + n K + k] =
+// W[off + k K + n] (the adjoint kernel's weights).
+template <int L, int C>
+__global__ __launch_bounds__(256) void k_so2_transpose(const float* __restrict__ W, float* __restrict__ Wt) {
+  using S = So2Shape<L, C>;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= S::NW) return;
+  int off = 0, K = 0;
+  for (int m = 0; m <= L; ++m) {
+    const int k = S::K(m), n = (m ? 2 : 1) * k * k;
+    if (idx < off + n) {
+      K = k;
+      if (idx >= off + k * k) off += k * k;  // B_m
+      break;
+    }
+    off += n;
+  }
+  const int r = idx - off, n = r / K, k = r - n * K;
+  Wt[idx] = W[off + k * K + n];
 }
 
 // row of CSR slot k: the last r with row_ptr[r] <= k
@@ -427,10 +443,16 @@ __global__ __launch_bounds__(256) void k_so2_wsum(int nb, int64_t nw, const floa
 
 template <int L, int C>
 hipError_t conv_LC(bool adjoint, int n_rows, const int32_t* row_ptr, const int32_t* col, const int32_t* eid,
-                   const int32_t* order, const float* X, const float* D, const float* W, float* out, hipStream_t s) {
-  if (adjoint)
+                   const int32_t* order, const float* X, const float* D, const float* W, float* out, float* Wt,
+                   hipStream_t s) {
+  using S = So2Shape<L, C>;
+  if (adjoint) {
+    hipLaunchKernelGGL((k_so2_transpose<L, C>), dim3((unsigned)((S::NW + 255) / 256)), dim3(256), 0, s, W, Wt);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_so2_conv<L, C, true>), dim3((unsigned)n_rows), dim3(64), 0, s, row_ptr, col, eid, order, X,
-                       D, W, out);
+                       D, Wt, out);
+  }
   else
     hipLaunchKernelGGL((k_so2_conv<L, C, false>), dim3((unsigned)n_rows), dim3(64), 0, s, row_ptr, col, eid, order,
                        X, D, W, out);
@@ -478,9 +500,9 @@ int so2_wgrad_blocks(int64_t n_edges) {
 
 hipError_t launch_so2_conv(int L, int C, bool adjoint, int n_rows, const int32_t* row_ptr, const int32_t* col,
                            const int32_t* eid, const int32_t* order, const float* X, const float* D, const float* W,
-                           float* out, hipStream_t s) {
+                           float* out, float* Wt, hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
-  SO2_CASES(conv_LC, adjoint, n_rows, row_ptr, col, eid, order, X, D, W, out, s)
+  SO2_CASES(conv_LC, adjoint, n_rows, row_ptr, col, eid, order, X, D, W, out, Wt, s)
 }
 
 hipError_t launch_so2_wgrad(int L, int C, int n_rows, int64_t n_edges, const int32_t* row_ptr, const int32_t* col,

@@ -392,7 +392,7 @@ def tpconv_so2_backward(graph: Graph, lmax: int, channels: int, x, D, weights, g
     if grad_weights is not None:
         _need(grad_weights, (nw,), f, "grad_weights")
     ws_bytes = 0
-    if grad_weights is not None:
+    if grad_x is not None or grad_weights is not None:
         if workspace is None:
             workspace = torch.empty(max(tpconv_so2_workspace_bytes(lmax, channels, E), 256), dtype=torch.uint8,
                                     device=dev)

@@ -286,30 +286,32 @@ tpconv_status tpconv_so2_rotations(int lmax, tpconv_dtype dtype, int64_t n_edges
  * over the graph's destination-sorted rows: one wavefront per row; per chunk
  * of 16 edges the neighbour rows are rotated into an LDS tile, the per-|m|
  * maps run on the matrix cores, and the inverse rotations are summed in
- * registers.  x, D, weights, out: device fp32.  Errors: TPCONV_E_INVALID_ARG
- * (NULL handle or pointer), TPCONV_E_UNSUPPORTED, TPCONV_E_HIP. */
+ * registers.  x, D, weights, out: device fp32; weights 16-byte aligned.
+ * Errors: TPCONV_E_INVALID_ARG (NULL handle or pointer, misaligned weights),
+ * TPCONV_E_UNSUPPORTED, TPCONV_E_HIP. */
 tpconv_status tpconv_so2_forward(tpconv_graph_t g, int lmax, int channels, tpconv_dtype dtype, const void* x,
                                  const void* D, const void* weights, void* out, hipStream_t stream);
 
-/* Workspace bytes tpconv_so2_backward needs for n_edges edges (the partial
- * sums of the map gradients, one row of weight_numel floats per block of at
- * most 512 blocks). */
+/* Workspace bytes tpconv_so2_backward needs for n_edges edges: the
+ * transposed maps (weight_numel floats) and the partial sums of the map
+ * gradients (weight_numel floats per block of edges, at most 512 blocks). */
 size_t tpconv_so2_workspace_bytes(int lmax, int channels, int64_t n_edges);
 
 /* tpconv_so2_backward: gradients of <grad_out, out>:
  *   grad_x[j]     = sum_{e: src = j} D_e^T SO2^T(D_e grad_out[dst e])
- *                   (the forward's kernel with the adjoint maps, over the
- *                   source-sorted rows);
+ *                   (the forward's kernel with the adjoint maps, transposed
+ *                   once into the workspace, over the source-sorted rows);
  *   grad_weights  = sum over edges of g~ x~^T per block (g~, x~ the rotated
  *                   grad_out[dst] and x[src]):  A_0: g~_0 X_0^T;
  *                   A_m: g~_+m X_+m^T + g~_-m X_-m^T;
  *                   B_m: g~_-m X_+m^T - g~_+m X_-m^T;
  *                   partial sums per block of edges in `workspace`
  *                   (tpconv_so2_workspace_bytes), then added in block order.
- * Outputs are overwritten; pass NULL to skip one (grad_weights NULL needs no
- * workspace).  Deterministic (no atomics).  Errors: TPCONV_E_INVALID_ARG,
- * TPCONV_E_WORKSPACE (workspace too small), TPCONV_E_UNSUPPORTED,
- * TPCONV_E_HIP. */
+ * Outputs are overwritten; pass NULL to skip one.  The workspace (device,
+ * 16-byte aligned, at least tpconv_so2_workspace_bytes) is the caller's and
+ * holds nothing between calls.  Deterministic (no atomics).  Errors:
+ * TPCONV_E_INVALID_ARG, TPCONV_E_WORKSPACE (workspace too small),
+ * TPCONV_E_UNSUPPORTED, TPCONV_E_HIP. */
 tpconv_status tpconv_so2_backward(tpconv_graph_t g, int lmax, int channels, tpconv_dtype dtype, const void* x,
                                   const void* D, const void* weights, const void* grad_out, void* grad_x,
                                   void* grad_weights, void* workspace, size_t workspace_bytes, hipStream_t stream);

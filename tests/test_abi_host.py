@@ -149,7 +149,7 @@ def test_so2_sizes_and_errors_need_no_gpu(tp):
         for C in (16, 32):
             assert tp.tpconv_so2_weight_numel(L, C) == weight_numel(L, C)
             nb = min(512, max(1, -(-100000 // 64)))
-            assert tp.tpconv_so2_workspace_bytes(L, C, 100000) == nb * weight_numel(L, C) * 4
+            assert tp.tpconv_so2_workspace_bytes(L, C, 100000) == (nb + 1) * weight_numel(L, C) * 4
     assert tp.tpconv_so2_weight_numel(3, 32) == 45056
     for L, C in ((0, 16), (4, 16), (3, 8), (3, 64), (2, 24)):
         assert tp.tpconv_so2_weight_numel(L, C) == 0
