@@ -154,15 +154,107 @@ __device__ __forceinline__ void load_wigner(int tid, int ne, int my_id, const fl
   });
 }
 
-template <int L, int C, bool ADJ>
-__global__ __launch_bounds__(64) void k_so2_conv(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
-                                                 const int32_t* __restrict__ eid, const int32_t* __restrict__ order,
-                                                 const float* __restrict__ X, const float* __restrict__ Dm,
-                                                 const float* __restrict__ W, float* __restrict__ out) {
+// The per-|m| maps of one chunk on the matrix cores (v_mfma_f32_16x16x4f32:
+// M = the 16 edges, N = output (l, c), K = input (l, c)) for the n-tiles
+// T = WV, WV + 2, ... of each |m|; the block's other wavefront takes the rest.
+// Per |m|: products, a barrier (both wavefronts have read X_+-m), then the
+// results overwrite the tile at the same (+-m) places.
+template <int L, int C, bool ADJ, int WV>
+__device__ __forceinline__ void so2_maps(float* tile, const float* __restrict__ W, const int lane) {
   using S = So2Shape<L, C>;
+  const int er = lane & 15;  // A fragment: edge row; B fragment and result: column
+  const int kq = lane >> 4;  // A/B fragment: k within the step; result: rows 4 kq .. 4 kq + 3
+  so2_for<L + 1>([&](auto IM) {
+    constexpr int m = IM;
+    constexpr int K = S::K(m), NT = K / 16, NTW = (NT - WV + 1) / 2;
+    constexpr int NA = NTW > 0 ? NTW : 1, NB = (m > 0 && NTW > 0) ? NTW : 1;
+    const float* WA = W + S::woffA(m);
+    const float* WB = W + (m > 0 ? S::woffB(m) : 0);
+    v4f yp[NA], ym[NB];
+    if constexpr (NTW > 0) {
+      so2_for<NTW>([&](auto I) {
+        yp[I] = v4f{0.f, 0.f, 0.f, 0.f};
+        if constexpr (m > 0) ym[I] = v4f{0.f, 0.f, 0.f, 0.f};
+      });
+      // K runs in groups of 16: in group g, lane quarter kq supplies
+      // k = 16 g + 4 kq + s at step s = 0..3 (a permutation of K, the same for
+      // both fragments), so a lane's four weights of a group for one n-tile
+      // are W[n][k..k+3], one 16-byte load.  The adjoint gets the maps
+      // transposed (k_so2_transpose) and reads them the same way.  The next
+      // group's weights are in flight while this group's products run.
+      constexpr int NG = K / 16;
+      auto load_w = [&](const int g, v4f (&wa)[NA], v4f (&wb)[NB]) {
+        const int k = 16 * g + 4 * kq;
+        so2_for<NTW>([&](auto I) {
+          const int n = (WV + 2 * int(I)) * 16 + er;
+          wa[I] = *reinterpret_cast<const v4f*>(WA + n * K + k);
+          if constexpr (m > 0) wb[I] = *reinterpret_cast<const v4f*>(WB + n * K + k);
+        });
+      };
+      auto run_group = [&](const int g, const v4f (&wa)[NA], const v4f (&wb)[NB]) {
+        so2_for<4>([&](auto SS) {
+          const int k = 16 * g + 4 * kq + int(SS);
+          const int l1 = m + k / C, c1 = k % C;
+          const float* t1 = &tile[er * S::PAD + C * l1 * l1 + c1 * (2 * l1 + 1) + l1];
+          const float ap = t1[m];
+          const float am = m > 0 ? t1[-m] : 0.f;
+          so2_for<NTW>([&](auto I) {
+            const float a_w = wa[I][int(SS)];
+            yp[I] = mfma(ap, a_w, yp[I]);
+            if constexpr (m > 0) {
+              const float b_w = wb[I][int(SS)];
+              // forward: y+ += A x+ - B x-, y- += B x+ + A x-
+              // adjoint: y+ += A^T g+ + B^T g-, y- += -B^T g+ + A^T g-
+              yp[I] = mfma(am, ADJ ? b_w : -b_w, yp[I]);
+              ym[I] = mfma(ap, ADJ ? -b_w : b_w, ym[I]);
+              ym[I] = mfma(am, a_w, ym[I]);
+            }
+          });
+        });
+      };
+      v4f wa0[NA], wb0[NB], wa1[NA], wb1[NB];
+      load_w(0, wa0, wb0);
+#pragma unroll 1
+      for (int g = 0; g < NG; g += 2) {
+        if (g + 1 < NG) load_w(g + 1, wa1, wb1);
+        run_group(g, wa0, wb0);
+        if (g + 1 >= NG) break;
+        if (g + 2 < NG) load_w(g + 2, wa0, wb0);
+        run_group(g + 1, wa1, wb1);
+      }
+    }
+    __syncthreads();
+    if constexpr (NTW > 0) {
+      so2_for<NTW>([&](auto I) {
+        const int n = (WV + 2 * int(I)) * 16 + er;
+        const int l3 = m + n / C, c3 = n % C;
+        float* t3 = &tile[C * l3 * l3 + c3 * (2 * l3 + 1) + l3];
+        so2_for<4>([&](auto R) {
+          const int e = 4 * kq + int(R);
+          t3[e * S::PAD + m] = yp[I][int(R)];
+          if constexpr (m > 0) t3[e * S::PAD - m] = ym[I][int(R)];
+        });
+      });
+    }
+  });
+}
+
+// One CSR row per block of two wavefronts sharing the chunk's LDS tile (two
+// rows' blocks fit a SIMD pair's LDS, so each SIMD holds two wavefronts).
+// Wavefront w rotates and inverse-rotates edges 8w .. 8w + 7 of each chunk
+// and runs half of the n-tiles; the two row sums meet in LDS at the end.
+template <int L, int C, bool ADJ>
+__global__ __launch_bounds__(128, 2) void k_so2_conv(const int32_t* __restrict__ row_ptr,
+                                                     const int32_t* __restrict__ col, const int32_t* __restrict__ eid,
+                                                     const int32_t* __restrict__ order, const float* __restrict__ X,
+                                                     const float* __restrict__ Dm, const float* __restrict__ W,
+                                                     float* __restrict__ out) {
+  using S = So2Shape<L, C>;
+  static_assert(S::NACC * 64 <= S::kEdges * S::PAD, "row-sum exchange must fit the tile");
   __shared__ float tile[S::kEdges * S::PAD];
   __shared__ float dl[S::kEdges * S::NDP];
-  const int lane = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int c = lane % C, h = lane / C;
   const int row = order[blockIdx.x];
   const int beg = row_ptr[row], end = row_ptr[row + 1];
@@ -174,9 +266,9 @@ __global__ __launch_bounds__(64) void k_so2_conv(const int32_t* __restrict__ row
     const int my_n = lane < ne ? col[k0 + lane] : 0;
     // the chunk's Wigner rows (zeros past the row end, so those edges rotate to zero)
     const int my_id = lane < ne ? eid[k0 + lane] : 0;
-    load_wigner<L, C, 64>(lane, ne, my_id, Dm, dl);
+    load_wigner<L, C, 128>(threadIdx.x, ne, my_id, Dm, dl);
     __syncthreads();
-    for (int e0 = 0; e0 < S::kEdges; e0 += 4) {  // wave-uniform; four edges' loads issued together
+    for (int e0 = 8 * wave; e0 < 8 * wave + 8; e0 += 4) {  // wave-uniform; four edges' loads issued together
       float xv[4][S::NC];
       so2_for<4>([&](auto I) {
         load_channel<L, C>(X + (int64_t)__builtin_amdgcn_readlane(my_n, e0 + int(I)) * S::DN, c, xv[I]);
@@ -187,83 +279,15 @@ __global__ __launch_bounds__(64) void k_so2_conv(const int32_t* __restrict__ row
       });
     }
     __syncthreads();
-
-    // the per-|m| maps on the matrix cores
-    const int er = lane & 15;  // A fragment: edge row; B fragment and result: column
-    const int kq = lane >> 4;  // A/B fragment: k within the step; result: rows 4 kq .. 4 kq + 3
-    so2_for<L + 1>([&](auto IM) {
-      constexpr int m = IM;
-      constexpr int K = S::K(m), NT = K / 16, KS = K / 4;
-      const float* WA = W + S::woffA(m);
-      const float* WB = W + (m > 0 ? S::woffB(m) : 0);
-      v4f yp[NT], ym[m > 0 ? NT : 1];
-      so2_for<NT>([&](auto T) {
-        yp[T] = v4f{0.f, 0.f, 0.f, 0.f};
-        if constexpr (m > 0) ym[T] = v4f{0.f, 0.f, 0.f, 0.f};
-      });
-      // K runs in groups of 16: in group g, lane quarter kq supplies
-      // k = 16 g + 4 kq + s at step s = 0..3 (a permutation of K, the same for
-      // both fragments), so a lane's four weights of a group for one n-tile
-      // are W[n][k..k+3], one 16-byte load.  The adjoint gets the maps
-      // transposed (k_so2_transpose) and reads them the same way.  The next
-      // group's weights are in flight while this group's products run.
-      constexpr int NG = K / 16;
-      constexpr int NB = m > 0 ? NT : 1;
-      auto load_w = [&](const int g, v4f (&wa)[NT], v4f (&wb)[NB]) {
-        const int k = 16 * g + 4 * kq;
-        so2_for<NT>([&](auto T) {
-          const int n = int(T) * 16 + er;
-          wa[T] = *reinterpret_cast<const v4f*>(WA + n * K + k);
-          if constexpr (m > 0) wb[T] = *reinterpret_cast<const v4f*>(WB + n * K + k);
-        });
-      };
-      auto run_group = [&](const int g, const v4f (&wa)[NT], const v4f (&wb)[NB]) {
-        so2_for<4>([&](auto SS) {
-          const int k = 16 * g + 4 * kq + int(SS);
-          const int l1 = m + k / C, c1 = k % C;
-          const float* t1 = &tile[er * S::PAD + C * l1 * l1 + c1 * (2 * l1 + 1) + l1];
-          const float ap = t1[m];
-          const float am = m > 0 ? t1[-m] : 0.f;
-          so2_for<NT>([&](auto T) {
-            const float a_w = wa[T][int(SS)];
-            yp[T] = mfma(ap, a_w, yp[T]);
-            if constexpr (m > 0) {
-              const float b_w = wb[T][int(SS)];
-              // forward: y+ += A x+ - B x-, y- += B x+ + A x-
-              // adjoint: y+ += A^T g+ + B^T g-, y- += -B^T g+ + A^T g-
-              yp[T] = mfma(am, ADJ ? b_w : -b_w, yp[T]);
-              ym[T] = mfma(ap, ADJ ? -b_w : b_w, ym[T]);
-              ym[T] = mfma(am, a_w, ym[T]);
-            }
-          });
-        });
-      };
-      v4f wa0[NT], wb0[NB], wa1[NT], wb1[NB];
-      load_w(0, wa0, wb0);
-#pragma unroll 1
-      for (int g = 0; g < NG; g += 2) {
-        if (g + 1 < NG) load_w(g + 1, wa1, wb1);
-        run_group(g, wa0, wb0);
-        if (g + 1 >= NG) break;
-        if (g + 2 < NG) load_w(g + 2, wa0, wb0);
-        run_group(g + 1, wa1, wb1);
-      }
-      // every read of this |m| is done: the results take the same places
-      so2_for<NT>([&](auto T) {
-        const int n = int(T) * 16 + er;
-        const int l3 = m + n / C, c3 = n % C;
-        float* t3 = &tile[C * l3 * l3 + c3 * (2 * l3 + 1) + l3];
-        so2_for<4>([&](auto R) {
-          const int e = 4 * kq + int(R);
-          t3[e * S::PAD + m] = yp[T][int(R)];
-          if constexpr (m > 0) t3[e * S::PAD - m] = ym[T][int(R)];
-        });
-      });
-    });
+    if (wave == 0)
+      so2_maps<L, C, ADJ, 0>(tile, W, lane);
+    else
+      so2_maps<L, C, ADJ, 1>(tile, W, lane);
     __syncthreads();
 
     // inverse rotation on reduction: lane (c, h) sums components n = h, h + NSPLIT, ...
-    for (int e = 0; e < ne; ++e) {  // wave-uniform
+    const int e_end = min(ne, 8 * wave + 8);
+    for (int e = 8 * wave; e < e_end; ++e) {  // wave-uniform
       const float* te = &tile[e * S::PAD];
       const float* dle = &dl[e * S::NDP];
       so2_for<L + 1>([&](auto IL) {
@@ -273,9 +297,9 @@ __global__ __launch_bounds__(64) void k_so2_conv(const int32_t* __restrict__ row
         so2_for<S::J(l)>([&](auto JJ) {
           const int n = h + S::NSPLIT * int(JJ);
           if (n < n2) {
-            float s = acc[S::jbase(l) + JJ];
-            so2_for<n2>([&](auto M) { s = fmaf(dle[S::doff(l) + M * n2 + n], yv[M], s); });
-            acc[S::jbase(l) + JJ] = s;
+            float sum = acc[S::jbase(l) + JJ];
+            so2_for<n2>([&](auto M) { sum = fmaf(dle[S::doff(l) + M * n2 + n], yv[M], sum); });
+            acc[S::jbase(l) + JJ] = sum;
           }
         });
       });
@@ -283,14 +307,20 @@ __global__ __launch_bounds__(64) void k_so2_conv(const int32_t* __restrict__ row
     __syncthreads();
   }
 
-  float* orow = out + (int64_t)row * S::DN;
-  so2_for<L + 1>([&](auto IL) {
-    constexpr int l = IL, n2 = 2 * l + 1;
-    so2_for<S::J(l)>([&](auto JJ) {
-      const int n = h + S::NSPLIT * int(JJ);
-      if (n < n2) orow[S::xoff(l) + c * n2 + n] = acc[S::jbase(l) + JJ];
+  // the two wavefronts' row sums (wavefront 1's through the tile), written once
+  if (wave == 1) so2_for<S::NACC>([&](auto I) { tile[int(I) * 64 + lane] = acc[I]; });
+  __syncthreads();
+  if (wave == 0) {
+    so2_for<S::NACC>([&](auto I) { acc[I] += tile[int(I) * 64 + lane]; });
+    float* orow = out + (int64_t)row * S::DN;
+    so2_for<L + 1>([&](auto IL) {
+      constexpr int l = IL, n2 = 2 * l + 1;
+      so2_for<S::J(l)>([&](auto JJ) {
+        const int n = h + S::NSPLIT * int(JJ);
+        if (n < n2) orow[S::xoff(l) + c * n2 + n] = acc[S::jbase(l) + JJ];
+      });
     });
-  });
+  }
 }
 
 // Each map block of W transposed in place of itself: Wt[off + n K + k] =
@@ -450,11 +480,11 @@ hipError_t conv_LC(bool adjoint, int n_rows, const int32_t* row_ptr, const int32
     hipLaunchKernelGGL((k_so2_transpose<L, C>), dim3((unsigned)((S::NW + 255) / 256)), dim3(256), 0, s, W, Wt);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_so2_conv<L, C, true>), dim3((unsigned)n_rows), dim3(64), 0, s, row_ptr, col, eid, order, X,
-                       D, Wt, out);
+    hipLaunchKernelGGL((k_so2_conv<L, C, true>), dim3((unsigned)n_rows), dim3(128), 0, s, row_ptr, col, eid, order,
+                       X, D, Wt, out);
   }
   else
-    hipLaunchKernelGGL((k_so2_conv<L, C, false>), dim3((unsigned)n_rows), dim3(64), 0, s, row_ptr, col, eid, order,
+    hipLaunchKernelGGL((k_so2_conv<L, C, false>), dim3((unsigned)n_rows), dim3(128), 0, s, row_ptr, col, eid, order,
                        X, D, W, out);
   return hipGetLastError();
 }
