@@ -63,7 +63,11 @@ struct So2Shape {
   static constexpr int NC = (L + 1) * (L + 1);
   static constexpr int DN = C * NC;                        // node row, floats
   static constexpr int NSPLIT = 64 / C;                    // lanes per channel
-  static constexpr int PAD = (DN + 31) / 32 * 32 + 2;      // LDS tile edge stride
+  // LDS tile edge strides: 2 mod 32 in the convolution (fragment rows are
+  // edges), 16 mod 32 in the map gradient (fragment rows are (l, c), and the
+  // two quarter-waves of a half-wave read edges e and e + 1: disjoint banks)
+  static constexpr int PAD = (DN + 31) / 32 * 32 + 2;
+  static constexpr int PADW = (DN + 31) / 32 * 32 + 16;
   static constexpr int ND = (L + 1) * (2 * L + 1) * (2 * L + 3) / 3;  // Wigner floats per edge
   static constexpr int NDP = ND + 1;                       // LDS stride of a Wigner row
   static constexpr int kEdges = 16;
@@ -154,6 +158,16 @@ __device__ __forceinline__ void load_wigner(int tid, int ne, int my_id, const fl
   });
 }
 
+// K index supplied by lane quarter kq at step s of 16-wide unit g.  Any
+// permutation of K serves (it applies to both fragments); this one keeps a
+// lane's four steps contiguous (one 16-byte weight load).  (Placing the two
+// quarters of a half-wave 16 channels apart removes the remaining 2-way LDS
+// bank conflicts of the A fragments but costs registers: measured slower.)
+template <int C>
+__device__ __forceinline__ int so2_k(int g, int kq, int s) {
+  return 16 * g + 4 * kq + s;
+}
+
 // The per-|m| maps of one chunk on the matrix cores (v_mfma_f32_16x16x4f32:
 // M = the 16 edges, N = output (l, c), K = input (l, c)) for the n-tiles
 // T = WV, WV + 2, ... of each |m|; the block's other wavefront takes the rest.
@@ -176,15 +190,13 @@ __device__ __forceinline__ void so2_maps(float* tile, const float* __restrict__ 
         yp[I] = v4f{0.f, 0.f, 0.f, 0.f};
         if constexpr (m > 0) ym[I] = v4f{0.f, 0.f, 0.f, 0.f};
       });
-      // K runs in groups of 16: in group g, lane quarter kq supplies
-      // k = 16 g + 4 kq + s at step s = 0..3 (a permutation of K, the same for
-      // both fragments), so a lane's four weights of a group for one n-tile
-      // are W[n][k..k+3], one 16-byte load.  The adjoint gets the maps
-      // transposed (k_so2_transpose) and reads them the same way.  The next
-      // group's weights are in flight while this group's products run.
+      // K runs in units of 16 (so2_k): a lane's four weights of a unit for
+      // one n-tile are W[n][k..k+3], one 16-byte load.  The adjoint gets the
+      // maps transposed (k_so2_transpose) and reads them the same way.  The
+      // next unit's weights are in flight while this unit's products run.
       constexpr int NG = K / 16;
       auto load_w = [&](const int g, v4f (&wa)[NA], v4f (&wb)[NB]) {
-        const int k = 16 * g + 4 * kq;
+        const int k = so2_k<C>(g, kq, 0);
         so2_for<NTW>([&](auto I) {
           const int n = (WV + 2 * int(I)) * 16 + er;
           wa[I] = *reinterpret_cast<const v4f*>(WA + n * K + k);
@@ -193,7 +205,7 @@ __device__ __forceinline__ void so2_maps(float* tile, const float* __restrict__ 
       };
       auto run_group = [&](const int g, const v4f (&wa)[NA], const v4f (&wb)[NB]) {
         so2_for<4>([&](auto SS) {
-          const int k = 16 * g + 4 * kq + int(SS);
+          const int k = so2_k<C>(g, kq, int(SS));
           const int l1 = m + k / C, c1 = k % C;
           const float* t1 = &tile[er * S::PAD + C * l1 * l1 + c1 * (2 * l1 + 1) + l1];
           const float ap = t1[m];
@@ -400,8 +412,8 @@ __device__ __forceinline__ void wgrad_wave(int n_rows, int64_t s0, int64_t s1, c
       });
       so2_for<2>([&](auto I) {
         constexpr int e = WV + 8 * int(P) + 4 * int(I);
-        rotate_in<L, C>(xv[I], &dl[e * S::NDP], &xt[e * S::PAD], c, h);
-        rotate_in<L, C>(gv[I], &dl[e * S::NDP], &gt[e * S::PAD], c, h);
+        rotate_in<L, C>(xv[I], &dl[e * S::NDP], &xt[e * S::PADW], c, h);
+        rotate_in<L, C>(gv[I], &dl[e * S::NDP], &gt[e * S::PADW], c, h);
       });
     });
     __syncthreads();
@@ -414,10 +426,10 @@ __device__ __forceinline__ void wgrad_wave(int n_rows, int64_t s0, int64_t s1, c
       const float* xi = &xt[C * li * li + ci * (2 * li + 1) + li];
       so2_for<4>([&](auto KS) {
         const int e = 4 * int(KS) + kq;  // K index of both fragments: the edge
-        const float gp = go[e * S::PAD + m], xp = xi[e * S::PAD + m];
+        const float gp = go[e * S::PADW + m], xp = xi[e * S::PADW + m];
         accA[I] = mfma(gp, xp, accA[I]);
         if constexpr (m > 0) {
-          const float gm = go[e * S::PAD - m], xm = xi[e * S::PAD - m];
+          const float gm = go[e * S::PADW - m], xm = xi[e * S::PADW - m];
           accA[I] = mfma(gm, xm, accA[I]);   // dA += g+ x+^T + g- x-^T
           accB[I] = mfma(gm, xp, accB[I]);   // dB += g- x+^T - g+ x-^T
           accB[I] = mfma(-gp, xm, accB[I]);
@@ -447,8 +459,8 @@ __global__ __launch_bounds__(256) void k_so2_wgrad(int n_rows, int64_t n_slots, 
                                                    const float* __restrict__ X, const float* __restrict__ G,
                                                    const float* __restrict__ Dm, float* __restrict__ part) {
   using S = So2Shape<L, C>;
-  __shared__ float xt[S::kEdges * S::PAD];
-  __shared__ float gt[S::kEdges * S::PAD];
+  __shared__ float xt[S::kEdges * S::PADW];
+  __shared__ float gt[S::kEdges * S::PADW];
   __shared__ float dl[S::kEdges * S::NDP];
   const int64_t s0 = (int64_t)blockIdx.x * per_block;
   const int64_t s1 = min(n_slots, s0 + per_block);
