@@ -105,6 +105,34 @@ struct So2Shape {
     }
     return Job{-1, 0, 0};
   }
+  // the map-gradient block's wavefronts and their jobs: longest first, each
+  // to the least-loaded wavefront (a job costs 4 products per k-step when
+  // m > 0, one when m = 0)
+  static constexpr int kWaves = 8;
+  struct Assign {
+    int nmine[kWaves];
+    int list[kWaves][njobs()];
+  };
+  static constexpr Assign assign() {
+    Assign a{};
+    int load[kWaves] = {};
+    for (int pass = 0; pass < 2; ++pass)
+      for (int j = 0; j < njobs(); ++j) {
+        const bool heavy = job(j).m > 0;
+        if (heavy != (pass == 0)) continue;
+        int best = 0;
+        for (int w = 1; w < kWaves; ++w)
+          if (load[w] < load[best]) best = w;
+        load[best] += heavy ? 4 : 1;
+        a.list[best][a.nmine[best]++] = j;
+      }
+    return a;
+  }
+};
+
+template <int L, int C>
+struct So2Jobs {
+  static constexpr typename So2Shape<L, C>::Assign value = So2Shape<L, C>::assign();
 };
 
 // Channel c of a node row: its (L+1)^2 components, (l, n) at l*l + l + n.
@@ -376,12 +404,11 @@ __device__ __forceinline__ void wgrad_wave(int n_rows, int64_t s0, int64_t s1, c
                                            const float* __restrict__ Dm, float* __restrict__ part, float* xt,
                                            float* gt, float* dl) {
   using S = So2Shape<L, C>;
-  constexpr int NJ = S::njobs();
-  constexpr int NMINE = (NJ - WV + 3) / 4;  // jobs j = WV, WV + 4, ...
+  constexpr int NMINE = So2Jobs<L, C>::value.nmine[WV];
   const int lane = threadIdx.x & 63;
   const int c = lane % C, h = lane / C;
   const int er = lane & 15, kq = lane >> 4;
-  v4f accA[NMINE], accB[NMINE];
+  v4f accA[NMINE > 0 ? NMINE : 1], accB[NMINE > 0 ? NMINE : 1];  // a wavefront may own no tile
   so2_for<NMINE>([&](auto I) {
     accA[I] = v4f{0.f, 0.f, 0.f, 0.f};
     accB[I] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -401,24 +428,24 @@ __device__ __forceinline__ void wgrad_wave(int n_rows, int64_t s0, int64_t s1, c
       my_d = r;
     }
     cur = __builtin_amdgcn_readlane(my_d, ne - 1);
-    load_wigner<L, C, 256>(threadIdx.x, ne, my_id, Dm, dl);
+    load_wigner<L, C, 64 * S::kWaves>(threadIdx.x, ne, my_id, Dm, dl);
     __syncthreads();
-    so2_for<2>([&](auto P) {   // two edges at a time, x and grad_out rows loaded together
+    {  // this wavefront's two edges, x and grad_out rows loaded together
       float xv[2][S::NC], gv[2][S::NC];
       so2_for<2>([&](auto I) {
-        constexpr int e = WV + 8 * int(P) + 4 * int(I);
+        constexpr int e = WV + S::kWaves * int(I);
         load_channel<L, C>(X + (int64_t)__builtin_amdgcn_readlane(my_s, e) * S::DN, c, xv[I]);
         load_channel<L, C>(G + (int64_t)__builtin_amdgcn_readlane(my_d, e) * S::DN, c, gv[I]);
       });
       so2_for<2>([&](auto I) {
-        constexpr int e = WV + 8 * int(P) + 4 * int(I);
+        constexpr int e = WV + S::kWaves * int(I);
         rotate_in<L, C>(xv[I], &dl[e * S::NDP], &xt[e * S::PADW], c, h);
         rotate_in<L, C>(gv[I], &dl[e * S::NDP], &gt[e * S::PADW], c, h);
       });
-    });
+    }
     __syncthreads();
     so2_for<NMINE>([&](auto I) {
-      constexpr typename S::Job jb = S::job(WV + 4 * int(I));
+      constexpr typename S::Job jb = S::job(So2Jobs<L, C>::value.list[WV][int(I)]);
       constexpr int m = jb.m;
       const int o = jb.ot * 16 + er, i = jb.it * 16 + er;
       const int lo = m + o / C, co = o % C, li = m + i / C, ci = i % C;
@@ -441,7 +468,7 @@ __device__ __forceinline__ void wgrad_wave(int n_rows, int64_t s0, int64_t s1, c
 
   float* pb = part + (int64_t)blockIdx.x * S::NW;
   so2_for<NMINE>([&](auto I) {
-    constexpr typename S::Job jb = S::job(WV + 4 * int(I));
+    constexpr typename S::Job jb = S::job(So2Jobs<L, C>::value.list[WV][int(I)]);
     constexpr int m = jb.m, K = S::K(m);
     const int i = jb.it * 16 + er;
     so2_for<4>([&](auto R) {
@@ -453,7 +480,7 @@ __device__ __forceinline__ void wgrad_wave(int n_rows, int64_t s0, int64_t s1, c
 }
 
 template <int L, int C>
-__global__ __launch_bounds__(256) void k_so2_wgrad(int n_rows, int64_t n_slots, int64_t per_block,
+__global__ __launch_bounds__(512) void k_so2_wgrad(int n_rows, int64_t n_slots, int64_t per_block,
                                                    const int32_t* __restrict__ row_ptr,
                                                    const int32_t* __restrict__ col, const int32_t* __restrict__ eid,
                                                    const float* __restrict__ X, const float* __restrict__ G,
@@ -468,7 +495,11 @@ __global__ __launch_bounds__(256) void k_so2_wgrad(int n_rows, int64_t n_slots, 
     case 0: wgrad_wave<L, C, 0>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, part, xt, gt, dl); break;
     case 1: wgrad_wave<L, C, 1>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, part, xt, gt, dl); break;
     case 2: wgrad_wave<L, C, 2>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, part, xt, gt, dl); break;
-    default: wgrad_wave<L, C, 3>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, part, xt, gt, dl); break;
+    case 3: wgrad_wave<L, C, 3>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, part, xt, gt, dl); break;
+    case 4: wgrad_wave<L, C, 4>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, part, xt, gt, dl); break;
+    case 5: wgrad_wave<L, C, 5>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, part, xt, gt, dl); break;
+    case 6: wgrad_wave<L, C, 6>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, part, xt, gt, dl); break;
+    default: wgrad_wave<L, C, 7>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, part, xt, gt, dl); break;
   }
 }
 
@@ -507,7 +538,8 @@ hipError_t wgrad_LC(int n_rows, int64_t n_slots, int nb, const int32_t* row_ptr,
                     hipStream_t s) {
   using S = So2Shape<L, C>;
   const int64_t per_block = (n_slots + nb - 1) / nb;
-  hipLaunchKernelGGL((k_so2_wgrad<L, C>), dim3((unsigned)nb), dim3(256), 0, s, n_rows, n_slots, per_block, row_ptr,
+  hipLaunchKernelGGL((k_so2_wgrad<L, C>), dim3((unsigned)nb), dim3(64 * S::kWaves), 0, s, n_rows, n_slots, per_block,
+                     row_ptr,
                      col, eid, X, G, D, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
