@@ -14,18 +14,18 @@
 // over all edges of outer products of the rotated grad_out and x.
 //
 // Kernels (one wavefront = 64 lanes):
-//  * k_so2_conv<L, C, ADJ>: one wavefront per CSR row, edges in chunks of 16.
-//    Per chunk: the 16 Wigner rows go to LDS; each neighbour row is rotated
-//    in registers (lane = channel c and a share of the m) and written to an
-//    LDS tile [edge][node layout]; per |m| the maps run on the matrix cores
-//    (v_mfma_f32_16x16x4f32: M = the 16 edges, N = output (l, c), K = input
-//    (l, c)), their A and B fragments shared by the four products of a
-//    (+m, -m) pair, weights streamed from L2; the results overwrite the
-//    tile at the same (+-m) places; the inverse rotation then adds each
-//    edge's message into per-lane row sums.  Nothing per edge reaches HBM.
-//    The tile's edge stride is 2 mod 32 floats, which keeps the fragment
-//    reads (16 edges x 4 consecutive k) free of LDS bank conflicts.
-//  * k_so2_wgrad<L, C>: four wavefronts share one LDS copy of the rotated x
+//  * k_so2_conv<L, C, ADJ>: one CSR row per block of two wavefronts, edges
+//    in chunks of 16.  Per chunk: the 16 Wigner rows go to LDS; each
+//    wavefront rotates 8 neighbour rows in registers (lane = channel c and a
+//    share of the m) into an LDS tile [edge][node layout]; per |m| the maps
+//    run on the matrix cores (v_mfma_f32_16x16x4f32: M = the 16 edges,
+//    N = output (l, c), K = input (l, c)), the wavefronts splitting the
+//    n-tiles, A and B fragments shared by the four products of a (+m, -m)
+//    pair, weights streamed from L2 a unit ahead; after a barrier the
+//    results overwrite the tile at the same (+-m) places; the inverse
+//    rotation then adds each edge's message into per-lane row sums, which
+//    the two wavefronts combine once per row.  Nothing per edge reaches HBM.
+//  * k_so2_wgrad<L, C>: eight wavefronts share one LDS copy of the rotated x
 //    and grad_out of 16 edges; each wavefront owns a fixed set of 16 x 16
 //    output tiles of the map gradients (compile-time list, its accumulators
 //    stay in registers over all of the block's edges) and runs them on the

@@ -283,10 +283,10 @@ tpconv_status tpconv_so2_rotations(int lmax, tpconv_dtype dtype, int64_t n_edges
                                    hipStream_t stream);
 
 /* tpconv_so2_forward: out (overwritten, zero rows for nodes without in-edges)
- * over the graph's destination-sorted rows: one wavefront per row; per chunk
- * of 16 edges the neighbour rows are rotated into an LDS tile, the per-|m|
- * maps run on the matrix cores, and the inverse rotations are summed in
- * registers.  x, D, weights, out: device fp32; weights 16-byte aligned.
+ * over the graph's destination-sorted rows: one block of two wavefronts per
+ * row; per chunk of 16 edges the neighbour rows are rotated into an LDS
+ * tile, the per-|m| maps run on the matrix cores, and the inverse rotations
+ * are summed in registers.  x, D, weights, out: device fp32; weights 16-byte aligned.
  * Errors: TPCONV_E_INVALID_ARG (NULL handle or pointer, misaligned weights),
  * TPCONV_E_UNSUPPORTED, TPCONV_E_HIP. */
 tpconv_status tpconv_so2_forward(tpconv_graph_t g, int lmax, int channels, tpconv_dtype dtype, const void* x,

@@ -207,3 +207,29 @@ def test_workload(tp, name):
     log(f"[so2] workload {name} errors {errs}")
     for k, v in errs.items():
         assert v <= TOL, (name, k, v)
+
+
+def test_error_paths(tp):
+    """Refusals the host side reports before launching anything."""
+    import torch
+    lmax, C, n = 2, 16, 10
+    d = C * 9
+    rng = np.random.default_rng(340)
+    src, dst = rng.integers(0, n, 50).astype(np.int32), rng.integers(0, n, 50).astype(np.int32)
+    g = tp.tpconv_graph_create(n, dev(src), dev(dst))
+    D = tp.tpconv_so2_rotations(lmax, dev(rng.standard_normal((50, 3)).astype(np.float32)))
+    x = dev(rng.standard_normal((n, d)).astype(np.float32))
+    nw = weight_numel(lmax, C)
+    wbuf = torch.zeros(nw + 4, dtype=torch.float32, device="cuda")
+    with pytest.raises(tp.TPConvError, match="aligned") as ei:
+        tp.tpconv_so2_forward(g, lmax, C, x, D, wbuf[1:nw + 1])          # 4-byte offset
+    assert ei.value.name == "TPCONV_E_INVALID_ARG"
+    need = tp.tpconv_so2_workspace_bytes(lmax, C, 50)
+    small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(tp.TPConvError) as ei:
+        tp.tpconv_so2_backward(g, lmax, C, x, D, wbuf[:nw], x, workspace=small)
+    assert ei.value.name == "TPCONV_E_WORKSPACE"
+    with pytest.raises(tp.TPConvError) as ei:
+        tp.tpconv_so2_forward(g, 3, 24, x, D, wbuf[:nw])
+    assert ei.value.name == "TPCONV_E_UNSUPPORTED"
+    torch.cuda.synchronize()
