@@ -230,3 +230,31 @@ def so2_backward(lmax, C, x, D, weights, G, src, dst, n_nodes):
             blk = gp.T @ xp + gm.T @ xm if name == "A" else gm.T @ xp - gp.T @ xm
         gw[off:off + K * K] = blk.reshape(-1)
     return grad_x, gw
+
+
+def so2_double_backward(lmax, C, x, D, weights, G, ggx, ggw, src, dst, n_nodes):
+    """Gradients of L2 = <ggx, grad_x> + <ggw, grad_w>, where (grad_x, grad_w)
+    = so2_backward(x, weights, G), with respect to x, the weights and G (the
+    frames D held fixed).  The convolution f(x; w) is linear in x and in w
+    separately, and grad_x = f(.; w)^T G, grad_w = the map gradient of (x, G),
+    so
+        L2 = <f(ggx; w), G> + <f(x; ggw), G>
+    and
+        grad_G = f(ggx; w) + f(x; ggw)
+        grad_x = f(.; ggw)^T G         (the backward's grad_x with ggw for w)
+        grad_w = map gradient of (ggx, G)  (the backward's grad_w with ggx for x).
+    ggx or ggw may be None (zero).  Returns (grad_x, grad_w, grad_G)."""
+    x = np.asarray(x, dtype=np.float64)
+    G = np.asarray(G, dtype=np.float64)
+    d = C * (lmax + 1) ** 2
+    nw = weight_numel(lmax, C)
+    grad_G = np.zeros((n_nodes, d))
+    grad_x = np.zeros((n_nodes, d))
+    grad_w = np.zeros(nw)
+    if ggx is not None:
+        grad_G += so2_forward(lmax, C, ggx, D, weights, src, dst, n_nodes)
+        grad_w = so2_backward(lmax, C, ggx, D, weights, G, src, dst, n_nodes)[1]
+    if ggw is not None:
+        grad_G += so2_forward(lmax, C, x, D, ggw, src, dst, n_nodes)
+        grad_x = so2_backward(lmax, C, x, D, ggw, G, src, dst, n_nodes)[0]
+    return grad_x, grad_w, grad_G

@@ -13,7 +13,10 @@ itself:
     oracle when A_m, B_m are built from the real CG coefficients at m2 = 0,
     which is what a tensor product with Y(r_hat) becomes in the edge frame;
   * the backward: the operator is linear in x and in the weights, so
-    <G, f(dx)> = <grad_x, dx> and <G, f(x; dw)> = <grad_w, dw> exactly.
+    <G, f(dx)> = <grad_x, dx> and <G, f(x; dw)> = <grad_w, dw> exactly;
+  * the double backward: central differences of <ggx, grad_x> + <ggw, grad_w>
+    through the pinned backward (exact: linear in each input separately),
+    the Euler identity in G, and the split by cotangent.
 """
 
 from math import gamma
@@ -286,3 +289,43 @@ def test_isolated_nodes_and_no_edges():
     assert out.shape == (n, 18) and np.all(out == 0)
     gx, gw = so2_backward(lmax, C, x, np.zeros((0, 35)), w, x, e, e, n)
     assert np.all(gx == 0) and np.all(gw == 0)
+
+
+@pytest.mark.parametrize("lmax,C", [(1, 2), (2, 2), (3, 2)])
+def test_double_backward_by_differences(lmax, C):
+    """L2 = <ggx, grad_x> + <ggw, grad_w> is linear in each of x, w, G
+    separately, so a central difference along any direction is exact up to
+    rounding: it pins every output of so2_double_backward against the
+    (separately pinned) backward."""
+    from oracle.so2 import so2_double_backward
+    rng = np.random.default_rng(110 + lmax)
+    n, E = 7, 45
+    src, dst, vec = make_graph(rng, n, E)
+    D = edge_wigner(lmax, vec)
+    d, nw = C * (lmax + 1) ** 2, weight_numel(lmax, C)
+    x, G = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    w = rng.standard_normal(nw)
+    ggx, ggw = rng.standard_normal((n, d)), rng.standard_normal(nw)
+
+    def L2(x_, w_, G_):
+        gx, gw = so2_backward(lmax, C, x_, D, w_, G_, src, dst, n)
+        return np.vdot(ggx, gx) + np.vdot(ggw, gw)
+
+    gx2, gw2, gG2 = so2_double_backward(lmax, C, x, D, w, G, ggx, ggw, src, dst, n)
+    h = 0.5
+    for _ in range(2):
+        dx, dw, dG = rng.standard_normal((n, d)), rng.standard_normal(nw), rng.standard_normal((n, d))
+        fx = (L2(x + h * dx, w, G) - L2(x - h * dx, w, G)) / (2 * h)
+        fw = (L2(x, w + h * dw, G) - L2(x, w - h * dw, G)) / (2 * h)
+        fG = (L2(x, w, G + h * dG) - L2(x, w, G - h * dG)) / (2 * h)
+        assert np.vdot(gx2, dx) == pytest.approx(fx, rel=1e-10, abs=1e-9)
+        assert np.vdot(gw2, dw) == pytest.approx(fw, rel=1e-10, abs=1e-9)
+        assert np.vdot(gG2, dG) == pytest.approx(fG, rel=1e-10, abs=1e-9)
+    # Euler identity: L2 is homogeneous of degree 1 in G
+    assert np.vdot(gG2, G) == pytest.approx(L2(x, w, G), rel=1e-10)
+    # one cotangent at a time
+    gx_a, gw_a, gG_a = so2_double_backward(lmax, C, x, D, w, G, ggx, None, src, dst, n)
+    assert np.all(gx_a == 0) and np.abs(gw_a).max() > 0
+    gx_b, gw_b, gG_b = so2_double_backward(lmax, C, x, D, w, G, None, ggw, src, dst, n)
+    assert np.all(gw_b == 0) and np.abs(gx_b).max() > 0
+    np.testing.assert_allclose(gG_a + gG_b, gG2, atol=1e-12)
