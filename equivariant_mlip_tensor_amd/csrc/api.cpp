@@ -275,7 +275,7 @@ extern "C" tpconv_status tpconv_so2_forward(tpconv_graph_t hg, int lmax, int cha
   if (reinterpret_cast<uintptr_t>(weights) % 16 != 0)
     return fail(TPCONV_E_INVALID_ARG, "SO(2) weights must be 16-byte aligned");
   if (g.n_edges > 0 && (x == nullptr || D == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL x or D");
-  const hipError_t he = launch_so2_conv(lmax, channels, false, (int)g.n_nodes, g.dst_row, g.dst_col, g.dst_eid,
+  const hipError_t he = launch_so2_conv(lmax, channels, false, false, (int)g.n_nodes, g.dst_row, g.dst_col, g.dst_eid,
                                         g.dst_order, static_cast<const float*>(x), static_cast<const float*>(D),
                                         static_cast<const float*>(weights), static_cast<float*>(out), nullptr, stream);
   if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("SO(2) forward launch: ") + hipGetErrorString(he));
@@ -307,7 +307,7 @@ extern "C" tpconv_status tpconv_so2_backward(tpconv_graph_t hg, int lmax, int ch
     return fail(TPCONV_E_INVALID_ARG, "SO(2) workspace must be 16-byte aligned");
   if (g.n_edges > 0 && (x == nullptr || D == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL x or D");
   if (grad_x != nullptr && g.n_nodes > 0) {
-    const hipError_t he = launch_so2_conv(lmax, channels, true, (int)g.n_nodes, g.src_row, g.src_col, g.src_eid,
+    const hipError_t he = launch_so2_conv(lmax, channels, true, false, (int)g.n_nodes, g.src_row, g.src_col, g.src_eid,
                                           g.src_order, static_cast<const float*>(grad_out),
                                           static_cast<const float*>(D), static_cast<const float*>(weights),
                                           static_cast<float*>(grad_x), ws_maps, stream);
@@ -322,5 +322,81 @@ extern "C" tpconv_status tpconv_so2_backward(tpconv_graph_t hg, int lmax, int ch
       return fail(TPCONV_E_HIP, std::string("SO(2) weight-gradient launch: ") + hipGetErrorString(he));
   }
   return TPCONV_OK;
+}
+
+extern "C" tpconv_status tpconv_so2_double_backward(tpconv_graph_t hg, int lmax, int channels, tpconv_dtype dtype,
+                                                    const void* x, const void* D, const void* weights,
+                                                    const void* grad_out, const void* ggx, const void* ggw,
+                                                    void* grad_x, void* grad_weights, void* grad_G, void* workspace,
+                                                    size_t workspace_bytes, hipStream_t stream) {
+  if (hg == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL graph");
+  if (!so2_supported(lmax, channels) || dtype != TPCONV_F32)
+    return fail(TPCONV_E_UNSUPPORTED, "SO(2) convolution: lmax 1..3, channels 16 or 32, fp32");
+  const Graph& g = *reinterpret_cast<const Graph*>(hg);
+  if (grad_x == nullptr && grad_weights == nullptr && grad_G == nullptr) return TPCONV_OK;
+  if (grad_x != nullptr || grad_weights != nullptr) {
+    const size_t need = tpconv_so2_workspace_bytes(lmax, channels, g.n_edges);
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(TPCONV_E_WORKSPACE, "SO(2) double backward: workspace smaller than tpconv_so2_workspace_bytes()");
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+      return fail(TPCONV_E_INVALID_ARG, "SO(2) workspace must be 16-byte aligned");
+  }
+  const bool need_x = g.n_nodes > 0 && (ggw != nullptr || ggx != nullptr);
+  if (need_x && (x == nullptr || D == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL x or D");
+  if (g.n_nodes > 0 && (grad_x != nullptr || grad_weights != nullptr) && grad_out == nullptr)
+    return fail(TPCONV_E_INVALID_ARG, "NULL grad_out");
+  if (grad_G != nullptr && ggx != nullptr && weights == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL weights");
+  if ((weights != nullptr && reinterpret_cast<uintptr_t>(weights) % 16 != 0) ||
+      (ggw != nullptr && reinterpret_cast<uintptr_t>(ggw) % 16 != 0))
+    return fail(TPCONV_E_INVALID_ARG, "SO(2) weights and ggw must be 16-byte aligned");
+  const int64_t nw = so2_weight_numel(lmax, channels);
+  const int64_t nd = g.n_nodes * (int64_t)channels * (lmax + 1) * (lmax + 1);
+  float* const ws_maps = static_cast<float*>(workspace);
+  float* const ws_part = ws_maps == nullptr ? nullptr : ws_maps + nw;
+  const float* fx = static_cast<const float*>(x);
+  const float* fD = static_cast<const float*>(D);
+  const float* fG = static_cast<const float*>(grad_out);
+  auto check = [](hipError_t he, const char* what) -> tpconv_status {
+    if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string(what) + hipGetErrorString(he));
+    return TPCONV_OK;
+  };
+  tpconv_status st = TPCONV_OK;
+  // grad_G = f(ggx; w) + f(x; ggw)
+  if (grad_G != nullptr) {
+    float* out = static_cast<float*>(grad_G);
+    if (ggx != nullptr)
+      st = check(launch_so2_conv(lmax, channels, false, false, (int)g.n_nodes, g.dst_row, g.dst_col, g.dst_eid,
+                                 g.dst_order, static_cast<const float*>(ggx), fD, static_cast<const float*>(weights),
+                                 out, nullptr, stream),
+                 "SO(2) double backward launch: ");
+    if (st == TPCONV_OK && ggw != nullptr)
+      st = check(launch_so2_conv(lmax, channels, false, ggx != nullptr, (int)g.n_nodes, g.dst_row, g.dst_col,
+                                 g.dst_eid, g.dst_order, fx, fD, static_cast<const float*>(ggw), out, nullptr,
+                                 stream),
+                 "SO(2) double backward launch: ");
+    if (st == TPCONV_OK && ggx == nullptr && ggw == nullptr)
+      st = check(launch_so2_fill_zero(nd, out, stream), "SO(2) double backward fill: ");
+    if (st != TPCONV_OK) return st;
+  }
+  // grad_x = f(.; ggw)^T grad_out
+  if (grad_x != nullptr) {
+    float* out = static_cast<float*>(grad_x);
+    st = ggw != nullptr
+             ? check(launch_so2_conv(lmax, channels, true, false, (int)g.n_nodes, g.src_row, g.src_col, g.src_eid,
+                                     g.src_order, fG, fD, static_cast<const float*>(ggw), out, ws_maps, stream),
+                     "SO(2) double backward launch: ")
+             : check(launch_so2_fill_zero(nd, out, stream), "SO(2) double backward fill: ");
+    if (st != TPCONV_OK) return st;
+  }
+  // grad_w = map gradient of (ggx, grad_out)
+  if (grad_weights != nullptr) {
+    float* out = static_cast<float*>(grad_weights);
+    st = ggx != nullptr
+             ? check(launch_so2_wgrad(lmax, channels, (int)g.n_nodes, g.n_edges, g.dst_row, g.dst_col, g.dst_eid,
+                                      static_cast<const float*>(ggx), fG, fD, ws_part, out, stream),
+                     "SO(2) double backward launch: ")
+             : check(launch_so2_fill_zero(nw, out, stream), "SO(2) double backward fill: ");
+  }
+  return st;
 }
 

@@ -288,7 +288,7 @@ __global__ __launch_bounds__(128, 2) void k_so2_conv(const int32_t* __restrict__
                                                      const int32_t* __restrict__ col, const int32_t* __restrict__ eid,
                                                      const int32_t* __restrict__ order, const float* __restrict__ X,
                                                      const float* __restrict__ Dm, const float* __restrict__ W,
-                                                     float* __restrict__ out) {
+                                                     float* __restrict__ out, const int accumulate) {
   using S = So2Shape<L, C>;
   static_assert(S::NACC * 64 <= S::kEdges * S::PAD, "row-sum exchange must fit the tile");
   __shared__ float tile[S::kEdges * S::PAD];
@@ -357,10 +357,18 @@ __global__ __launch_bounds__(128, 2) void k_so2_conv(const int32_t* __restrict__
       constexpr int l = IL, n2 = 2 * l + 1;
       so2_for<S::J(l)>([&](auto JJ) {
         const int n = h + S::NSPLIT * int(JJ);
-        if (n < n2) orow[S::xoff(l) + c * n2 + n] = acc[S::jbase(l) + JJ];
+        if (n < n2) {
+          float* o = &orow[S::xoff(l) + c * n2 + n];
+          *o = accumulate ? *o + acc[S::jbase(l) + JJ] : acc[S::jbase(l) + JJ];  // the row's only writer
+        }
       });
     });
   }
+}
+
+__global__ __launch_bounds__(256) void k_so2_fill_zero(int64_t n, float* __restrict__ p) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.f;
 }
 
 // Each map block of W transposed in place of itself: Wt[off + n K + k] =
@@ -515,20 +523,20 @@ __global__ __launch_bounds__(256) void k_so2_wsum(int nb, int64_t nw, const floa
 }
 
 template <int L, int C>
-hipError_t conv_LC(bool adjoint, int n_rows, const int32_t* row_ptr, const int32_t* col, const int32_t* eid,
-                   const int32_t* order, const float* X, const float* D, const float* W, float* out, float* Wt,
-                   hipStream_t s) {
+hipError_t conv_LC(bool adjoint, bool accumulate, int n_rows, const int32_t* row_ptr, const int32_t* col,
+                   const int32_t* eid, const int32_t* order, const float* X, const float* D, const float* W,
+                   float* out, float* Wt, hipStream_t s) {
   using S = So2Shape<L, C>;
   if (adjoint) {
     hipLaunchKernelGGL((k_so2_transpose<L, C>), dim3((unsigned)((S::NW + 255) / 256)), dim3(256), 0, s, W, Wt);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_so2_conv<L, C, true>), dim3((unsigned)n_rows), dim3(128), 0, s, row_ptr, col, eid, order,
-                       X, D, Wt, out);
+                       X, D, Wt, out, (int)accumulate);
   }
   else
     hipLaunchKernelGGL((k_so2_conv<L, C, false>), dim3((unsigned)n_rows), dim3(128), 0, s, row_ptr, col, eid, order,
-                       X, D, W, out);
+                       X, D, W, out, (int)accumulate);
   return hipGetLastError();
 }
 
@@ -572,11 +580,11 @@ int so2_wgrad_blocks(int64_t n_edges) {
     default: return hipErrorInvalidValue;                   \
   }
 
-hipError_t launch_so2_conv(int L, int C, bool adjoint, int n_rows, const int32_t* row_ptr, const int32_t* col,
-                           const int32_t* eid, const int32_t* order, const float* X, const float* D, const float* W,
-                           float* out, float* Wt, hipStream_t s) {
+hipError_t launch_so2_conv(int L, int C, bool adjoint, bool accumulate, int n_rows, const int32_t* row_ptr,
+                           const int32_t* col, const int32_t* eid, const int32_t* order, const float* X,
+                           const float* D, const float* W, float* out, float* Wt, hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
-  SO2_CASES(conv_LC, adjoint, n_rows, row_ptr, col, eid, order, X, D, W, out, Wt, s)
+  SO2_CASES(conv_LC, adjoint, accumulate, n_rows, row_ptr, col, eid, order, X, D, W, out, Wt, s)
 }
 
 hipError_t launch_so2_wgrad(int L, int C, int n_rows, int64_t n_edges, const int32_t* row_ptr, const int32_t* col,
@@ -584,6 +592,12 @@ hipError_t launch_so2_wgrad(int L, int C, int n_rows, int64_t n_edges, const int
                             float* grad_w, hipStream_t s) {
   const int nb = so2_wgrad_blocks(n_edges);
   SO2_CASES(wgrad_LC, n_rows, n_edges, nb, row_ptr, col, eid, X, G, D, part, grad_w, s)
+}
+
+hipError_t launch_so2_fill_zero(int64_t n, float* p, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_so2_fill_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n, p);
+  return hipGetLastError();
 }
 
 }  // namespace tpconv

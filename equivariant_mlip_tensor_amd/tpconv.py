@@ -30,7 +30,7 @@ EXPORTS = ("tpconv_plan", "tpconv_plan_query", "tpconv_plan_paths", "tpconv_plan
            "tpconv_graph_workspace_bytes", "tpconv_graph_create", "tpconv_graph_export", "tpconv_graph_destroy",
            "tpconv_forward", "tpconv_backward", "tpconv_double_backward", "tpconv_sh", "tpconv_sh_backward",
            "tpconv_positions_backward", "tpconv_so2_weight_numel", "tpconv_so2_rotations", "tpconv_so2_forward",
-           "tpconv_so2_workspace_bytes", "tpconv_so2_backward", "tpconv_last_error")
+           "tpconv_so2_workspace_bytes", "tpconv_so2_backward", "tpconv_so2_double_backward", "tpconv_last_error")
 
 
 class TPConvError(RuntimeError):
@@ -75,6 +75,7 @@ def _load():
         "tpconv_so2_workspace_bytes": (sz, [ctypes.c_int, ctypes.c_int, i64]),
         "tpconv_so2_backward": (i32, [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, sz,
                                       vp]),
+        "tpconv_so2_double_backward": (i32, [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int] + [vp] * 10 + [sz, vp]),
         "tpconv_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -401,3 +402,43 @@ def tpconv_so2_backward(graph: Graph, lmax: int, channels: int, x, D, weights, g
                                     _ptr(grad_out), _ptr(grad_x), _ptr(grad_weights), _ptr(workspace), ws_bytes,
                                     _stream_handle(stream)))
     return grad_x, grad_weights
+
+
+def tpconv_so2_double_backward(graph: Graph, lmax: int, channels: int, x, D, weights, grad_out, ggx=None, ggw=None,
+                               grad_x=None, grad_weights=None, grad_G=None, workspace=None,
+                               need=(True, True, True), stream=None):
+    """Gradients of <ggx, grad_x> + <ggw, grad_w> (the backward's outputs) with
+    respect to x, the maps and grad_out; ggx / ggw may be None (zero).
+    Returns (grad_x, grad_weights, grad_G); an output is None when `need`
+    turns it off."""
+    N, E = graph.n_nodes, graph.n_edges
+    dn, nd, nw = _so2_sizes(lmax, channels)
+    f = torch.float32
+    _need(x, (N, dn), f, "x")
+    _need(D, (E, nd), f, "D")
+    _need(weights, (nw,), f, "weights")
+    _need(grad_out, (N, dn), f, "grad_out")
+    if ggx is not None:
+        _need(ggx, (N, dn), f, "ggx")
+    if ggw is not None:
+        _need(ggw, (nw,), f, "ggw")
+    dev = x.device
+    outs = [grad_x, grad_weights, grad_G]
+    shapes = ((N, dn), (nw,), (N, dn))
+    for k in range(3):
+        if need[k] and outs[k] is None:
+            outs[k] = torch.empty(shapes[k], dtype=f, device=dev)
+        if outs[k] is not None:
+            _need(outs[k], shapes[k], f, ("grad_x", "grad_weights", "grad_G")[k])
+    ws_bytes = 0
+    if outs[0] is not None or outs[1] is not None:
+        if workspace is None:
+            workspace = torch.empty(max(tpconv_so2_workspace_bytes(lmax, channels, E), 256), dtype=torch.uint8,
+                                    device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.tpconv_so2_double_backward(graph.handle, int(lmax), int(channels), F32, _ptr(x), _ptr(D),
+                                           _ptr(weights), _ptr(grad_out), _ptr(ggx), _ptr(ggw), _ptr(outs[0]),
+                                           _ptr(outs[1]), _ptr(outs[2]), _ptr(workspace), ws_bytes,
+                                           _stream_handle(stream)))
+    return tuple(outs)
+

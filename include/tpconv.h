@@ -316,6 +316,26 @@ tpconv_status tpconv_so2_backward(tpconv_graph_t g, int lmax, int channels, tpco
                                   const void* D, const void* weights, const void* grad_out, void* grad_x,
                                   void* grad_weights, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* tpconv_so2_double_backward: the backward of tpconv_so2_backward, with the
+ * frames D held fixed (the TrimSO(2) abstract counts the double backward
+ * among the operator's passes).  With (grad_x, grad_w) = the backward of
+ * (x, weights, grad_out) and their cotangents ggx [N][C (L+1)^2] and
+ * ggw [weight_numel] (either may be NULL = zero), it returns the gradients
+ * of L2 = <ggx, grad_x> + <ggw, grad_w>.  The convolution f(x; w) is linear
+ * in x and in w separately, so
+ *   grad_G       = f(ggx; w) + f(x; ggw)          [N][C (L+1)^2]
+ *   grad_x       = f(.; ggw)^T grad_out           (the backward's grad_x, ggw for w)
+ *   grad_weights = map gradient of (ggx, grad_out) (the backward's grad_w, ggx for x)
+ * each from the same kernels as the forward and backward (the second
+ * forward adds into grad_G; each row has one writer).  Outputs are
+ * overwritten; pass NULL to skip one.  Workspace and alignment as
+ * tpconv_so2_backward (needed when grad_x or grad_weights is asked for; ggw
+ * 16-byte aligned).  Errors as tpconv_so2_backward. */
+tpconv_status tpconv_so2_double_backward(tpconv_graph_t g, int lmax, int channels, tpconv_dtype dtype, const void* x,
+                                         const void* D, const void* weights, const void* grad_out, const void* ggx,
+                                         const void* ggw, void* grad_x, void* grad_weights, void* grad_G,
+                                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* tpconv_last_error(void);
 

@@ -36,7 +36,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(tp):
     declared = header_functions()
-    assert len(declared) == 21
+    assert len(declared) == 22
     assert sorted(tp.EXPORTS) == declared
     lib = ctypes.CDLL(LIB)
     for name in declared:
@@ -162,6 +162,7 @@ def test_so2_sizes_and_errors_need_no_gpu(tp):
     assert lib.tpconv_so2_rotations(2, 0, 0, None, None, None) == 0       # nothing to do
     assert lib.tpconv_so2_forward(None, 2, 16, 0, None, None, None, None, None) == 1
     assert lib.tpconv_so2_backward(None, 2, 16, 0, *([None] * 7), 0, None) == 1
+    assert lib.tpconv_so2_double_backward(None, 2, 16, 0, *([None] * 10), 0, None) == 1
     # unsupported shapes and dtypes are refused before the graph is read
     fake = ctypes.c_void_p(ctypes.addressof(buf))
     assert lib.tpconv_so2_forward(fake, 4, 16, 0, None, None, None, None, None) == 3

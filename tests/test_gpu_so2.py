@@ -19,7 +19,7 @@ import numpy as np
 import pytest
 
 import workloads
-from oracle.so2 import edge_wigner, so2_backward, so2_forward, weight_numel
+from oracle.so2 import edge_wigner, so2_backward, so2_double_backward, so2_forward, weight_numel
 
 pytestmark = pytest.mark.gpu
 
@@ -233,3 +233,71 @@ def test_error_paths(tp):
         tp.tpconv_so2_forward(g, 3, 24, x, D, wbuf[:nw])
     assert ei.value.name == "TPCONV_E_UNSUPPORTED"
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("case", ["both", "ggx only", "ggw only", "none"])
+@pytest.mark.parametrize("lmax,C", [(1, 16), (3, 32)])
+def test_double_backward_small(tp, case, lmax, C):
+    import torch
+    rng = np.random.default_rng(350 + lmax)
+    n = 30
+    dst = np.concatenate([np.full(19, 2), rng.integers(0, n, 150)])
+    src = rng.integers(0, n, len(dst))
+    keep = (src != 5) & (dst != 5)
+    src, dst = src[keep].astype(np.int32), dst[keep].astype(np.int32)
+    vec = rng.standard_normal((len(src), 3))
+    d, nw = C * (lmax + 1) ** 2, weight_numel(lmax, C)
+    f32 = lambda a: np.asarray(a, np.float32)  # noqa: E731
+    x, G = f32(rng.standard_normal((n, d))), f32(rng.standard_normal((n, d)))
+    w = f32(rng.standard_normal(nw) / np.sqrt(2 * C * (lmax + 1)))
+    ggx = f32(rng.standard_normal((n, d))) if case in ("both", "ggx only") else None
+    ggw = f32(rng.standard_normal(nw) / np.sqrt(2 * C * (lmax + 1))) if case in ("both", "ggw only") else None
+    g = tp.tpconv_graph_create(n, dev(src), dev(dst))
+    D = tp.tpconv_so2_rotations(lmax, dev(f32(vec)))
+    outs = tp.tpconv_so2_double_backward(g, lmax, C, dev(x), D, dev(w), dev(G),
+                                         None if ggx is None else dev(ggx), None if ggw is None else dev(ggw))
+    torch.cuda.synchronize()
+    ref = so2_double_backward(lmax, C, x, D.cpu().numpy().astype(np.float64), w, G, ggx, ggw, src, dst, n)
+    errs = {k: rel_err(o.cpu().numpy(), r) for k, o, r in zip(("grad_x", "grad_w", "grad_G"), outs, ref)}
+    log(f"[so2] double backward {case} l<={lmax} C={C} errors {errs}")
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)
+    if case == "none":
+        assert all(np.all(o.cpu().numpy() == 0) for o in outs)
+
+
+@pytest.mark.parametrize("name", ["c1k", "c4k"])
+def test_double_backward_workload(tp, name):
+    """Full-size outputs from the GPU against the oracle on sampled rows
+    (grad_G, grad_x) and the map gradient against the backward's, which it
+    equals with ggx for x (both GPU, bitwise: same kernels, same order)."""
+    import torch
+    w = workloads.WORKLOADS[name]
+    lmax, C = workloads.SO2_SHAPES[name]
+    nw = weight_numel(lmax, C)
+    inp = workloads.make_so2_inputs(w, nw)
+    src, dst, vec, n = inp["src"], inp["dst"], inp["vec"], inp["n_nodes"]
+    rng = np.random.default_rng(360)
+    ggx = rng.standard_normal(inp["x"].shape).astype(np.float32)
+    ggw = (rng.standard_normal(nw) / np.sqrt(2 * C * (lmax + 1))).astype(np.float32)
+    g = tp.tpconv_graph_create(n, dev(src), dev(dst))
+    D = tp.tpconv_so2_rotations(lmax, dev(vec.astype(np.float32)))
+    xd, wd, Gd = dev(inp["x"]), dev(inp["weights"]), dev(inp["G"])
+    gx, gw, gG = tp.tpconv_so2_double_backward(g, lmax, C, xd, D, wd, Gd, dev(ggx), dev(ggw))
+    _, gw_ref = tp.tpconv_so2_backward(g, lmax, C, dev(ggx), D, wd, Gd, need=(False, True))
+    torch.cuda.synchronize()
+    assert torch.equal(gw, gw_ref)
+    Dn = D.cpu().numpy().astype(np.float64)
+    errs = {}
+    for tag, deg_of, pick in (("grad_G", dst, dst), ("grad_x", src, src)):
+        rows = sample_rows(np.bincount(deg_of, minlength=n), rng, k=24)
+        sel = np.isin(pick, rows)
+        r_gx, _, r_gG = so2_double_backward(lmax, C, inp["x"], Dn[sel], inp["weights"], inp["G"], ggx, ggw,
+                                            src[sel], dst[sel], n)
+        got = (gG if tag == "grad_G" else gx).cpu().numpy()
+        ref = r_gG if tag == "grad_G" else r_gx
+        errs[tag] = rel_err(got[rows], ref[rows])
+    log(f"[so2] double backward workload {name} errors {errs}")
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)
+
