@@ -12,8 +12,8 @@ of the same workload.  Outside the timed steps it also reports cold-cache
 kernel times (1 GiB read before each step), the double backward's two
 kernels (tpconv_double_backward with seeded cotangents), the upstream
 kernels (edge harmonics, their gradient, the position gradient) and the SO(2)
-convolution on the same graph (its rotations, forward, grad_x and
-map-gradient passes, against the fp32 matrix-core peak).
+convolution on the same graph (its rotations, forward, grad_x,
+map-gradient and double-backward passes, against the fp32 matrix-core peak).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -299,7 +299,10 @@ def main():
         o2, gx2 = torch.empty_like(x2), torch.empty_like(x2)
         gw2 = torch.empty_like(w2)
         ws2 = torch.empty(tp.tpconv_so2_workspace_bytes(L2, C2, E), dtype=torch.uint8, device=dev)
-        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.so2_reps + 2)]
+        ggx2 = torch.randn(x2.shape, dtype=torch.float32, device=dev, generator=torch.Generator(device=dev).manual_seed(5))
+        ggw2 = torch.randn(w2.shape, dtype=torch.float32, device=dev, generator=torch.Generator(device=dev).manual_seed(6))
+        dd2 = [torch.empty_like(x2), torch.empty_like(w2), torch.empty_like(x2)]
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.so2_reps + 2)]
         for k in range(args.so2_reps + 2):   # the first two are warm-up
             sev[k][0].record(stream)
             tp.tpconv_so2_rotations(L2, vec2, D2)
@@ -311,8 +314,10 @@ def main():
             tp.tpconv_so2_backward(graph, L2, C2, x2, D2, w2, G2, grad_weights=gw2, workspace=ws2,
                                    need=(False, True))
             sev[k][4].record(stream)
+            tp.tpconv_so2_double_backward(graph, L2, C2, x2, D2, w2, G2, ggx2, ggw2, *dd2, workspace=ws2)
+            sev[k][5].record(stream)
         torch.cuda.synchronize()
-        med = [float(np.median([e[i].elapsed_time(e[i + 1]) for e in sev[2:]])) for i in range(4)]
+        med = [float(np.median([e[i].elapsed_time(e[i + 1]) for e in sev[2:]])) for i in range(5)]
         fl = so2_flops_per_edge(L2, C2) * E
         tf = lambda ms: round(fl / (ms * 1e-3) / 1e12, 2)   # noqa: E731
         so2 = {"shape": f"l<={L2}, {C2} channels, {N} nodes, {E} edges, fp32",
@@ -325,8 +330,10 @@ def main():
                             "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(fl / (med[1] * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)},
                "fwd_bwd_edges_per_s": round(E / ((med[1] + med[2] + med[3]) * 1e-3), 1),
+               "double_backward_ms_median": round(med[4], 4),
+               "double_backward_TFLOPs": round(4 * fl / (med[4] * 1e-3) / 1e12, 2),
                "reps": args.so2_reps}
-        del vec2, x2, w2, G2, D2, o2, gx2, gw2, ws2
+        del vec2, x2, w2, G2, D2, o2, gx2, gw2, ws2, ggx2, ggw2, dd2
 
     b = 4 if w.dtype == "f32" else 8
     fwd_bytes, bwd_bytes = algorithmic_bytes(plan, N, E, b)
