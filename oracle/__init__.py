@@ -27,7 +27,8 @@ Modules:
   tp      -- dense per-edge forward, backward and double backward.
   forces  -- edge SH with their gradient, and the position gradient.
   so2     -- the SO(2) convolution (edge-frame rotation, per-|m| dense maps,
-             inverse rotation on reduction), its backward and double backward.
+             inverse rotation on reduction), its backward and double backward,
+             and the gradient through the edge frames to the edge vectors.
 
 Every function here is pinned by a test in ``tests/test_oracle_*.py`` against
 mathematics it does not itself use (library routines, closed forms,
@@ -40,4 +41,5 @@ from .sh import sh_complex, sh_real  # noqa: F401
 from .tp import TPProblem, tp_forward, tp_backward, tp_double_backward  # noqa: F401
 from .forces import sh_and_jacobian, sh_edges, sh_backward, positions_backward  # noqa: F401
 from .so2 import (edge_rotation, wigner_D, edge_wigner, so2_forward, so2_backward,  # noqa: F401
-                  so2_double_backward, weight_numel as so2_weight_numel)
+                  so2_double_backward, so2_frames_backward, rotations_backward,
+                  weight_numel as so2_weight_numel)

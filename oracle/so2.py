@@ -258,3 +258,67 @@ def so2_double_backward(lmax, C, x, D, weights, G, ggx, ggw, src, dst, n_nodes):
         grad_G += so2_forward(lmax, C, x, D, ggw, src, dst, n_nodes)
         grad_x = so2_backward(lmax, C, x, D, ggw, G, src, dst, n_nodes)[0]
     return grad_x, grad_w, grad_G
+
+
+# ------------------------------------------------- gradient through the frames
+def so2_frames_backward(lmax, C, x, D, weights, G, src, dst, n_nodes):
+    """grad_D [E, sum (2l+1)^2]: the gradient of <G, so2_forward(...)> with
+    respect to each edge's Wigner blocks.  D_e enters twice, in the rotation
+    on gather and in the inverse rotation, so with x~ = D_e x[src],
+    y~ = SO2(x~), g~ = D_e G[dst] and dx~ = SO2^T(g~):
+        grad_D^l[m][n] = sum_c dx~[l][c][m] x[src][l][c][n] + y~[l][c][m] G[dst][l][c][n]."""
+    x = np.asarray(x, dtype=np.float64)
+    G = np.asarray(G, dtype=np.float64)
+    src, dst = np.asarray(src, np.int64), np.asarray(dst, np.int64)
+    A, B = _maps(lmax, C, weights)
+    Dl = unpack_D(D, lmax)
+    xs, gd = _split(x[src], lmax, C), _split(G[dst], lmax, C)
+    yt = _so2_apply(_rotate(xs, Dl), lmax, C, A, B)
+    dxt = _so2_apply(_rotate(gd, Dl), lmax, C, A, B, adjoint=True)
+    return pack_D([np.einsum("ecm,ecn->emn", dxt[l], xs[l]) + np.einsum("ecm,ecn->emn", yt[l], gd[l])
+                   for l in range(lmax + 1)])
+
+
+def _rotation_of(v):
+    """edge_rotation's Rodrigues formula for one vector, written with plain
+    arithmetic only (so that it also runs on complex inputs)."""
+    r = np.sqrt(v[0] * v[0] + v[1] * v[1] + v[2] * v[2])
+    u = v / r
+    s = np.sqrt(u[0] * u[0] + u[1] * u[1])
+    c = u[2]
+    k = np.array([u[1] / s, -u[0] / s, 0.0 * s])
+    K = np.array([[0.0 * s, -k[2], k[1]], [k[2], 0.0 * s, -k[0]], [-k[1], k[0], 0.0 * s]])
+    return np.eye(3) + s * K + (1.0 - c) * (K @ K)
+
+
+def rotations_backward(lmax, vec, grad_D):
+    """grad_vec [E, 3] = sum over blocks of grad_D . dD/dvec for D = edge_wigner(lmax, vec).
+    dD^l[m][n]/dR = (1/4 pi) sum_k w_k grad Y_lm(R p_k) p_k^T Y_ln(p_k) over the
+    quadrature of wigner_D (the harmonics' Jacobian from forces.sh_and_jacobian;
+    R stays a rotation, so only the tangential part of grad Y enters), and
+    dR/dvec by the complex step on the Rodrigues formula (exact to rounding,
+    no subtraction).  Zero vectors and vectors along the z axis, where the
+    frame is set by convention, get zero."""
+    from .forces import sh_and_jacobian
+    vec = np.asarray(vec, dtype=np.float64).reshape(-1, 3)
+    Gl = unpack_D(grad_D, lmax)
+    pts, w = sphere_quadrature(2 * lmax)
+    Yp = sh_real(lmax, pts)                                   # [K, (L+1)^2]
+    out = np.zeros((len(vec), 3))
+    hstep = 1e-30
+    for e, v in enumerate(vec):
+        if np.hypot(v[0], v[1]) == 0.0:
+            continue
+        R = _rotation_of(v)
+        dR = np.stack([_rotation_of(v + 1j * hstep * np.eye(3)[j]).imag / hstep for j in range(3)])  # [3, 3, 3]
+        q = pts @ R.T                                         # R p_k
+        _, J = sh_and_jacobian(lmax, q)                       # [K, (L+1)^2, 3]
+        # dL/dR_ab = (1/4pi) sum_k w_k sum_{l,m,n} Gl[m][n] dY_lm/dq_a (q_k) p_kb Y_ln(p_k)
+        T = np.zeros((len(pts), (lmax + 1) ** 2))             # T[k, lm] = sum_n Gl[m][n] Y_ln(p_k)
+        for l in range(lmax + 1):
+            sl = slice(l * l, (l + 1) ** 2)
+            T[:, sl] = Yp[:, sl] @ Gl[l][e].T
+        dLdq = np.einsum("k,km,kma->ka", w, T, J) / (4.0 * np.pi)   # [K, 3]
+        dLdR = dLdq.T @ pts                                   # [3, 3]: sum_k dLdq[k, a] p_k[b]
+        out[e] = np.einsum("ab,jab->j", dLdR, dR)
+    return out

@@ -16,7 +16,10 @@ itself:
     <G, f(dx)> = <grad_x, dx> and <G, f(x; dw)> = <grad_w, dw> exactly;
   * the double backward: central differences of <ggx, grad_x> + <ggw, grad_w>
     through the pinned backward (exact: linear in each input separately),
-    the Euler identity in G, and the split by cotangent.
+    the Euler identity in G, and the split by cotangent;
+  * the gradient through the frames: central differences in D (exact: the
+    energy is quadratic in D), of <grad_D, D(vec)> in the edge vectors, and
+    of the whole energy in the edge vectors, plus radial invariance.
 """
 
 from math import gamma
@@ -329,3 +332,58 @@ def test_double_backward_by_differences(lmax, C):
     gx_b, gw_b, gG_b = so2_double_backward(lmax, C, x, D, w, G, None, ggw, src, dst, n)
     assert np.all(gw_b == 0) and np.abs(gx_b).max() > 0
     np.testing.assert_allclose(gG_a + gG_b, gG2, atol=1e-12)
+
+
+def test_frames_backward_exact_in_D():
+    """<G, out> is quadratic in the Wigner blocks (they enter twice), so a
+    central difference in D is exact up to rounding."""
+    from oracle.so2 import so2_frames_backward
+    rng = np.random.default_rng(120)
+    lmax, C, n, E = 2, 2, 6, 25
+    src, dst, vec = make_graph(rng, n, E)
+    D = edge_wigner(lmax, vec)
+    x, G = rng.standard_normal((n, C * 9)), rng.standard_normal((n, C * 9))
+    w = rng.standard_normal(weight_numel(lmax, C))
+    gD = so2_frames_backward(lmax, C, x, D, w, G, src, dst, n)
+    f = lambda D_: np.vdot(G, so2_forward(lmax, C, x, D_, w, src, dst, n))  # noqa: E731
+    for _ in range(3):
+        dD = rng.standard_normal(D.shape)
+        fd = (f(D + 0.5 * dD) - f(D - 0.5 * dD)) / 1.0
+        assert np.vdot(gD, dD) == pytest.approx(fd, rel=1e-10)
+
+
+@pytest.mark.parametrize("lmax", [1, 3])
+def test_rotations_backward_by_differences(lmax):
+    from oracle.so2 import rotations_backward
+    rng = np.random.default_rng(121 + lmax)
+    vec = rng.standard_normal((12, 3)) * 2.0
+    gD = rng.standard_normal(edge_wigner(lmax, vec).shape)
+    g = rotations_backward(lmax, vec, gD)
+    h = 1e-6
+    for j in range(3):
+        dv = np.zeros_like(vec)
+        dv[:, j] = h
+        fd = (np.sum(gD * edge_wigner(lmax, vec + dv), axis=1) - np.sum(gD * edge_wigner(lmax, vec - dv), axis=1)) / (2 * h)
+        np.testing.assert_allclose(g[:, j], fd, rtol=1e-6, atol=1e-7)
+
+
+def test_force_through_the_frames():
+    """The whole chain: d<G, out>/dvec from so2_frames_backward and
+    rotations_backward against central differences of the energy in the edge
+    vectors (the energy does not depend on the frames' roll, so this also
+    checks the chain against the frame convention)."""
+    from oracle.so2 import rotations_backward, so2_frames_backward
+    rng = np.random.default_rng(125)
+    lmax, C, n, E = 3, 2, 6, 20
+    src, dst, vec = make_graph(rng, n, E)
+    x, G = rng.standard_normal((n, C * 16)), rng.standard_normal((n, C * 16))
+    w = rng.standard_normal(weight_numel(lmax, C))
+    gvec = rotations_backward(lmax, vec, so2_frames_backward(lmax, C, x, edge_wigner(lmax, vec), w, G, src, dst, n))
+    energy = lambda v: np.vdot(G, so2_forward(lmax, C, x, edge_wigner(lmax, v), w, src, dst, n))  # noqa: E731
+    h = 1e-6
+    for _ in range(3):
+        dv = rng.standard_normal(vec.shape)
+        fd = (energy(vec + h * dv) - energy(vec - h * dv)) / (2 * h)
+        assert np.vdot(gvec, dv) == pytest.approx(fd, rel=1e-6, abs=1e-8)
+    # radial invariance: the frames depend on the direction only
+    np.testing.assert_allclose(np.einsum("ej,ej->e", gvec, vec), 0.0, atol=1e-9)
