@@ -277,7 +277,8 @@ extern "C" tpconv_status tpconv_so2_forward(tpconv_graph_t hg, int lmax, int cha
   if (g.n_edges > 0 && (x == nullptr || D == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL x or D");
   const hipError_t he = launch_so2_conv(lmax, channels, false, false, (int)g.n_nodes, g.dst_row, g.dst_col, g.dst_eid,
                                         g.dst_order, static_cast<const float*>(x), static_cast<const float*>(D),
-                                        static_cast<const float*>(weights), static_cast<float*>(out), nullptr, stream);
+                                        static_cast<const float*>(weights), static_cast<float*>(out), nullptr, nullptr,
+                                        stream);
   if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("SO(2) forward launch: ") + hipGetErrorString(he));
   return TPCONV_OK;
 }
@@ -310,7 +311,7 @@ extern "C" tpconv_status tpconv_so2_backward(tpconv_graph_t hg, int lmax, int ch
     const hipError_t he = launch_so2_conv(lmax, channels, true, false, (int)g.n_nodes, g.src_row, g.src_col, g.src_eid,
                                           g.src_order, static_cast<const float*>(grad_out),
                                           static_cast<const float*>(D), static_cast<const float*>(weights),
-                                          static_cast<float*>(grad_x), ws_maps, stream);
+                                          static_cast<float*>(grad_x), ws_maps, nullptr, stream);
     if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("SO(2) backward launch: ") + hipGetErrorString(he));
   }
   if (grad_weights != nullptr) {
@@ -367,12 +368,12 @@ extern "C" tpconv_status tpconv_so2_double_backward(tpconv_graph_t hg, int lmax,
     if (ggx != nullptr)
       st = check(launch_so2_conv(lmax, channels, false, false, (int)g.n_nodes, g.dst_row, g.dst_col, g.dst_eid,
                                  g.dst_order, static_cast<const float*>(ggx), fD, static_cast<const float*>(weights),
-                                 out, nullptr, stream),
+                                 out, nullptr, nullptr, stream),
                  "SO(2) double backward launch: ");
     if (st == TPCONV_OK && ggw != nullptr)
       st = check(launch_so2_conv(lmax, channels, false, ggx != nullptr, (int)g.n_nodes, g.dst_row, g.dst_col,
                                  g.dst_eid, g.dst_order, fx, fD, static_cast<const float*>(ggw), out, nullptr,
-                                 stream),
+                                 nullptr, stream),
                  "SO(2) double backward launch: ");
     if (st == TPCONV_OK && ggx == nullptr && ggw == nullptr)
       st = check(launch_so2_fill_zero(nd, out, stream), "SO(2) double backward fill: ");
@@ -383,7 +384,8 @@ extern "C" tpconv_status tpconv_so2_double_backward(tpconv_graph_t hg, int lmax,
     float* out = static_cast<float*>(grad_x);
     st = ggw != nullptr
              ? check(launch_so2_conv(lmax, channels, true, false, (int)g.n_nodes, g.src_row, g.src_col, g.src_eid,
-                                     g.src_order, fG, fD, static_cast<const float*>(ggw), out, ws_maps, stream),
+                                     g.src_order, fG, fD, static_cast<const float*>(ggw), out, ws_maps, nullptr,
+                                     stream),
                      "SO(2) double backward launch: ")
              : check(launch_so2_fill_zero(nd, out, stream), "SO(2) double backward fill: ");
     if (st != TPCONV_OK) return st;
@@ -398,5 +400,49 @@ extern "C" tpconv_status tpconv_so2_double_backward(tpconv_graph_t hg, int lmax,
              : check(launch_so2_fill_zero(nw, out, stream), "SO(2) double backward fill: ");
   }
   return st;
+}
+
+extern "C" tpconv_status tpconv_so2_frames_backward(tpconv_graph_t hg, int lmax, int channels, tpconv_dtype dtype,
+                                                    const void* x, const void* D, const void* weights,
+                                                    const void* grad_out, void* grad_D, void* workspace,
+                                                    size_t workspace_bytes, hipStream_t stream) {
+  if (hg == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL graph");
+  if (!so2_supported(lmax, channels) || dtype != TPCONV_F32)
+    return fail(TPCONV_E_UNSUPPORTED, "SO(2) convolution: lmax 1..3, channels 16 or 32, fp32");
+  const Graph& g = *reinterpret_cast<const Graph*>(hg);
+  if (grad_D == nullptr || g.n_edges == 0) return TPCONV_OK;
+  const size_t need = tpconv_so2_workspace_bytes(lmax, channels, g.n_edges);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(TPCONV_E_WORKSPACE, "SO(2) frames backward: workspace smaller than tpconv_so2_workspace_bytes()");
+  if (x == nullptr || D == nullptr || weights == nullptr || grad_out == nullptr)
+    return fail(TPCONV_E_INVALID_ARG, "NULL x, D, weights or grad_out");
+  if (reinterpret_cast<uintptr_t>(weights) % 16 != 0 || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(TPCONV_E_INVALID_ARG, "SO(2) weights and workspace must be 16-byte aligned");
+  const float* fx = static_cast<const float*>(x);
+  const float* fG = static_cast<const float*>(grad_out);
+  const float* fD = static_cast<const float*>(D);
+  const float* fW = static_cast<const float*>(weights);
+  float* out = static_cast<float*>(grad_D);
+  // the y~ G^T term over the destination rows (overwrites), then the dx~ x^T term over the source rows (adds)
+  hipError_t he = launch_so2_conv(lmax, channels, false, false, (int)g.n_nodes, g.dst_row, g.dst_col, g.dst_eid,
+                                  g.dst_order, fx, fD, fW, out, nullptr, fG, stream);
+  if (he == hipSuccess)
+    he = launch_so2_conv(lmax, channels, true, true, (int)g.n_nodes, g.src_row, g.src_col, g.src_eid, g.src_order,
+                         fG, fD, fW, out, static_cast<float*>(workspace), fx, stream);
+  if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("SO(2) frames backward launch: ") + hipGetErrorString(he));
+  return TPCONV_OK;
+}
+
+extern "C" tpconv_status tpconv_so2_rotations_backward(int lmax, tpconv_dtype dtype, int64_t n_edges, const void* vec,
+                                                       const void* grad_D, void* grad_vec, hipStream_t stream) {
+  if (n_edges < 0) return fail(TPCONV_E_INVALID_ARG, "n_edges < 0");
+  if (lmax < 0 || lmax > 4) return fail(TPCONV_E_UNSUPPORTED, "SO(2) rotations: lmax must be 0..4");
+  if (dtype != TPCONV_F32 && dtype != TPCONV_F64) return fail(TPCONV_E_INVALID_ARG, "unknown dtype");
+  if (n_edges > 0 && (vec == nullptr || grad_D == nullptr || grad_vec == nullptr))
+    return fail(TPCONV_E_INVALID_ARG, "NULL vec, grad_D or grad_vec");
+  const hipError_t he = launch_so2_wigner_backward(lmax, dtype == TPCONV_F64, n_edges, vec, grad_D, grad_vec, stream);
+  if (he != hipSuccess)
+    return fail(TPCONV_E_HIP, std::string("SO(2) rotations backward launch: ") + hipGetErrorString(he));
+  return TPCONV_OK;
 }
 

@@ -320,6 +320,116 @@ __global__ __launch_bounds__(64) void k_so2_wigner(int64_t n, const T* __restric
   for (int q = 0; q < ND; ++q) out[q] = T(acc[q]);
 }
 
+// The gradient through the frames: grad_vec[e] = sum_{l,m,n} grad_D[e]^l[m][n]
+// dD^l[m][n]/dvec, differentiating the same quadrature,
+//   dD^l[m][n]/dvec = sum_k w_k (2l+1) (dS_lm(R p_k)/dvec) S_ln(p_k),
+// with dual numbers carrying d/dvec through the Rodrigues frame and the
+// solid-harmonic recurrences at q_k = R p_k.  Vectors on the z axis (the
+// zero vector included), where the frame is set by convention, get zero.
+template <typename T>
+__device__ __forceinline__ Dual<T> dsum(const Dual<T>& a, const Dual<T>& b) {
+  return {a.v + b.v, a.dx + b.dx, a.dy + b.dy, a.dz + b.dz};
+}
+template <typename T>
+__device__ __forceinline__ Dual<T> dsqrt(const Dual<T>& a) {
+  const T v = sqrt(a.v), f = T(0.5) / v;
+  return {v, a.dx * f, a.dy * f, a.dz * f};
+}
+template <typename T>
+__device__ __forceinline__ Dual<T> ddiv(const Dual<T>& a, const Dual<T>& b) {
+  const T iv = T(1) / b.v, q = a.v * iv;
+  return {q, (a.dx - q * b.dx) * iv, (a.dy - q * b.dy) * iv, (a.dz - q * b.dz) * iv};
+}
+
+template <typename T, int L>
+__global__ __launch_bounds__(64) void k_so2_wigner_backward(int64_t n, const T* __restrict__ vec,
+                                                            const T* __restrict__ gD, T* __restrict__ gvec) {
+  using D3 = Dual<double>;
+  constexpr int NS = (L + 1) * (L + 1);
+  constexpr int ND = (L + 1) * (2 * L + 1) * (2 * L + 3) / 3;
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  const double vx = vec[3 * e], vy = vec[3 * e + 1], vz = vec[3 * e + 2];
+  T* o = gvec + 3 * e;
+  if (vx == 0.0 && vy == 0.0) {
+    o[0] = o[1] = o[2] = T(0);
+    return;
+  }
+  const D3 X{vx, 1.0, 0.0, 0.0}, Yv{vy, 0.0, 1.0, 0.0}, Z{vz, 0.0, 0.0, 1.0};
+  const D3 r = dsqrt(dsum(dsum(dmul(X, X), dmul(Yv, Yv)), dmul(Z, Z)));
+  const D3 ux = ddiv(X, r), uy = ddiv(Yv, r), uz = ddiv(Z, r);
+  const D3 sn = dsqrt(dsum(dmul(ux, ux), dmul(uy, uy)));
+  const D3 kx = ddiv(uy, sn), ky = dscale(-1.0, ddiv(ux, sn));
+  const D3 zero{0.0, 0.0, 0.0, 0.0};
+  const D3 one_m_c = dlin(1.0, D3{1.0, 0.0, 0.0, 0.0}, -1.0, uz);
+  const D3 K[3][3] = {{zero, zero, ky}, {zero, zero, dscale(-1.0, kx)}, {dscale(-1.0, ky), kx, zero}};
+  D3 R[3][3];
+  for (int a = 0; a < 3; ++a)
+    for (int b = 0; b < 3; ++b) {
+      D3 k2 = zero;
+      for (int q = 0; q < 3; ++q) k2 = dsum(k2, dmul(K[a][q], K[q][b]));
+      R[a][b] = dsum(dsum(D3{a == b ? 1.0 : 0.0, 0.0, 0.0, 0.0}, dmul(sn, K[a][b])), dmul(one_m_c, k2));
+    }
+  double g[ND];
+  for (int q = 0; q < ND; ++q) g[q] = gD[e * ND + q];
+  double gx = 0.0, gy = 0.0, gz = 0.0;
+  constexpr int NZ = L + 1, NP = 2 * L + 1;
+  for (int iz = 0; iz < NZ; ++iz) {
+    double z, wz;
+    gauss_legendre(NZ, iz, z, wz);
+    const double rho = sqrt(fmax(0.0, 1.0 - z * z));
+    for (int ip = 0; ip < NP; ++ip) {
+      double sp, cp;
+      sincos(2.0 * M_PI * ip / NP, &sp, &cp);
+      const double p[3] = {rho * cp, rho * sp, z};
+      D3 q[3];
+      for (int a = 0; a < 3; ++a) q[a] = dsum(dsum(dscale(p[0], R[a][0]), dscale(p[1], R[a][1])), dscale(p[2], R[a][2]));
+      const D3 q2 = dsum(dsum(dmul(q[0], q[0]), dmul(q[1], q[1])), dmul(q[2], q[2]));
+      double Sp[NS];
+      D3 Sq[NS];
+      solid_harmonics<L, double, PlainOps<double>>(p[0], p[1], p[2], 1.0, 1.0, Sp);
+      solid_harmonics<L, D3, DualOps<double>>(q[0], q[1], q[2], q2, D3{1.0, 0.0, 0.0, 0.0}, Sq);
+      const double w = wz / (2.0 * NP);
+      sh_for<L + 1>([&](auto IL) {
+        constexpr int l = IL, n2 = 2 * l + 1, off = l * (2 * l - 1) * (2 * l + 1) / 3;
+        const double wl = w * n2;
+        sh_for<n2>([&](auto M) {
+          double t = 0.0;
+          sh_for<n2>([&](auto N) { t += g[off + M * n2 + N] * Sp[l * l + N]; });
+          t *= wl;
+          const D3& sq = Sq[l * l + M];
+          gx += t * sq.dx;
+          gy += t * sq.dy;
+          gz += t * sq.dz;
+        });
+      });
+    }
+  }
+  o[0] = T(gx);
+  o[1] = T(gy);
+  o[2] = T(gz);
+}
+
+template <typename T, int L>
+hipError_t wigner_bwd_T(int64_t n, const void* vec, const void* gD, void* gvec, hipStream_t s) {
+  const int64_t blocks = (n + 63) / 64;
+  hipLaunchKernelGGL((k_so2_wigner_backward<T, L>), dim3((unsigned)blocks), dim3(64), 0, s, n,
+                     static_cast<const T*>(vec), static_cast<const T*>(gD), static_cast<T*>(gvec));
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t wigner_bwd_dispatch(int L, int64_t n, const void* vec, const void* gD, void* gvec, hipStream_t s) {
+  switch (L) {
+    case 0: return wigner_bwd_T<T, 0>(n, vec, gD, gvec, s);
+    case 1: return wigner_bwd_T<T, 1>(n, vec, gD, gvec, s);
+    case 2: return wigner_bwd_T<T, 2>(n, vec, gD, gvec, s);
+    case 3: return wigner_bwd_T<T, 3>(n, vec, gD, gvec, s);
+    case 4: return wigner_bwd_T<T, 4>(n, vec, gD, gvec, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename T, int L>
 hipError_t wigner_T(int64_t n, const void* vec, void* D, hipStream_t s) {
   const int64_t blocks = (n + 63) / 64;
@@ -385,6 +495,13 @@ hipError_t launch_sh_backward(int L, bool f64, int64_t n_edges, const void* vec,
 hipError_t launch_so2_wigner(int L, bool f64, int64_t n_edges, const void* vec, void* D, hipStream_t s) {
   if (n_edges <= 0) return hipSuccess;
   return f64 ? wigner_dispatch<double>(L, n_edges, vec, D, s) : wigner_dispatch<float>(L, n_edges, vec, D, s);
+}
+
+hipError_t launch_so2_wigner_backward(int L, bool f64, int64_t n_edges, const void* vec, const void* grad_D,
+                                      void* grad_vec, hipStream_t s) {
+  if (n_edges <= 0) return hipSuccess;
+  return f64 ? wigner_bwd_dispatch<double>(L, n_edges, vec, grad_D, grad_vec, s)
+             : wigner_bwd_dispatch<float>(L, n_edges, vec, grad_D, grad_vec, s);
 }
 
 hipError_t launch_pos_backward(bool f64, int64_t n_nodes, const int32_t* src_row, const int32_t* src_eid,

@@ -283,16 +283,27 @@ __device__ __forceinline__ void so2_maps(float* tile, const float* __restrict__ 
 // rows' blocks fit a SIMD pair's LDS, so each SIMD holds two wavefronts).
 // Wavefront w rotates and inverse-rotates edges 8w .. 8w + 7 of each chunk
 // and runs half of the n-tiles; the two row sums meet in LDS at the end.
-template <int L, int C, bool ADJ>
+//
+// FRAMES: the same rotation and maps, then, instead of the inverse rotation,
+// the gradient with respect to the chunk's Wigner blocks.  With V the row's
+// own vector (grad_out of the destination row over the destination-sorted
+// rows, x of the source row over the source-sorted rows with the adjoint
+// maps), the tile holds y~ (resp. dx~) and
+//   gD[e]^l[m][n] (+)= sum_c tile[e][l][c][m] V[l][c][n],
+// which is grad_D's y~ G^T (resp. dx~ x^T) term: out is then gD [E][ND],
+// indexed by edge id, overwritten or (accumulate) added to.
+template <int L, int C, bool ADJ, bool FRAMES>
 __global__ __launch_bounds__(128, 2) void k_so2_conv(const int32_t* __restrict__ row_ptr,
                                                      const int32_t* __restrict__ col, const int32_t* __restrict__ eid,
                                                      const int32_t* __restrict__ order, const float* __restrict__ X,
                                                      const float* __restrict__ Dm, const float* __restrict__ W,
-                                                     float* __restrict__ out, const int accumulate) {
+                                                     float* __restrict__ out, const int accumulate,
+                                                     const float* __restrict__ V) {
   using S = So2Shape<L, C>;
   static_assert(S::NACC * 64 <= S::kEdges * S::PAD, "row-sum exchange must fit the tile");
   __shared__ float tile[S::kEdges * S::PAD];
   __shared__ float dl[S::kEdges * S::NDP];
+  __shared__ float vrow[FRAMES ? S::DN : 1];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int c = lane % C, h = lane / C;
@@ -300,6 +311,9 @@ __global__ __launch_bounds__(128, 2) void k_so2_conv(const int32_t* __restrict__
   const int beg = row_ptr[row], end = row_ptr[row + 1];
   float acc[S::NACC];
   so2_for<S::NACC>([&](auto I) { acc[I] = 0.f; });
+  if constexpr (FRAMES) {
+    for (int q = threadIdx.x; q < S::DN; q += 128) vrow[q] = V[(int64_t)row * S::DN + q];
+  }
 
   for (int k0 = beg; k0 < end; k0 += S::kEdges) {
     const int ne = min(S::kEdges, end - k0);
@@ -325,6 +339,28 @@ __global__ __launch_bounds__(128, 2) void k_so2_conv(const int32_t* __restrict__
       so2_maps<L, C, ADJ, 1>(tile, W, lane);
     __syncthreads();
 
+    if constexpr (FRAMES) {
+      // entry r = (l, m, n) of edge e: thread q covers q, q + 128, ...
+      for (int q = threadIdx.x; q < ne * S::ND; q += 128) {
+        const int e = q / S::ND;
+        int r = q - e * S::ND, l = 0;
+        while (r >= (2 * l + 1) * (2 * l + 1)) {
+          r -= (2 * l + 1) * (2 * l + 1);
+          ++l;
+        }
+        const int n2 = 2 * l + 1, m = r / n2, n = r - m * n2;
+        const float* te = &tile[e * S::PAD + C * l * l + m];
+        const float* ve = &vrow[C * l * l + n];
+        float sum = 0.f;
+#pragma unroll 8
+        for (int cc = 0; cc < C; ++cc) sum = fmaf(te[cc * n2], ve[cc * n2], sum);
+        float* o = &out[(int64_t)eid[k0 + e] * S::ND + (q - e * S::ND)];
+        *o = accumulate ? *o + sum : sum;  // each edge has one row in each view
+      }
+      __syncthreads();
+      continue;
+    }
+
     // inverse rotation on reduction: lane (c, h) sums components n = h, h + NSPLIT, ...
     const int e_end = min(ne, 8 * wave + 8);
     for (int e = 8 * wave; e < e_end; ++e) {  // wave-uniform
@@ -347,6 +383,7 @@ __global__ __launch_bounds__(128, 2) void k_so2_conv(const int32_t* __restrict__
     __syncthreads();
   }
 
+  if constexpr (FRAMES) return;
   // the two wavefronts' row sums (wavefront 1's through the tile), written once
   if (wave == 1) so2_for<S::NACC>([&](auto I) { tile[int(I) * 64 + lane] = acc[I]; });
   __syncthreads();
@@ -525,18 +562,26 @@ __global__ __launch_bounds__(256) void k_so2_wsum(int nb, int64_t nw, const floa
 template <int L, int C>
 hipError_t conv_LC(bool adjoint, bool accumulate, int n_rows, const int32_t* row_ptr, const int32_t* col,
                    const int32_t* eid, const int32_t* order, const float* X, const float* D, const float* W,
-                   float* out, float* Wt, hipStream_t s) {
+                   float* out, float* Wt, const float* V, hipStream_t s) {
   using S = So2Shape<L, C>;
   if (adjoint) {
     hipLaunchKernelGGL((k_so2_transpose<L, C>), dim3((unsigned)((S::NW + 255) / 256)), dim3(256), 0, s, W, Wt);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_so2_conv<L, C, true>), dim3((unsigned)n_rows), dim3(128), 0, s, row_ptr, col, eid, order,
-                       X, D, Wt, out, (int)accumulate);
+    if (V != nullptr)
+      hipLaunchKernelGGL((k_so2_conv<L, C, true, true>), dim3((unsigned)n_rows), dim3(128), 0, s, row_ptr, col, eid,
+                         order, X, D, Wt, out, (int)accumulate, V);
+    else
+      hipLaunchKernelGGL((k_so2_conv<L, C, true, false>), dim3((unsigned)n_rows), dim3(128), 0, s, row_ptr, col, eid,
+                         order, X, D, Wt, out, (int)accumulate, V);
   }
   else
-    hipLaunchKernelGGL((k_so2_conv<L, C, false>), dim3((unsigned)n_rows), dim3(128), 0, s, row_ptr, col, eid, order,
-                       X, D, W, out, (int)accumulate);
+    if (V != nullptr)
+      hipLaunchKernelGGL((k_so2_conv<L, C, false, true>), dim3((unsigned)n_rows), dim3(128), 0, s, row_ptr, col, eid,
+                         order, X, D, W, out, (int)accumulate, V);
+    else
+      hipLaunchKernelGGL((k_so2_conv<L, C, false, false>), dim3((unsigned)n_rows), dim3(128), 0, s, row_ptr, col, eid,
+                         order, X, D, W, out, (int)accumulate, V);
   return hipGetLastError();
 }
 
@@ -582,9 +627,9 @@ int so2_wgrad_blocks(int64_t n_edges) {
 
 hipError_t launch_so2_conv(int L, int C, bool adjoint, bool accumulate, int n_rows, const int32_t* row_ptr,
                            const int32_t* col, const int32_t* eid, const int32_t* order, const float* X,
-                           const float* D, const float* W, float* out, float* Wt, hipStream_t s) {
+                           const float* D, const float* W, float* out, float* Wt, const float* V, hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
-  SO2_CASES(conv_LC, adjoint, accumulate, n_rows, row_ptr, col, eid, order, X, D, W, out, Wt, s)
+  SO2_CASES(conv_LC, adjoint, accumulate, n_rows, row_ptr, col, eid, order, X, D, W, out, Wt, V, s)
 }
 
 hipError_t launch_so2_wgrad(int L, int C, int n_rows, int64_t n_edges, const int32_t* row_ptr, const int32_t* col,

@@ -104,11 +104,14 @@ TPCONV_DECLARE_LAUNCHERS(4)
 hipError_t launch_so2_wigner(int L, bool f64, int64_t n_edges, const void* vec, void* D, hipStream_t s);
 int64_t so2_weight_numel(int L, int C);
 int so2_wgrad_blocks(int64_t n_edges);
-// accumulate: out += instead of out = (each row has one writer, so still deterministic)
+// accumulate: out += instead of out = (each row has one writer, so still deterministic).
+// Wt: adjoint only, weight_numel floats.  V non-null: the frame-gradient mode, out = grad_D
+// [E][sum (2l+1)^2] by edge id, V the rows' own vectors (grad_out, or x for the adjoint).
 hipError_t launch_so2_conv(int L, int C, bool adjoint, bool accumulate, int n_rows, const int32_t* row_ptr,
                            const int32_t* col, const int32_t* eid, const int32_t* order, const float* X,
-                           const float* D, const float* W, float* out, float* Wt,
-                           hipStream_t s);  // Wt: adjoint only, weight_numel floats
+                           const float* D, const float* W, float* out, float* Wt, const float* V, hipStream_t s);
+hipError_t launch_so2_wigner_backward(int L, bool f64, int64_t n_edges, const void* vec, const void* grad_D,
+                                      void* grad_vec, hipStream_t s);
 hipError_t launch_so2_fill_zero(int64_t n, float* p, hipStream_t s);
 hipError_t launch_so2_wgrad(int L, int C, int n_rows, int64_t n_edges, const int32_t* row_ptr, const int32_t* col,
                             const int32_t* eid, const float* X, const float* G, const float* D, float* part,

@@ -30,7 +30,8 @@ EXPORTS = ("tpconv_plan", "tpconv_plan_query", "tpconv_plan_paths", "tpconv_plan
            "tpconv_graph_workspace_bytes", "tpconv_graph_create", "tpconv_graph_export", "tpconv_graph_destroy",
            "tpconv_forward", "tpconv_backward", "tpconv_double_backward", "tpconv_sh", "tpconv_sh_backward",
            "tpconv_positions_backward", "tpconv_so2_weight_numel", "tpconv_so2_rotations", "tpconv_so2_forward",
-           "tpconv_so2_workspace_bytes", "tpconv_so2_backward", "tpconv_so2_double_backward", "tpconv_last_error")
+           "tpconv_so2_workspace_bytes", "tpconv_so2_backward", "tpconv_so2_double_backward",
+           "tpconv_so2_frames_backward", "tpconv_so2_rotations_backward", "tpconv_last_error")
 
 
 class TPConvError(RuntimeError):
@@ -76,6 +77,8 @@ def _load():
         "tpconv_so2_backward": (i32, [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, sz,
                                       vp]),
         "tpconv_so2_double_backward": (i32, [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int] + [vp] * 10 + [sz, vp]),
+        "tpconv_so2_frames_backward": (i32, [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int] + [vp] * 6 + [sz, vp]),
+        "tpconv_so2_rotations_backward": (i32, [ctypes.c_int, ctypes.c_int, i64, vp, vp, vp, vp]),
         "tpconv_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -441,4 +444,41 @@ def tpconv_so2_double_backward(graph: Graph, lmax: int, channels: int, x, D, wei
                                            _ptr(outs[1]), _ptr(outs[2]), _ptr(workspace), ws_bytes,
                                            _stream_handle(stream)))
     return tuple(outs)
+
+
+def tpconv_so2_frames_backward(graph: Graph, lmax: int, channels: int, x, D, weights, grad_out, grad_D=None,
+                               workspace=None, stream=None) -> torch.Tensor:
+    """grad_D [E, sum (2l+1)^2]: gradient of <grad_out, out> with respect to the Wigner blocks."""
+    N, E = graph.n_nodes, graph.n_edges
+    dn, nd, nw = _so2_sizes(lmax, channels)
+    f = torch.float32
+    _need(x, (N, dn), f, "x")
+    _need(D, (E, nd), f, "D")
+    _need(weights, (nw,), f, "weights")
+    _need(grad_out, (N, dn), f, "grad_out")
+    if grad_D is None:
+        grad_D = torch.empty((E, nd), dtype=f, device=x.device)
+    _need(grad_D, (E, nd), f, "grad_D")
+    if workspace is None:
+        workspace = torch.empty(max(tpconv_so2_workspace_bytes(lmax, channels, E), 256), dtype=torch.uint8,
+                                device=x.device)
+    _check(_lib.tpconv_so2_frames_backward(graph.handle, int(lmax), int(channels), F32, _ptr(x), _ptr(D),
+                                           _ptr(weights), _ptr(grad_out), _ptr(grad_D), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _stream_handle(stream)))
+    return grad_D
+
+
+def tpconv_so2_rotations_backward(lmax: int, vec, grad_D, grad_vec=None, stream=None) -> torch.Tensor:
+    """grad_vec [E, 3] from grad_D [E, sum (2l+1)^2] (dtype of vec)."""
+    E = vec.shape[0] if vec.dim() == 2 else -1
+    dt = vec.dtype
+    _need(vec, (E, 3), dt, "vec")
+    nd = (lmax + 1) * (2 * lmax + 1) * (2 * lmax + 3) // 3
+    _need(grad_D, (E, nd), dt, "grad_D")
+    if grad_vec is None:
+        grad_vec = torch.empty((E, 3), dtype=dt, device=vec.device)
+    _need(grad_vec, (E, 3), dt, "grad_vec")
+    _check(_lib.tpconv_so2_rotations_backward(int(lmax), F64 if dt == torch.float64 else F32, E, _ptr(vec),
+                                              _ptr(grad_D), _ptr(grad_vec), _stream_handle(stream)))
+    return grad_vec
 

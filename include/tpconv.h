@@ -336,6 +336,29 @@ tpconv_status tpconv_so2_double_backward(tpconv_graph_t g, int lmax, int channel
                                          const void* ggw, void* grad_x, void* grad_weights, void* grad_G,
                                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* tpconv_so2_frames_backward: grad_D [E][sum (2l+1)^2] (overwritten), the
+ * gradient of <grad_out, out> with respect to each edge's Wigner blocks, for
+ * forces through the edge frames (chain on with tpconv_so2_rotations_backward
+ * and tpconv_positions_backward).  D_e enters twice, so with
+ * x~ = D_e x[src], y~ = SO2(x~), dx~ = SO2^T(D_e grad_out[dst]):
+ *   grad_D[e]^l[m][n] = sum_c y~[l][c][m] grad_out[dst][l][c][n]
+ *                     + sum_c dx~[l][c][m] x[src][l][c][n].
+ * The forward's kernel recomputes y~ over the destination rows and the
+ * adjoint's recomputes dx~ over the source rows (no per-edge tensor is
+ * kept between passes); each contracts its tile with the row's own vector.
+ * Workspace, alignment and errors as tpconv_so2_backward. */
+tpconv_status tpconv_so2_frames_backward(tpconv_graph_t g, int lmax, int channels, tpconv_dtype dtype, const void* x,
+                                         const void* D, const void* weights, const void* grad_out, void* grad_D,
+                                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* tpconv_so2_rotations_backward: grad_vec [E][3] (overwritten) =
+ * sum over blocks of grad_D[e] . dD/dvec for D = tpconv_so2_rotations(vec),
+ * differentiating the same quadrature through the frame (dual numbers,
+ * fp64 inside).  Vectors on the z axis (and the zero vector), where the
+ * frame is a convention, get zero.  Errors as tpconv_so2_rotations. */
+tpconv_status tpconv_so2_rotations_backward(int lmax, tpconv_dtype dtype, int64_t n_edges, const void* vec,
+                                            const void* grad_D, void* grad_vec, hipStream_t stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* tpconv_last_error(void);
 

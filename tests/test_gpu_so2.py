@@ -301,3 +301,99 @@ def test_double_backward_workload(tp, name):
     for k, v in errs.items():
         assert v <= TOL, (k, v)
 
+
+
+# ------------------------------------------------------ gradient through frames
+@pytest.mark.parametrize("lmax", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("dt", ["f32", "f64"])
+def test_rotations_backward(tp, lmax, dt):
+    import torch
+    from oracle.so2 import rotations_backward
+    rng = np.random.default_rng(400 + lmax)
+    npdt = np.float32 if dt == "f32" else np.float64
+    vec = (rng.standard_normal((700, 3)) * rng.uniform(0.1, 6.0, (700, 1))).astype(npdt)
+    vec[::53] = 0.0
+    vec[1] = [0, 0, 1.5]
+    vec[2] = [0, 0, -2.0]
+    vec[3] = [1e-3, 0, -1.0]
+    nd = (lmax + 1) * (2 * lmax + 1) * (2 * lmax + 3) // 3
+    gD = rng.standard_normal((700, nd)).astype(npdt)
+    gv = tp.tpconv_so2_rotations_backward(lmax, dev(vec), dev(gD))
+    torch.cuda.synchronize()
+    ref = rotations_backward(lmax, vec.astype(np.float64), gD.astype(np.float64))
+    err = rel_err(gv.cpu().numpy(), ref)
+    log(f"[so2] rotations backward l<={lmax} {dt} error {err:.3e}")
+    assert err <= (TOL if dt == "f32" else 1e-11)
+    g = gv.cpu().numpy()
+    assert np.all(g[::53] == 0) and np.all(g[1:3] == 0)
+
+
+@pytest.mark.parametrize("lmax,C", [(1, 16), (2, 32), (3, 16), (3, 32)])
+def test_frames_backward_small(tp, lmax, C):
+    import torch
+    from oracle.so2 import rotations_backward, so2_frames_backward
+    rng = np.random.default_rng(410 + 10 * lmax + C)
+    n = 35
+    dst = np.concatenate([np.full(21, 3), rng.integers(0, n, 160)])
+    src = rng.integers(0, n, len(dst))
+    keep = (src != 6) & (dst != 6)
+    src, dst = src[keep].astype(np.int32), dst[keep].astype(np.int32)
+    vec = (rng.standard_normal((len(src), 3)) * 2.0).astype(np.float32)
+    d, nw = C * (lmax + 1) ** 2, weight_numel(lmax, C)
+    x, G = rng.standard_normal((n, d)).astype(np.float32), rng.standard_normal((n, d)).astype(np.float32)
+    w = (rng.standard_normal(nw) / np.sqrt(2 * C * (lmax + 1))).astype(np.float32)
+    g = tp.tpconv_graph_create(n, dev(src), dev(dst))
+    D = tp.tpconv_so2_rotations(lmax, dev(vec))
+    gD = tp.tpconv_so2_frames_backward(g, lmax, C, dev(x), D, dev(w), dev(G))
+    gv = tp.tpconv_so2_rotations_backward(lmax, dev(vec), gD)
+    torch.cuda.synchronize()
+    Dn, gDn = D.cpu().numpy().astype(np.float64), gD.cpu().numpy().astype(np.float64)
+    v64 = vec.astype(np.float64)
+    errs = dict(grad_D=rel_err(gDn, so2_frames_backward(lmax, C, x, Dn, w, G, src, dst, n)),
+                grad_vec=rel_err(gv.cpu().numpy(), rotations_backward(lmax, v64, gDn)))
+    log(f"[so2] frames backward l<={lmax} C={C} E={len(src)} errors {errs}")
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)
+    # The whole chain against the oracle's own frames.  grad_vec is a
+    # cancelling contraction of grad_D (84 entries x 28 quadrature points for
+    # l <= 3), so grad_D's fp32 rounding (held to 1e-5 above) shows up larger
+    # relative to grad_vec.  The bound is that rounding carried through the
+    # (linear) rotations backward: a grad_D perturbation of 1e-6 of its RMS
+    # per entry, propagated, as an RMS, times 30 (the test takes the maximum
+    # over all components, which sits several times above an RMS).  A wrong
+    # term in the chain gives errors of the order of grad_vec itself, four
+    # orders above this bound.
+    ref_D = so2_frames_backward(lmax, C, x, edge_wigner(lmax, v64), w, G, src, dst, n)
+    chain = rotations_backward(lmax, v64, ref_D)
+    noise = rng.standard_normal(ref_D.shape) * 1e-6 * np.sqrt(np.mean(ref_D ** 2))
+    bound = 30.0 * np.sqrt(np.mean(rotations_backward(lmax, v64, noise) ** 2))
+    chain_err = float(np.max(np.abs(gv.cpu().numpy() - chain)))
+    log(f"[so2] frames backward chain l<={lmax} C={C}: max err {chain_err:.3e}, propagated-rounding bound {bound:.3e}, "
+        f"relative to rms {rel_err(gv.cpu().numpy(), chain):.3e}")
+    assert chain_err <= bound
+
+
+@pytest.mark.parametrize("name", ["c1k", "c4k"])
+def test_frames_backward_workload(tp, name):
+    """Full-size passes; grad_D and grad_vec of each edge depend on that edge
+    alone, so the oracle checks a sample of edges."""
+    import torch
+    from oracle.so2 import rotations_backward, so2_frames_backward
+    w = workloads.WORKLOADS[name]
+    lmax, C = workloads.SO2_SHAPES[name]
+    inp = workloads.make_so2_inputs(w, weight_numel(lmax, C))
+    src, dst, vec, n = inp["src"], inp["dst"], inp["vec"].astype(np.float32), inp["n_nodes"]
+    g = tp.tpconv_graph_create(n, dev(src), dev(dst))
+    D = tp.tpconv_so2_rotations(lmax, dev(vec))
+    gD = tp.tpconv_so2_frames_backward(g, lmax, C, dev(inp["x"]), D, dev(inp["weights"]), dev(inp["G"]))
+    gv = tp.tpconv_so2_rotations_backward(lmax, dev(vec), gD)
+    torch.cuda.synchronize()
+    sel = np.random.default_rng(420).choice(len(src), size=600, replace=False)
+    Dn = D.cpu().numpy()[sel].astype(np.float64)
+    gDn = gD.cpu().numpy()[sel].astype(np.float64)
+    ref_D = so2_frames_backward(lmax, C, inp["x"], Dn, inp["weights"], inp["G"], src[sel], dst[sel], n)
+    ref_v = rotations_backward(lmax, vec[sel].astype(np.float64), gDn)
+    errs = dict(grad_D=rel_err(gDn, ref_D), grad_vec=rel_err(gv.cpu().numpy()[sel], ref_v))
+    log(f"[so2] frames backward workload {name} errors {errs}")
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)
