@@ -13,7 +13,8 @@ kernel times (1 GiB read before each step), the double backward's two
 kernels (tpconv_double_backward with seeded cotangents), the upstream
 kernels (edge harmonics, their gradient, the position gradient) and the SO(2)
 convolution on the same graph (its rotations, forward, grad_x,
-map-gradient and double-backward passes, against the fp32 matrix-core peak).
+map-gradient, double-backward and frame-gradient passes, against the fp32
+matrix-core peak).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -302,7 +303,9 @@ def main():
         ggx2 = torch.randn(x2.shape, dtype=torch.float32, device=dev, generator=torch.Generator(device=dev).manual_seed(5))
         ggw2 = torch.randn(w2.shape, dtype=torch.float32, device=dev, generator=torch.Generator(device=dev).manual_seed(6))
         dd2 = [torch.empty_like(x2), torch.empty_like(w2), torch.empty_like(x2)]
-        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.so2_reps + 2)]
+        gD2 = torch.empty_like(D2)
+        gv2 = torch.empty_like(vec2)
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.so2_reps + 2)]
         for k in range(args.so2_reps + 2):   # the first two are warm-up
             sev[k][0].record(stream)
             tp.tpconv_so2_rotations(L2, vec2, D2)
@@ -316,8 +319,12 @@ def main():
             sev[k][4].record(stream)
             tp.tpconv_so2_double_backward(graph, L2, C2, x2, D2, w2, G2, ggx2, ggw2, *dd2, workspace=ws2)
             sev[k][5].record(stream)
+            tp.tpconv_so2_frames_backward(graph, L2, C2, x2, D2, w2, G2, gD2, workspace=ws2)
+            sev[k][6].record(stream)
+            tp.tpconv_so2_rotations_backward(L2, vec2, gD2, gv2)
+            sev[k][7].record(stream)
         torch.cuda.synchronize()
-        med = [float(np.median([e[i].elapsed_time(e[i + 1]) for e in sev[2:]])) for i in range(5)]
+        med = [float(np.median([e[i].elapsed_time(e[i + 1]) for e in sev[2:]])) for i in range(7)]
         fl = so2_flops_per_edge(L2, C2) * E
         tf = lambda ms: round(fl / (ms * 1e-3) / 1e12, 2)   # noqa: E731
         so2 = {"shape": f"l<={L2}, {C2} channels, {N} nodes, {E} edges, fp32",
@@ -332,8 +339,10 @@ def main():
                "fwd_bwd_edges_per_s": round(E / ((med[1] + med[2] + med[3]) * 1e-3), 1),
                "double_backward_ms_median": round(med[4], 4),
                "double_backward_TFLOPs": round(4 * fl / (med[4] * 1e-3) / 1e12, 2),
+               "frames_backward_ms_median": round(med[5], 4),
+               "rotations_backward_ms_median": round(med[6], 4),
                "reps": args.so2_reps}
-        del vec2, x2, w2, G2, D2, o2, gx2, gw2, ws2, ggx2, ggw2, dd2
+        del vec2, x2, w2, G2, D2, o2, gx2, gw2, ws2, ggx2, ggw2, dd2, gD2, gv2
 
     b = 4 if w.dtype == "f32" else 8
     fwd_bytes, bwd_bytes = algorithmic_bytes(plan, N, E, b)
