@@ -5,6 +5,11 @@
 // inside them would cost every channel lane the same ~100-500 operations per
 // edge to save 16 values of HBM traffic per edge.
 //
+// Also the SO(2) convolution's edge frames: the real Wigner blocks of each
+// edge's frame rotation (k_so2_wigner) and their gradient with respect to
+// the edge vector (k_so2_wigner_backward), both from an exact sphere
+// quadrature of the harmonics below.
+//
 // Harmonics: component-normalised real SH, Y_lm(r) = sqrt(2l+1) S_lm(r / |r|),
 // with S_lm the real solid harmonics in Racah normalisation, built by their
 // standard recurrences in l (sectoral terms from (x, y) and S_ll, S_l,-l; the

@@ -25,6 +25,10 @@
 //    results overwrite the tile at the same (+-m) places; the inverse
 //    rotation then adds each edge's message into per-lane row sums, which
 //    the two wavefronts combine once per row.  Nothing per edge reaches HBM.
+//    In the frame-gradient mode (FRAMES) the inverse rotation is replaced by
+//    a contraction of the tile (y~, or dx~ for the adjoint) with the row's
+//    own vector over channels: the two terms of the gradient with respect to
+//    each edge's Wigner blocks, recomputed rather than kept per edge.
 //  * k_so2_wgrad<L, C>: eight wavefronts share one LDS copy of the rotated x
 //    and grad_out of 16 edges; each wavefront owns a fixed set of 16 x 16
 //    output tiles of the map gradients (compile-time list, its accumulators
