@@ -269,10 +269,43 @@ __device__ __forceinline__ void gauss_legendre(int n, int i, double& x, double& 
   }
 }
 
+// The frames' quadrature, the same for every edge, built once per block in
+// LDS: point k = (iz, ip), its weight w_k / (4 pi) and the solid harmonics
+// there.
+template <int L>
+struct FrameQuad {
+  static constexpr int NZ = L + 1, NP = 2 * L + 1, NQ = NZ * NP, NS = (L + 1) * (L + 1);
+  double p[NQ][3];
+  double w[NQ];
+  double S[NQ][NS];
+};
+
+template <int L>
+__device__ __forceinline__ void frame_quad_fill(FrameQuad<L>& Q) {
+  using F = FrameQuad<L>;
+  for (int k = threadIdx.x; k < F::NQ; k += blockDim.x) {
+    const int iz = k / F::NP, ip = k - iz * F::NP;
+    double z, wz, sp, cp;
+    gauss_legendre(F::NZ, iz, z, wz);
+    const double rho = sqrt(fmax(0.0, 1.0 - z * z));
+    sincos(2.0 * M_PI * ip / F::NP, &sp, &cp);
+    Q.p[k][0] = rho * cp;
+    Q.p[k][1] = rho * sp;
+    Q.p[k][2] = z;
+    Q.w[k] = wz / (2.0 * F::NP);  // (wz * 2 pi / NP) / (4 pi)
+    double S[F::NS];
+    solid_harmonics<L, double, PlainOps<double>>(rho * cp, rho * sp, z, 1.0, 1.0, S);
+    for (int q = 0; q < F::NS; ++q) Q.S[k][q] = S[q];
+  }
+  __syncthreads();
+}
+
 template <typename T, int L>
 __global__ __launch_bounds__(64) void k_so2_wigner(int64_t n, const T* __restrict__ vec, T* __restrict__ D) {
   constexpr int NS = (L + 1) * (L + 1);
   constexpr int ND = (L + 1) * (2 * L + 1) * (2 * L + 3) / 3;
+  __shared__ FrameQuad<L> Q;
+  frame_quad_fill<L>(Q);
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= n) return;
   double ux, uy, uz;
@@ -295,22 +328,16 @@ __global__ __launch_bounds__(64) void k_so2_wigner(int64_t n, const T* __restric
   }
   double acc[ND];
   for (int q = 0; q < ND; ++q) acc[q] = 0.0;
-  constexpr int NZ = L + 1, NP = 2 * L + 1;
-  for (int iz = 0; iz < NZ; ++iz) {
-    double z, wz;
-    gauss_legendre(NZ, iz, z, wz);
-    const double rho = sqrt(fmax(0.0, 1.0 - z * z));
-    for (int ip = 0; ip < NP; ++ip) {
-      double sp, cp;
-      sincos(2.0 * M_PI * ip / NP, &sp, &cp);
-      const double px = rho * cp, py = rho * sp;
+  for (int k = 0; k < FrameQuad<L>::NQ; ++k) {
+    {
+      const double px = Q.p[k][0], py = Q.p[k][1], z = Q.p[k][2];
       const double qx = R[0][0] * px + R[0][1] * py + R[0][2] * z;
       const double qy = R[1][0] * px + R[1][1] * py + R[1][2] * z;
       const double qz = R[2][0] * px + R[2][1] * py + R[2][2] * z;
-      double Sp[NS], Sq[NS];
-      solid_harmonics<L, double, PlainOps<double>>(px, py, z, 1.0, 1.0, Sp);
+      const double* Sp = Q.S[k];
+      double Sq[NS];
       solid_harmonics<L, double, PlainOps<double>>(qx, qy, qz, 1.0, 1.0, Sq);
-      const double w = wz / (2.0 * NP);  // (wz * 2 pi / NP) / (4 pi)
+      const double w = Q.w[k];
       sh_for<L + 1>([&](auto IL) {
         constexpr int l = IL, n2 = 2 * l + 1, off = l * (2 * l - 1) * (2 * l + 1) / 3;
         const double wl = w * n2;  // Y = sqrt(2l+1) S on the unit sphere
@@ -352,6 +379,8 @@ __global__ __launch_bounds__(64) void k_so2_wigner_backward(int64_t n, const T* 
   using D3 = Dual<double>;
   constexpr int NS = (L + 1) * (L + 1);
   constexpr int ND = (L + 1) * (2 * L + 1) * (2 * L + 3) / 3;
+  __shared__ FrameQuad<L> Q;
+  frame_quad_fill<L>(Q);
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= n) return;
   const double vx = vec[3 * e], vy = vec[3 * e + 1], vz = vec[3 * e + 2];
@@ -378,23 +407,16 @@ __global__ __launch_bounds__(64) void k_so2_wigner_backward(int64_t n, const T* 
   double g[ND];
   for (int q = 0; q < ND; ++q) g[q] = gD[e * ND + q];
   double gx = 0.0, gy = 0.0, gz = 0.0;
-  constexpr int NZ = L + 1, NP = 2 * L + 1;
-  for (int iz = 0; iz < NZ; ++iz) {
-    double z, wz;
-    gauss_legendre(NZ, iz, z, wz);
-    const double rho = sqrt(fmax(0.0, 1.0 - z * z));
-    for (int ip = 0; ip < NP; ++ip) {
-      double sp, cp;
-      sincos(2.0 * M_PI * ip / NP, &sp, &cp);
-      const double p[3] = {rho * cp, rho * sp, z};
+  for (int k = 0; k < FrameQuad<L>::NQ; ++k) {
+    {
+      const double p[3] = {Q.p[k][0], Q.p[k][1], Q.p[k][2]};
       D3 q[3];
       for (int a = 0; a < 3; ++a) q[a] = dsum(dsum(dscale(p[0], R[a][0]), dscale(p[1], R[a][1])), dscale(p[2], R[a][2]));
       const D3 q2 = dsum(dsum(dmul(q[0], q[0]), dmul(q[1], q[1])), dmul(q[2], q[2]));
-      double Sp[NS];
+      const double* Sp = Q.S[k];
       D3 Sq[NS];
-      solid_harmonics<L, double, PlainOps<double>>(p[0], p[1], p[2], 1.0, 1.0, Sp);
       solid_harmonics<L, D3, DualOps<double>>(q[0], q[1], q[2], q2, D3{1.0, 0.0, 0.0, 0.0}, Sq);
-      const double w = wz / (2.0 * NP);
+      const double w = Q.w[k];
       sh_for<L + 1>([&](auto IL) {
         constexpr int l = IL, n2 = 2 * l + 1, off = l * (2 * l - 1) * (2 * l + 1) / 3;
         const double wl = w * n2;
