@@ -815,8 +815,8 @@ struct BwdDD {
   static constexpr int NL = (L + 1) * (L + 1);
   static constexpr int NT = triple_count(L);
 
-  template <bool kLate, int NV>
-  static __device__ __forceinline__ void edge(const KernelArgs& a, int tok, const T (&x)[NL], const T (&xa)[NL],
+  template <bool kLate, int NV, class XR>
+  static __device__ __forceinline__ void edge(const KernelArgs& a, int tok, const XR& x, const XR& xa,
                                               const T (&y)[NL], const T (&yb)[NL], const T (&g)[NL],
                                               const T (&w)[NT], const T (&wc)[NT], T (&dxe)[NL], T (&dya)[NV],
                                               bool store_dw, T* dwr, T (&dwv)[NT]) {
@@ -973,10 +973,28 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
     // wait for the row here, before any dW / dY store is in flight
     static_for<NL>([&](auto I) { pin_vgpr(v[I]); });
   };
-  T x[NL];
-  T xa[DD ? NL : 1];
-  load_row(X, true, x);
-  if constexpr (DD) load_row(XA, XA != nullptr, xa);
+  // For the fp64 l >= 4 double backward the row's x and a live in a per-wave
+  // LDS slab (lane-major) instead of registers: its per-edge state otherwise
+  // spills to scratch, and the spills reached HBM.  (Whole rows only: the
+  // split-row kernels need their LDS to combine the row.)
+  constexpr bool kXLds = DD && sizeof(T) == 8 && L >= 4 && R == 1;
+  __shared__ T s_xrow[kXLds ? 4 : 1][2][kXLds ? NL : 1][64];
+  T x[kXLds ? 1 : NL];
+  T xa[(DD && !kXLds) ? NL : 1];
+  if constexpr (kXLds) {
+    T t[NL];
+    load_row(X, true, t);
+    static_for<NL>([&](auto I) { s_xrow[wave][0][I][lane] = t[I]; });
+    load_row(XA, XA != nullptr, t);
+    static_for<NL>([&](auto I) { s_xrow[wave][1][I][lane] = t[I]; });
+  } else {
+    load_row(X, true, x);
+    if constexpr (DD) load_row(XA, XA != nullptr, xa);
+  }
+  struct LdsRow {
+    const T* p;
+    __device__ __forceinline__ T operator[](int i) const { return p[i * 64]; }
+  };
   // The fp32 l = 3 double backward over whole rows with a compile-time
   // table (kLate) keeps an edge's grad_W and grad_Y values until the next
   // edge's loads are issued (store_pending below): those loads then sit
@@ -1085,7 +1103,11 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
     const bool store_dw = DW != nullptr;
     T* dwr = store_dw ? DW + (int64_t)e * wstride + uc : nullptr;
     const bool st = store_dw && chan_ok && valid;
-    if constexpr (DD)
+    if constexpr (DD && kXLds)
+      BD::template edge<kLate>(a, __builtin_amdgcn_readfirstlane(e), LdsRow{&s_xrow[wave][0][0][lane]},
+                               LdsRow{&s_xrow[wave][1][0][lane]}, in.y, in.yb, in.g, in.w, in.wc, dxe, dya, st, dwr,
+                               pd.dw);
+    else if constexpr (DD)
       BD::template edge<kLate>(a, __builtin_amdgcn_readfirstlane(e), x, xa, in.y, in.yb, in.g, in.w, in.wc, dxe,
                                dya, st, dwr, pd.dw);
     else
