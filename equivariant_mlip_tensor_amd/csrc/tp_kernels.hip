@@ -291,6 +291,38 @@ struct TabInfo {
       if (tab.e[j].m3 == m) return true;
     return false;
   }
+  // A path with an l = 0 leg couples by one coefficient c for every m:
+  // (l, 0, l) as c x[m] Y0, (0, l, l) as c x0 Y[m] (the identity, c = 1), and
+  // (l, l, 0) as c times the dot product x . Y.  kDiag: 1, 2, 3 for these
+  // forms, 0 for any other path (or a table not of that form).  The table's
+  // fp64 values carry the builder's rounding (0.99999999999999978 for 1), so
+  // magnitudes are compared to 1e-14 relative, and the identity uses c = 1.
+  static constexpr bool near(double a, double b) {
+    const double d = a > b ? a - b : b - a;
+    return d <= 1e-14 * (a > 0 ? a : -a);
+  }
+  static constexpr int diag_kind() {
+    const int kind = L2 == 0 ? 1 : L1 == 0 ? 2 : L3 == 0 ? 3 : 0;
+    if (kind == 0) return 0;
+    const int l = kind == 2 ? L2 : L1;
+    if (tab.n != 2 * l + 1) return 0;
+    if (kind != 3 && (tab.e[0].neg || !near(tab.e[0].mag, 1.0))) return 0;
+    bool seen[2 * cg::kLMax + 1] = {};
+    for (int j = 0; j < tab.n; ++j) {
+      const cg::Entry& en = tab.e[j];
+      if (!near(en.mag, tab.e[0].mag) || en.neg != tab.e[0].neg) return 0;
+      int m = en.m1;
+      if (kind == 1 && (en.m2 != 0 || en.m1 != en.m3)) return 0;
+      if (kind == 2 && (en.m1 != 0 || en.m2 != en.m3)) return 0;
+      if (kind == 3 && (en.m3 != 0 || en.m1 != en.m2)) return 0;
+      if (kind == 2) m = en.m2;
+      if (seen[m]) return 0;
+      seen[m] = true;
+    }
+    return kind;
+  }
+  static constexpr int kDiag = diag_kind();
+  static constexpr double kDiagCoef = kDiag == 1 || kDiag == 2 ? 1.0 : tab.e[0].neg ? -tab.e[0].mag : tab.e[0].mag;
 };
 
 // The table's entries grouped by (m3, |c|), for fp64 kernels: an fp64
@@ -409,10 +441,13 @@ struct Fwd {
         constexpr int l2 = I2;
         if (!group_on<L, P, l1, l2>(a)) return;
         constexpr int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1;
+        // a group with an l = 0 leg holds the one path (l1, l2, max(l1, l2));
+        // its weight and scalar factor are folded first, so no products
+        constexpr bool kDiagGroup = (l1 == 0 || l2 == 0) && TabInfo<l1, l2, (l1 > l2 ? l1 : l2)>::kDiag != 0;
         T pr[n1 * n2];
         static_for<n1>([&](auto M1) {
           static_for<n2>([&](auto M2) {
-            if constexpr (group_uses<L, P::kPar, l1, l2>(M1, M2))
+            if constexpr (!kDiagGroup && group_uses<L, P::kPar, l1, l2>(M1, M2))
               pr[M1 * n2 + M2] = x[l1 * l1 + M1] * y[l2 * l2 + M2];
           });
         });
@@ -423,39 +458,51 @@ struct Fwd {
             if (P::template on<t>(a) && P::template run<t>(a, tok)) {
               using TI = TabInfo<l1, l2, l3>;
               constexpr int n3 = 2 * l3 + 1;
-              T z[n3];
-              if constexpr (sizeof(T) == 8) {
-                using GR = Grouped<l1, l2, l3>;
-                T acc_g = T(0);
-                static_for<GR::ord.n>([&](auto K) {
-                  constexpr cg::Entry en = TI::tab.e[GR::ord.idx[K]];
-                  const T p = pr[en.m1 * n2 + en.m2];
-                  if constexpr (GR::ord.open[K]) acc_g = p;
-                  else if constexpr (GR::ord.sub[K]) acc_g = acc_g - p;
-                  else acc_g = acc_g + p;
-                  if constexpr (GR::ord.close[K]) {
-                    constexpr T c = GR::ord.flip[K] ? T(-en.mag) : T(en.mag);
-                    if constexpr (GR::ord.first_m3[K])
-                      z[en.m3] = c * acc_g;
+              if constexpr (kDiagGroup) {
+                // (l, 0, l): te += (W c Y0) x;  (0, l, l): te += (W c x0) Y
+                static_assert(TI::kDiag == 1 || TI::kDiag == 2, "l = 0 leg without the identity form");
+                constexpr T c = T(TI::kDiagCoef);
+                const T f = w[t] * (TI::kDiag == 1 ? c * y[0] : c * x[0]);
+                static_for<n3>([&](auto M3) {
+                  const T v = TI::kDiag == 1 ? x[l1 * l1 + M3] : y[l2 * l2 + M3];
+                  if (P::template first3<t>(a)) te[l3 * l3 + M3] = f * v;
+                  else te[l3 * l3 + M3] = fmaT(f, v, te[l3 * l3 + M3]);
+                });
+              } else {
+                T z[n3];
+                if constexpr (sizeof(T) == 8) {
+                  using GR = Grouped<l1, l2, l3>;
+                  T acc_g = T(0);
+                  static_for<GR::ord.n>([&](auto K) {
+                    constexpr cg::Entry en = TI::tab.e[GR::ord.idx[K]];
+                    const T p = pr[en.m1 * n2 + en.m2];
+                    if constexpr (GR::ord.open[K]) acc_g = p;
+                    else if constexpr (GR::ord.sub[K]) acc_g = acc_g - p;
+                    else acc_g = acc_g + p;
+                    if constexpr (GR::ord.close[K]) {
+                      constexpr T c = GR::ord.flip[K] ? T(-en.mag) : T(en.mag);
+                      if constexpr (GR::ord.first_m3[K])
+                        z[en.m3] = c * acc_g;
+                      else
+                        z[en.m3] = fmaT(c, acc_g, z[en.m3]);
+                    }
+                  });
+                } else {
+                  static_for<TI::tab.n>([&](auto K) {
+                    constexpr cg::Entry en = TI::tab.e[K];
+                    constexpr T c = en.neg ? T(-en.mag) : T(en.mag);
+                    const T p = pr[en.m1 * n2 + en.m2];
+                    if constexpr (TI::first_m3(K))
+                      z[en.m3] = c * p;
                     else
-                      z[en.m3] = fmaT(c, acc_g, z[en.m3]);
-                  }
-                });
-              } else {
-                static_for<TI::tab.n>([&](auto K) {
-                  constexpr cg::Entry en = TI::tab.e[K];
-                  constexpr T c = en.neg ? T(-en.mag) : T(en.mag);
-                  const T p = pr[en.m1 * n2 + en.m2];
-                  if constexpr (TI::first_m3(K))
-                    z[en.m3] = c * p;
-                  else
-                    z[en.m3] = fmaT(c, p, z[en.m3]);
-                });
-              }
-              if (P::template first3<t>(a)) {
-                static_for<n3>([&](auto M3) { te[l3 * l3 + M3] = w[t] * z[M3]; });
-              } else {
-                static_for<n3>([&](auto M3) { te[l3 * l3 + M3] = fmaT(w[t], z[M3], te[l3 * l3 + M3]); });
+                      z[en.m3] = fmaT(c, p, z[en.m3]);
+                  });
+                }
+                if (P::template first3<t>(a)) {
+                  static_for<n3>([&](auto M3) { te[l3 * l3 + M3] = w[t] * z[M3]; });
+                } else {
+                  static_for<n3>([&](auto M3) { te[l3 * l3 + M3] = fmaT(w[t], z[M3], te[l3 * l3 + M3]); });
+                }
               }
             }
           }
@@ -739,6 +786,50 @@ struct Bwd {
   static constexpr int NL = (L + 1) * (L + 1);
   static constexpr int NT = triple_count(L);
 
+  // A path with an l = 0 leg (one coefficient c for every m, TabInfo::kDiag):
+  //   (l, 0, l): d = x . G[l3];  dW = c Y0 d;  dx += (W c Y0) G;  dY0 += W c d
+  //   (0, l, l): d = G . Y[l2];  dW = c x0 d;  dx0 += W c d;     dY += (W c x0) G
+  //   (l, l, 0): s = c G0;       dW = s x.Y;   dx += (W s) Y;    dY += (W s) x
+  // The per-entry products of the general case are not formed.
+  template <int l1, int l2, int l3, int NV>
+  static __device__ __forceinline__ void diag_path(T w, const T (&x)[NL], const T (&y)[NL], const T (&g)[NL],
+                                                   T (&dxe)[NL], T (&dya)[NV], bool first1, bool store_dw,
+                                                   T* dw_at) {
+    using TI = TabInfo<l1, l2, l3>;
+    constexpr T c = T(TI::kDiagCoef);
+    constexpr int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1;
+    auto add_dx = [&](T f, auto src_at) {
+      static_for<n1>([&](auto M) {
+        if (first1) dxe[l1 * l1 + M] = f * src_at(M);
+        else dxe[l1 * l1 + M] = fmaT(f, src_at(M), dxe[l1 * l1 + M]);
+      });
+    };
+    if constexpr (TI::kDiag == 1) {
+      T d = x[l1 * l1] * g[l3 * l3];
+      static_for<n1 - 1>([&](auto M) { d = fmaT(x[l1 * l1 + M + 1], g[l3 * l3 + M + 1], d); });
+      const T cy = c * y[0];
+      if (store_dw) __builtin_nontemporal_store(cy * d, dw_at);
+      add_dx(w * cy, [&](int m) { return g[l3 * l3 + m]; });
+      dya[0] = fmaT(w, c * d, dya[0]);
+    } else if constexpr (TI::kDiag == 2) {
+      T d = g[l3 * l3] * y[l2 * l2];
+      static_for<n2 - 1>([&](auto M) { d = fmaT(g[l3 * l3 + M + 1], y[l2 * l2 + M + 1], d); });
+      const T cd = c * d;
+      if (store_dw) __builtin_nontemporal_store(x[0] * cd, dw_at);
+      add_dx(w * cd, [&](int) { return T(1); });
+      const T f = w * (c * x[0]);
+      static_for<n2>([&](auto M) { dya[l2 * l2 + M] = fmaT(f, g[l3 * l3 + M], dya[l2 * l2 + M]); });
+    } else {
+      const T s = c * g[l3 * l3];
+      T d = x[l1 * l1] * y[l2 * l2];
+      static_for<n1 - 1>([&](auto M) { d = fmaT(x[l1 * l1 + M + 1], y[l2 * l2 + M + 1], d); });
+      if (store_dw) __builtin_nontemporal_store(s * d, dw_at);
+      const T f = w * s;
+      add_dx(f, [&](int m) { return y[l2 * l2 + m]; });
+      static_for<n2>([&](auto M) { dya[l2 * l2 + M] = fmaT(f, x[l1 * l1 + M], dya[l2 * l2 + M]); });
+    }
+  }
+
   // One edge: dW for every path, the edge's contribution dxe to dx (summed
   // over its paths), and per-lane contributions to dY (summed over channels
   // afterwards).
@@ -758,6 +849,11 @@ struct Bwd {
             if (P::template on<t>(a) && P::template run<t>(a, tok)) {
               using TI = TabInfo<l1, l2, l3>;
               constexpr int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1;
+              if constexpr (TI::kDiag != 0) {
+                diag_path<l1, l2, l3>(w[t], x, y, g, dxe, dya, P::template first1<t>(a), store_dw,
+                                      dwr + P::template woff<t>(a));
+                return;
+              }
               T dxp[n1], dyp[n2];
               static_for<TI::tab.n>([&](auto K) {
                 constexpr cg::Entry en = TI::tab.e[K];

@@ -266,7 +266,7 @@ def test_double_backward_small(tp, case, lmax, C):
         assert all(np.all(o.cpu().numpy() == 0) for o in outs)
 
 
-@pytest.mark.parametrize("name", ["c1k", "c4k"])
+@pytest.mark.parametrize("name", ["c1k", "c2k", "c4k", "c28k"])
 def test_double_backward_workload(tp, name):
     """Full-size outputs from the GPU against the oracle on sampled rows
     (grad_G, grad_x) and the map gradient against the backward's, which it
@@ -373,7 +373,7 @@ def test_frames_backward_small(tp, lmax, C):
     assert chain_err <= bound
 
 
-@pytest.mark.parametrize("name", ["c1k", "c4k"])
+@pytest.mark.parametrize("name", ["c1k", "c2k", "c4k", "c28k"])
 def test_frames_backward_workload(tp, name):
     """Full-size passes; grad_D and grad_vec of each edge depend on that edge
     alone, so the oracle checks a sample of edges."""
