@@ -530,10 +530,11 @@ struct FwdDD {
         constexpr int l2 = I2;
         if (!group_on<L, P, l1, l2>(a)) return;
         constexpr int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1;
+        constexpr bool kDiagGroup = (l1 == 0 || l2 == 0) && TabInfo<l1, l2, (l1 > l2 ? l1 : l2)>::kDiag != 0;
         T p1[n1 * n2], p2[n1 * n2];
         static_for<n1>([&](auto M1) {
           static_for<n2>([&](auto M2) {
-            if constexpr (group_uses<L, P::kPar, l1, l2>(M1, M2)) {
+            if constexpr (!kDiagGroup && group_uses<L, P::kPar, l1, l2>(M1, M2)) {
               const T xv = x[l1 * l1 + M1], yv = y[l2 * l2 + M2];
               p1[M1 * n2 + M2] = xv * yv;
               p2[M1 * n2 + M2] = fmaT(xa[l1 * l1 + M1], yv, xv * yb[l2 * l2 + M2]);
@@ -547,6 +548,24 @@ struct FwdDD {
             if (P::template on<t>(a) && P::template run<t>(a, tok)) {
               using TI = TabInfo<l1, l2, l3>;
               constexpr int n3 = 2 * l3 + 1;
+              if constexpr (kDiagGroup) {
+                // (l, 0, l): te += (W c Y0) a + (W c b0 + C c Y0) x
+                // (0, l, l): te += (W c x0) b + (W c a0 + C c x0) Y
+                static_assert(TI::kDiag == 1 || TI::kDiag == 2, "l = 0 leg without the identity form");
+                constexpr T c = T(TI::kDiagCoef);
+                constexpr bool k1 = TI::kDiag == 1;
+                const T sm = c * (k1 ? y[0] : x[0]);
+                const T so = c * (k1 ? yb[0] : xa[0]);
+                const T f1 = w[t] * sm;
+                const T f2 = fmaT(w[t], so, wc[t] * sm);
+                static_for<n3>([&](auto M3) {
+                  const T v1 = k1 ? xa[l1 * l1 + M3] : yb[l2 * l2 + M3];
+                  const T v2 = k1 ? x[l1 * l1 + M3] : y[l2 * l2 + M3];
+                  if (P::template first3<t>(a)) te[l3 * l3 + M3] = fmaT(f1, v1, f2 * v2);
+                  else te[l3 * l3 + M3] = fmaT(f1, v1, fmaT(f2, v2, te[l3 * l3 + M3]));
+                });
+                return;
+              }
               T z1[n3], z2[n3];
               if constexpr (sizeof(T) == 8) {
                 using GR = Grouped<l1, l2, l3>;  // one coefficient per (m3, |c|) group
@@ -911,6 +930,66 @@ struct BwdDD {
   static constexpr int NL = (L + 1) * (L + 1);
   static constexpr int NT = triple_count(L);
 
+  // A path with an l = 0 leg (one coefficient c for every m, TabInfo::kDiag);
+  // S is the grad_W value, returned:
+  //   (l, 0, l): dA = a . G, dX = x . G;  S = c (Y0 dA + b0 dX)
+  //              grad_x += c (W b0 + C Y0) G;           grad_Y0 += c (W dA + C dX)
+  //   (0, l, l): dY = G . Y, dB = G . b;  S = c (a0 dY + x0 dB)
+  //              grad_x0 += c (W dB + C dY);            grad_Y += c (W a0 + C x0) G
+  //   (l, l, 0): s = c G0, d = a . Y + x . b;  S = s d
+  //              grad_x += (W s) b + (C s) Y;           grad_Y += (W s) a + (C s) x
+  template <int l1, int l2, int l3, int NV, class XR>
+  static __device__ __forceinline__ T diag_path(T w, T wc, const XR& x, const XR& xa, const T (&y)[NL],
+                                                const T (&yb)[NL], const T (&g)[NL], T (&dxe)[NL], T (&dya)[NV],
+                                                bool first1) {
+    using TI = TabInfo<l1, l2, l3>;
+    constexpr T c = T(TI::kDiagCoef);
+    constexpr int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1;
+    if constexpr (TI::kDiag == 1) {
+      T dA = xa[l1 * l1] * g[l3 * l3], dX = x[l1 * l1] * g[l3 * l3];
+      static_for<n1 - 1>([&](auto M) {
+        dA = fmaT(xa[l1 * l1 + M + 1], g[l3 * l3 + M + 1], dA);
+        dX = fmaT(x[l1 * l1 + M + 1], g[l3 * l3 + M + 1], dX);
+      });
+      const T f = c * fmaT(w, yb[0], wc * y[0]);
+      static_for<n1>([&](auto M) {
+        if (first1) dxe[l1 * l1 + M] = f * g[l3 * l3 + M];
+        else dxe[l1 * l1 + M] = fmaT(f, g[l3 * l3 + M], dxe[l1 * l1 + M]);
+      });
+      dya[0] = fmaT(c, fmaT(w, dA, wc * dX), dya[0]);
+      return c * fmaT(y[0], dA, yb[0] * dX);
+    } else if constexpr (TI::kDiag == 2) {
+      T dY = g[l3 * l3] * y[l2 * l2], dB = g[l3 * l3] * yb[l2 * l2];
+      static_for<n2 - 1>([&](auto M) {
+        dY = fmaT(g[l3 * l3 + M + 1], y[l2 * l2 + M + 1], dY);
+        dB = fmaT(g[l3 * l3 + M + 1], yb[l2 * l2 + M + 1], dB);
+      });
+      const T f0 = c * fmaT(w, dB, wc * dY);
+      if (first1) dxe[0] = f0;
+      else dxe[0] = dxe[0] + f0;
+      const T f = c * fmaT(w, xa[0], wc * x[0]);
+      static_for<n2>([&](auto M) { dya[l2 * l2 + M] = fmaT(f, g[l3 * l3 + M], dya[l2 * l2 + M]); });
+      return c * fmaT(xa[0], dY, x[0] * dB);
+    } else {
+      const T sg = c * g[l3 * l3];
+      T d = x[l1 * l1] * yb[l2 * l2];
+      d = fmaT(xa[l1 * l1], y[l2 * l2], d);
+      static_for<n1 - 1>([&](auto M) {
+        d = fmaT(xa[l1 * l1 + M + 1], y[l2 * l2 + M + 1], d);
+        d = fmaT(x[l1 * l1 + M + 1], yb[l2 * l2 + M + 1], d);
+      });
+      const T f1 = w * sg, f2 = wc * sg;
+      static_for<n1>([&](auto M) {
+        if (first1) dxe[l1 * l1 + M] = fmaT(f1, yb[l2 * l2 + M], f2 * y[l2 * l2 + M]);
+        else dxe[l1 * l1 + M] = fmaT(f1, yb[l2 * l2 + M], fmaT(f2, y[l2 * l2 + M], dxe[l1 * l1 + M]));
+      });
+      static_for<n2>([&](auto M) {
+        dya[l2 * l2 + M] = fmaT(f1, xa[l1 * l1 + M], fmaT(f2, x[l1 * l1 + M], dya[l2 * l2 + M]));
+      });
+      return sg * d;
+    }
+  }
+
   template <bool kLate, int NV, class XR>
   static __device__ __forceinline__ void edge(const KernelArgs& a, int tok, const XR& x, const XR& xa,
                                               const T (&y)[NL], const T (&yb)[NL], const T (&g)[NL],
@@ -928,6 +1007,14 @@ struct BwdDD {
             if (P::template on<t>(a) && P::template run<t>(a, tok)) {
               using TI = TabInfo<l1, l2, l3>;
               constexpr int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1;
+              if constexpr (TI::kDiag != 0) {
+                const T sd = diag_path<l1, l2, l3>(w[t], wc[t], x, xa, y, yb, g, dxe, dya, P::template first1<t>(a));
+                if constexpr (kLate)
+                  dwv[t] = sd;
+                else if (store_dw)
+                  __builtin_nontemporal_store(sd, dwr + P::template woff<t>(a));
+                return;
+              }
               T dxp[n1], dxq[n1], xt[n1], dyt[n2];
               static_for<n1>([&](auto M1) {
                 if constexpr (TI::has_m1(M1)) xt[M1] = fmaT(w[t], xa[l1 * l1 + M1], wc[t] * x[l1 * l1 + M1]);
