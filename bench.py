@@ -25,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -85,11 +86,20 @@ def so2_flops_per_edge(lmax, C):
     return 2 * (ks[0] ** 2 + 4 * sum(k * k for k in ks[1:]))
 
 
+def strip_comments(text):
+    """C++ source without its comments, trailing blanks and blank lines."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def kernel_source_hash():
+    """Hash of the kernel sources' code (comments removed: the counters depend
+    on what is compiled, not on how it is annotated)."""
     h = hashlib.sha256()
     for f in ("tp_kernels.hip", "cg_real.hpp", "tp_common.hpp"):
-        with open(os.path.join(ROOT, "equivariant_mlip_tensor_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "equivariant_mlip_tensor_amd", "csrc", f)) as fh:
+            h.update(strip_comments(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

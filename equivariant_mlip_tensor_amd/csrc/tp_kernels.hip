@@ -549,8 +549,9 @@ struct FwdDD {
               using TI = TabInfo<l1, l2, l3>;
               constexpr int n3 = 2 * l3 + 1;
               if constexpr (kDiagGroup) {
-                // (l, 0, l): te += (W c Y0) a + (W c b0 + C c Y0) x
-                // (0, l, l): te += (W c x0) b + (W c a0 + C c x0) Y
+                // with k the path's coefficient and c the weight cotangent:
+                // (l, 0, l): te += (W k Y0) a + (W k b0 + c k Y0) x
+                // (0, l, l): te += (W k x0) b + (W k a0 + c k x0) Y
                 static_assert(TI::kDiag == 1 || TI::kDiag == 2, "l = 0 leg without the identity form");
                 constexpr T c = T(TI::kDiagCoef);
                 constexpr bool k1 = TI::kDiag == 1;
@@ -930,13 +931,13 @@ struct BwdDD {
   static constexpr int NL = (L + 1) * (L + 1);
   static constexpr int NT = triple_count(L);
 
-  // A path with an l = 0 leg (one coefficient c for every m, TabInfo::kDiag);
-  // S is the grad_W value, returned:
-  //   (l, 0, l): dA = a . G, dX = x . G;  S = c (Y0 dA + b0 dX)
-  //              grad_x += c (W b0 + C Y0) G;           grad_Y0 += c (W dA + C dX)
-  //   (0, l, l): dY = G . Y, dB = G . b;  S = c (a0 dY + x0 dB)
-  //              grad_x0 += c (W dB + C dY);            grad_Y += c (W a0 + C x0) G
-  //   (l, l, 0): s = c G0, d = a . Y + x . b;  S = s d
+  // A path with an l = 0 leg (one coefficient k for every m, TabInfo::kDiag;
+  // C the weight cotangent); S is the grad_W value, returned:
+  //   (l, 0, l): dA = a . G, dX = x . G;  S = k (Y0 dA + b0 dX)
+  //              grad_x += k (W b0 + C Y0) G;           grad_Y0 += k (W dA + C dX)
+  //   (0, l, l): dY = G . Y, dB = G . b;  S = k (a0 dY + x0 dB)
+  //              grad_x0 += k (W dB + C dY);            grad_Y += k (W a0 + C x0) G
+  //   (l, l, 0): s = k G0, d = a . Y + x . b;  S = s d
   //              grad_x += (W s) b + (C s) Y;           grad_Y += (W s) a + (C s) x
   template <int l1, int l2, int l3, int NV, class XR>
   static __device__ __forceinline__ T diag_path(T w, T wc, const XR& x, const XR& xa, const T (&y)[NL],

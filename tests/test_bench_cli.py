@@ -28,3 +28,16 @@ def test_algorithmic_bytes_of_the_4096_atom_workload():
     ddf, ddb = bench.dd_algorithmic_bytes(P, 4096, 214648, 4)
     assert ddf == 214648 * ((2 * 736 + 32) * 4 + 4) + 4096 * (1536 * 4 + 4)
     assert ddb == 214648 * ((3 * 736 + 48) * 4 + 8) + 4096 * (2048 * 4 + 4)
+
+
+def test_kernel_source_hash_ignores_comments():
+    """The counters' key covers the compiled code only: comments, trailing
+    blanks and blank lines do not change it; a code change does."""
+    sys.path.insert(0, ROOT)
+    import bench
+    code = "int f(int a) {\n  return a + 1;\n}\n"
+    annotated = "// adds one\nint f(int a) {  /* the\n argument */\n\n  return a + 1;   // here\n}\n"
+    assert bench.strip_comments(code) == bench.strip_comments(annotated)
+    assert bench.strip_comments(code) != bench.strip_comments(code.replace("+ 1", "+ 2"))
+    h = bench.kernel_source_hash()
+    assert len(h) == 16 and h == bench.kernel_source_hash()
