@@ -133,6 +133,11 @@ def test_real_cg_known_patterns():
         np.testing.assert_allclose(cg_real(0, l, l)[0], np.eye(2 * l + 1), atol=1e-15)
     # 1 x 1 -> 0 is -1/sqrt(3) times the identity (a dot product)
     np.testing.assert_allclose(cg_real(1, 1, 0)[:, :, 0], -np.eye(3) / sqrt(3), atol=1e-15)
+    # l x l -> 0 in general: one coefficient (-1)^l / sqrt(2l+1) on the diagonal,
+    # from <l m l -m|0 0> = (-1)^(l-m) / sqrt(2l+1) and the unitarity of U
+    for l in range(5):
+        np.testing.assert_allclose(cg_real(l, l, 0)[:, :, 0], (-1) ** l * np.eye(2 * l + 1) / sqrt(2 * l + 1),
+                                   atol=1e-15)
     # 1 x 1 -> 1 (odd sum) is a cross product: components ordered (y, z, x)
     C = cg_real(1, 1, 1)
     rng = np.random.default_rng(0)
