@@ -432,10 +432,7 @@ struct Fwd {
   static constexpr int NL = (L + 1) * (L + 1);
   static constexpr int NT = triple_count(L);
 
-  // te[l3 block] (+)= sum over the edge's paths into l3 of W[p,u] * CG_p(x, y):
-  // kAcc adds into te (a running sum over edges), else the first path into
-  // each l3 sets it
-  template <bool kAcc = false>
+  // te[l3 block] = sum over the edge's paths into l3 of W[p,u] * CG_p(x, y)
   static __device__ __forceinline__ void edge(const KernelArgs& a, int tok, const T (&x)[NL], const T (&y)[NL],
                                               const T (&w)[NT], T (&te)[NL]) {
     static_for<L + 1>([&](auto I1) {
@@ -468,7 +465,7 @@ struct Fwd {
                 const T f = w[t] * (TI::kDiag == 1 ? c * y[0] : c * x[0]);
                 static_for<n3>([&](auto M3) {
                   const T v = TI::kDiag == 1 ? x[l1 * l1 + M3] : y[l2 * l2 + M3];
-                  if (!kAcc && P::template first3<t>(a)) te[l3 * l3 + M3] = f * v;
+                  if (P::template first3<t>(a)) te[l3 * l3 + M3] = f * v;
                   else te[l3 * l3 + M3] = fmaT(f, v, te[l3 * l3 + M3]);
                 });
               } else {
@@ -501,7 +498,7 @@ struct Fwd {
                       z[en.m3] = fmaT(c, p, z[en.m3]);
                   });
                 }
-                if (!kAcc && P::template first3<t>(a)) {
+                if (P::template first3<t>(a)) {
                   static_for<n3>([&](auto M3) { te[l3 * l3 + M3] = w[t] * z[M3]; });
                 } else {
                   static_for<n3>([&](auto M3) { te[l3 * l3 + M3] = fmaT(w[t], z[M3], te[l3 * l3 + M3]); });
@@ -681,11 +678,10 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
   const int d_in = P::d_in(a), d_sh = P::d_sh(a);
   const int64_t wstride = P::wstride(a);
 
-  // Row sum.  fp64 data: fp64 registers.  fp32 data: the edges' path terms
-  // are summed in fp32 into acc for kFlush edges at a time (the forward FMAs
-  // each path straight into acc; the double backward's grad_G adds each
-  // edge's sum te), and acc is then added into an fp64 row sum kept in LDS
-  // (one slab per wave, lane-major), which costs no VGPRs.
+  // Row sum.  fp64 data: fp64 registers.  fp32 data: each edge's path sum
+  // te is added in fp32 into acc for kFlush edges at a time, and acc is then
+  // added into an fp64 row sum kept in LDS (one slab per wave, lane-major),
+  // which costs no VGPRs.
   constexpr bool kLdsRow = !std::is_same<T, A>::value || row_sum_in_lds<T, L, DD>();
   constexpr bool kSlab = kLdsRow || R > 1;  // per-wave fp64 row slabs in LDS
   constexpr int kFlush = std::is_same<T, A>::value ? 1 : 4;  // fp64 data: straight into the slab
@@ -747,8 +743,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
     load_x(X, x);
     load_y(Yp, y);
     load_w<T, L, P>(a, Wp, wstride, uc, e, w);
+    T te[NL];
     if constexpr (DD) {
-      T te[NL];
       T xa[NL], yb[NL], wc[NT];
       if (XA != nullptr) load_x(XA, xa);
       else static_for<NL>([&](auto I) { xa[I] = T(0); });
@@ -757,15 +753,15 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
       if (WC != nullptr) load_w<T, L, P>(a, WC, wstride, uc, e, wc);
       else static_for<NT>([&](auto I) { wc[I] = T(0); });
       FD::edge(a, __builtin_amdgcn_readfirstlane(e), x, xa, y, yb, w, wc, te);
-      static_for<L + 1>([&](auto I) {
-        constexpr int l = I;
-        if (P::out_l(a, l)) {
-          static_for<2 * l + 1>([&](auto M) { acc[l * l + M] += te[l * l + M]; });
-        }
-      });
     } else {
-      F::template edge<true>(a, __builtin_amdgcn_readfirstlane(e), x, y, w, acc);  // paths straight into acc
+      F::edge(a, __builtin_amdgcn_readfirstlane(e), x, y, w, te);
     }
+    static_for<L + 1>([&](auto I) {
+      constexpr int l = I;
+      if (P::out_l(a, l)) {
+        static_for<2 * l + 1>([&](auto M) { acc[l * l + M] += te[l * l + M]; });
+      }
+    });
     if (it % kFlush == kFlush - 1) flush();
     }
   }
