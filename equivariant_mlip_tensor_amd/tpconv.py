@@ -15,6 +15,7 @@ The layouts are those of include/tpconv.h.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional, Tuple
 
@@ -106,6 +107,21 @@ def _stream_handle(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on_launch_stream(fn):
+    """Run a wrapper with its launch stream current, so the outputs and
+    workspaces it allocates come from that stream's pool: torch's caching
+    allocator does not hand such a block to other work before what was queued
+    on that stream has passed (a workspace freed when the wrapper returns may
+    still be in use by the kernels it launched)."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, **kw)
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kw)
+    return wrapper
+
+
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -179,6 +195,7 @@ class Graph:
             _lib.tpconv_graph_destroy(h)
 
 
+@_on_launch_stream
 def tpconv_graph_create(n_nodes: int, src: torch.Tensor, dst: torch.Tensor, workspace: Optional[torch.Tensor] = None,
                         stream=None) -> Graph:
     if src.dtype != torch.int32 or dst.dtype != torch.int32 or not src.is_cuda or not dst.is_cuda:
@@ -197,6 +214,7 @@ def tpconv_graph_create(n_nodes: int, src: torch.Tensor, dst: torch.Tensor, work
     return Graph(h, workspace, int(n_nodes), int(n_edges))
 
 
+@_on_launch_stream
 def tpconv_graph_export(graph: Graph, stream=None):
     """Host copies (numpy int32) of dst_row_ptr, dst_col, dst_eid, src_row_ptr, src_col, src_eid."""
     import numpy as np
@@ -222,6 +240,7 @@ def _need(t, shape, dtype, name):
     return t
 
 
+@_on_launch_stream
 def tpconv_forward(plan: Plan, graph: Graph, x, Y, W, out=None, stream=None) -> torch.Tensor:
     N, E, dt = graph.n_nodes, graph.n_edges, plan.torch_dtype
     _need(x, (N, plan.dim_in), dt, "x")
@@ -235,6 +254,7 @@ def tpconv_forward(plan: Plan, graph: Graph, x, Y, W, out=None, stream=None) -> 
     return out
 
 
+@_on_launch_stream
 def tpconv_backward(plan: Plan, graph: Graph, x, Y, W, grad_out, grad_x=None, grad_Y=None, grad_W=None,
                     need=(True, True, True), stream=None) -> Tuple[Optional[torch.Tensor], ...]:
     """Returns (grad_x, grad_Y, grad_W); an output is None when `need` turns it off."""
@@ -259,6 +279,7 @@ def tpconv_backward(plan: Plan, graph: Graph, x, Y, W, grad_out, grad_x=None, gr
     return grad_x, grad_Y, grad_W
 
 
+@_on_launch_stream
 def tpconv_double_backward(plan: Plan, graph: Graph, x, Y, W, grad_out, ggx=None, ggY=None, ggW=None,
                            grad_x=None, grad_Y=None, grad_W=None, grad_G=None,
                            need=(True, True, True, True), stream=None) -> Tuple[Optional[torch.Tensor], ...]:
@@ -292,6 +313,7 @@ def tpconv_double_backward(plan: Plan, graph: Graph, x, Y, W, grad_out, ggx=None
 
 
 # ------------------------------------------------- upstream: harmonics, forces
+@_on_launch_stream
 def tpconv_sh(plan: Plan, vec, Y=None, stream=None) -> torch.Tensor:
     """Y [E, (sh_lmax+1)^2] of the edge vectors vec [E, 3] (plan dtype)."""
     E = vec.shape[0] if vec.dim() == 2 else -1
@@ -303,6 +325,7 @@ def tpconv_sh(plan: Plan, vec, Y=None, stream=None) -> torch.Tensor:
     return Y
 
 
+@_on_launch_stream
 def tpconv_sh_backward(plan: Plan, vec, grad_Y, grad_vec=None, stream=None) -> torch.Tensor:
     """grad_vec [E, 3] from grad_Y [E, (sh_lmax+1)^2]."""
     E = vec.shape[0] if vec.dim() == 2 else -1
@@ -315,6 +338,7 @@ def tpconv_sh_backward(plan: Plan, vec, grad_Y, grad_vec=None, stream=None) -> t
     return grad_vec
 
 
+@_on_launch_stream
 def tpconv_positions_backward(plan: Plan, graph: Graph, grad_vec, grad_pos=None, stream=None) -> torch.Tensor:
     """grad_pos [N, 3] for vec[e] = pos[src[e]] - pos[dst[e]] (+ constant shift)."""
     N, E = graph.n_nodes, graph.n_edges
@@ -340,6 +364,7 @@ def _so2_sizes(lmax, channels):
     return channels * (lmax + 1) ** 2, (lmax + 1) * (2 * lmax + 1) * (2 * lmax + 3) // 3, nw
 
 
+@_on_launch_stream
 def tpconv_so2_rotations(lmax: int, vec, D=None, stream=None) -> torch.Tensor:
     """D [E, sum_l (2l+1)^2]: real Wigner blocks of each edge's frame rotation
     (dtype of vec, float32 or float64)."""
@@ -355,6 +380,7 @@ def tpconv_so2_rotations(lmax: int, vec, D=None, stream=None) -> torch.Tensor:
     return D
 
 
+@_on_launch_stream
 def tpconv_so2_forward(graph: Graph, lmax: int, channels: int, x, D, weights, out=None, stream=None) -> torch.Tensor:
     """out [N, C (L+1)^2] = sum over in-edges of D^T SO2(D x[src])."""
     N, E = graph.n_nodes, graph.n_edges
@@ -375,6 +401,7 @@ def tpconv_so2_workspace_bytes(lmax: int, channels: int, n_edges: int) -> int:
     return int(_lib.tpconv_so2_workspace_bytes(int(lmax), int(channels), int(n_edges)))
 
 
+@_on_launch_stream
 def tpconv_so2_backward(graph: Graph, lmax: int, channels: int, x, D, weights, grad_out, grad_x=None,
                         grad_weights=None, workspace=None, need=(True, True),
                         stream=None) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
@@ -407,6 +434,7 @@ def tpconv_so2_backward(graph: Graph, lmax: int, channels: int, x, D, weights, g
     return grad_x, grad_weights
 
 
+@_on_launch_stream
 def tpconv_so2_double_backward(graph: Graph, lmax: int, channels: int, x, D, weights, grad_out, ggx=None, ggw=None,
                                grad_x=None, grad_weights=None, grad_G=None, workspace=None,
                                need=(True, True, True), stream=None):
@@ -446,6 +474,7 @@ def tpconv_so2_double_backward(graph: Graph, lmax: int, channels: int, x, D, wei
     return tuple(outs)
 
 
+@_on_launch_stream
 def tpconv_so2_frames_backward(graph: Graph, lmax: int, channels: int, x, D, weights, grad_out, grad_D=None,
                                workspace=None, stream=None) -> torch.Tensor:
     """grad_D [E, sum (2l+1)^2]: gradient of <grad_out, out> with respect to the Wigner blocks."""
@@ -468,6 +497,7 @@ def tpconv_so2_frames_backward(graph: Graph, lmax: int, channels: int, x, D, wei
     return grad_D
 
 
+@_on_launch_stream
 def tpconv_so2_rotations_backward(lmax: int, vec, grad_D, grad_vec=None, stream=None) -> torch.Tensor:
     """grad_vec [E, 3] from grad_D [E, sum (2l+1)^2] (dtype of vec)."""
     E = vec.shape[0] if vec.dim() == 2 else -1

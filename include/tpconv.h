@@ -45,9 +45,10 @@
  *    atomics, so repeated calls give bitwise identical outputs.
  *
  * Kernel coverage: every irreps string may hold each l at most once, all
- * segments of irreps_in and irreps_out share one multiplicity U (any
- * U >= 1), and every l (inputs, outputs, SH) is at most TPCONV_MAX_L.
- * Other plans are rejected with TPCONV_E_UNSUPPORTED.
+ * segments of irreps_in and irreps_out share one multiplicity U with
+ * 1 <= U <= 64 (one 64-lane wavefront holds a channel per lane), and every l
+ * (inputs, outputs, SH) is at most TPCONV_MAX_L.  Other plans are rejected
+ * with TPCONV_E_UNSUPPORTED.
  */
 #ifndef TPCONV_H
 #define TPCONV_H
@@ -69,7 +70,7 @@ typedef enum {
   TPCONV_OK = 0,
   TPCONV_E_INVALID_ARG = 1, /* NULL pointer, negative size, bad dtype, size mismatch */
   TPCONV_E_IRREPS = 2,      /* irreps string does not parse */
-  TPCONV_E_UNSUPPORTED = 3, /* l > TPCONV_MAX_L, repeated l, unequal multiplicities */
+  TPCONV_E_UNSUPPORTED = 3, /* l > TPCONV_MAX_L, repeated l, unequal multiplicities, U > 64 */
   TPCONV_E_NO_PATHS = 4,    /* no admissible (s1, l2, s3) path */
   TPCONV_E_WORKSPACE = 5,   /* graph workspace too small or misaligned */
   TPCONV_E_INDEX = 6,       /* some src/dst index outside [0, n_nodes) */

@@ -232,6 +232,41 @@ def so2_backward(lmax, C, x, D, weights, G, src, dst, n_nodes):
     return grad_x, gw
 
 
+def so2_weight_grad_entries(lmax, C, x, D, G, src, dst, idx):
+    """Selected entries of so2_backward's grad_weights (flat indices idx into
+    the weights' layout), each evaluated from its definition over all edges.
+    With o = (lo - m) C + co and i = (li - m) C + ci the block's row and
+    column, g~ = D_e G[dst e] and x~ = D_e x[src e]:
+        A_0[o, i] = sum_e g~[lo][co][0] x~[li][ci][0]
+        A_m[o, i] = sum_e g~[lo][co][+m] x~[li][ci][+m] + g~[lo][co][-m] x~[li][ci][-m]
+        B_m[o, i] = sum_e g~[lo][co][-m] x~[li][ci][+m] - g~[lo][co][+m] x~[li][ci][-m]
+    (m indexed -l..l).  Only the one channel block of G and of x that the
+    entry touches is rotated, so an entry costs O(E) and any entry can be
+    checked at any graph size."""
+    x = np.asarray(x, dtype=np.float64)
+    G = np.asarray(G, dtype=np.float64)
+    src, dst = np.asarray(src, np.int64), np.asarray(dst, np.int64)
+    Dl = unpack_D(D, lmax)
+    blocks = weight_blocks(lmax, C)
+
+    def rotated(V, nodes, l, c, mm):
+        cols = V[:, C * l * l + c * (2 * l + 1):C * l * l + (c + 1) * (2 * l + 1)][nodes]   # [E, 2l+1]
+        return np.einsum("en,en->e", Dl[l][:, l + mm, :], cols)
+
+    out = np.zeros(len(idx))
+    for t, j in enumerate(idx):
+        name, m, off, K = next(b for b in blocks if b[2] <= j < b[2] + b[3] * b[3])
+        o, i = divmod(int(j) - off, K)
+        lo, co, li, ci = m + o // C, o % C, m + i // C, i % C
+        if m == 0:
+            out[t] = rotated(G, dst, lo, co, 0) @ rotated(x, src, li, ci, 0)
+            continue
+        gp, gm = rotated(G, dst, lo, co, m), rotated(G, dst, lo, co, -m)
+        xp, xm = rotated(x, src, li, ci, m), rotated(x, src, li, ci, -m)
+        out[t] = gp @ xp + gm @ xm if name == "A" else gm @ xp - gp @ xm
+    return out
+
+
 def so2_double_backward(lmax, C, x, D, weights, G, ggx, ggw, src, dst, n_nodes):
     """Gradients of L2 = <ggx, grad_x> + <ggw, grad_w>, where (grad_x, grad_w)
     = so2_backward(x, weights, G), with respect to x, the weights and G (the

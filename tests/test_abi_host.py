@@ -106,11 +106,16 @@ def test_survey_sizes(tp):
     ("4x1o+4x1o", 1, "4x1o", "f32", "TPCONV_E_UNSUPPORTED"),
     ("4x0e", 1, "8x1o", "f32", "TPCONV_E_UNSUPPORTED"),
     ("128x0e", 0, "128x0e", "f32", "TPCONV_E_UNSUPPORTED"),
+    ("65x0e+65x1o", 1, "65x0e+65x1o", "f32", "TPCONV_E_UNSUPPORTED"),   # U past one wavefront
+    ("64x0e+64x1o", 1, "64x0e", "f32", None),                             # U = 64 is the last one taken
     ("1x0e", 1, "1x2e", "f32", "TPCONV_E_NO_PATHS"),
     ("1x0e", -1, "1x0e", "f32", "TPCONV_E_INVALID_ARG"),
     ("1x0e", 0, "1x0e", 7, "TPCONV_E_INVALID_ARG"),
 ])
 def test_plan_errors(tp, irr_in, lsh, irr_out, dt, status):
+    if status is None:
+        assert tp.tpconv_plan(irr_in, lsh, irr_out, dt).mul == 64
+        return
     with pytest.raises(tp.TPConvError) as ei:
         tp.tpconv_plan(irr_in, lsh, irr_out, dt)
     assert ei.value.name == status

@@ -196,14 +196,19 @@ def test_isolated_duplicate_shuffled(tp):
     assert np.all(out[7] == 0) and np.all(dx[9] == 0) and np.all(out[40] == 0) and np.all(dx[40] == 0)
 
 
-def test_hub_node(tp):
+@pytest.mark.parametrize("spec", [
+    ("16x0e+16x1o+16x2e+16x3o", 3, "16x0e+16x1o+16x2e+16x3o", "f32"),   # vector kernels
+    ("32x0e+32x1o+32x2e+32x3o", 3, "32x0e+32x1o+32x2e+32x3o", "f32"),   # forward on the matrix cores
+    ("32x0e+32x1o+32x2e", 2, "32x0e+32x1o+32x2e", "f32"),
+])
+def test_hub_node(tp, spec):
     rng = np.random.default_rng(4)
     n = 1600
     src = np.concatenate([np.arange(1, n), rng.integers(0, n, 500)]).astype(np.int32)
     dst = np.concatenate([np.zeros(n - 1, np.int32), rng.integers(0, n, 500)]).astype(np.int32)
     src = np.concatenate([src, np.zeros(1200, np.int32)])    # and a source hub
     dst = np.concatenate([dst, rng.integers(0, n, 1200).astype(np.int32)])
-    check_full(tp, ("16x0e+16x1o+16x2e+16x3o", 3, "16x0e+16x1o+16x2e+16x3o", "f32"), n, src, dst, label="hub")
+    check_full(tp, spec, n, src, dst, label="hub")
 
 
 @pytest.mark.parametrize("spec", [

@@ -5,12 +5,14 @@ fp32 (1e-11 for the fp64 rotations).  The convolution tests hand the GPU's own
 fp32 Wigner blocks (upcast) to the oracle, so they measure the convolution
 alone; the chain tests let the oracle build its blocks from the edge vectors.
 
-Sizes: every workload graph.  Where the oracle would be slow (the 214k- and
-1.47M-edge graphs) it checks sampled rows -- the out rows of sampled centres
-from their in-edges, the grad_x rows of sampled neighbours from their
-out-edges -- and the map gradients are checked by the identity
-<grad_w, dw> = <grad_out, forward(x; dw)>, which holds at any size because the
-operator is linear in the weights (both sides from the GPU).
+Sizes: every workload graph.  Up to the 4096-atom graph (214 648 edges) the
+oracle checks every element of out, grad_x and grad_weights.  On the
+1.47M-edge graph it checks sampled rows -- the out rows of sampled centres from
+their in-edges, the grad_x rows of sampled neighbours from their out-edges --
+and sampled map-gradient entries, each summed by the oracle over all edges.
+Every workload also checks the identities <grad_w, dw> = <grad_out,
+forward(x; dw)> and <grad_x, dx> = <grad_out, forward(dx; w)> (linearity in
+the weights and in x; both sides from the GPU).
 """
 
 import sys
@@ -19,7 +21,8 @@ import numpy as np
 import pytest
 
 import workloads
-from oracle.so2 import edge_wigner, so2_backward, so2_double_backward, so2_forward, weight_numel
+from oracle.so2 import (edge_wigner, so2_backward, so2_double_backward, so2_forward, so2_weight_grad_entries,
+                        weight_numel, weight_blocks)
 
 pytestmark = pytest.mark.gpu
 
@@ -171,12 +174,21 @@ def test_workload(tp, name):
     r = gpu_run(tp, n, src, dst, vec, lmax, C, x, wt, G)
     D = r["D_np"].astype(np.float64)
     errs = {}
-    if E <= 120_000:
+    if E <= 250_000:
+        # every element (the 4096-atom graph's 214 648 edges included)
         errs["out"] = rel_err(r["out"], so2_forward(lmax, C, x, D, wt, src, dst, n))
         gx, gw = so2_backward(lmax, C, x, D, wt, G, src, dst, n)
         errs["grad_x"] = rel_err(r["gx"], gx)
         errs["grad_w"] = rel_err(r["gw"], gw)
     else:
+        # map gradients: sampled entries, each summed by the oracle over all
+        # edges (the first and last of every block and 96 random ones),
+        # normalised by the rms of the sampled reference entries
+        rng_w = np.random.default_rng(331)
+        idx = sorted({j for _, _, off, K in weight_blocks(lmax, C) for j in (off, off + K * K - 1)}
+                     | set(rng_w.choice(len(wt), size=96, replace=False).tolist()))
+        ref_w = so2_weight_grad_entries(lmax, C, x, D, G, src, dst, np.array(idx))
+        errs["grad_w_entries"] = rel_err(r["gw"][idx], ref_w)
         rng = np.random.default_rng(330)
         rows = sample_rows(np.bincount(dst, minlength=n), rng)
         sel = np.isin(dst, rows)
@@ -297,6 +309,12 @@ def test_double_backward_workload(tp, name):
         got = (gG if tag == "grad_G" else gx).cpu().numpy()
         ref = r_gG if tag == "grad_G" else r_gx
         errs[tag] = rel_err(got[rows], ref[rows])
+    # grad_weights = the map gradient of (ggx, grad_out): sampled entries, each
+    # summed by the oracle over all edges
+    idx = sorted({j for _, _, off, K in weight_blocks(lmax, C) for j in (off, off + K * K - 1)}
+                 | set(rng.choice(nw, size=48, replace=False).tolist()))
+    ref_w = so2_weight_grad_entries(lmax, C, ggx, Dn, inp["G"], src, dst, np.array(idx))
+    errs["grad_weights_entries"] = rel_err(gw.cpu().numpy()[idx], ref_w)
     log(f"[so2] double backward workload {name} errors {errs}")
     for k, v in errs.items():
         assert v <= TOL, (k, v)

@@ -28,7 +28,8 @@ import numpy as np
 import pytest
 
 from oracle import TPProblem, cg_real, sh_real, tp_forward
-from oracle.so2 import (edge_rotation, edge_wigner, pack_D, so2_backward, so2_forward, sphere_quadrature,
+from oracle.so2 import (edge_rotation, edge_wigner, pack_D, so2_backward, so2_forward, so2_weight_grad_entries,
+                        sphere_quadrature,
                         unpack_D, weight_blocks, weight_numel, wigner_D)
 
 from test_oracle_tp import fitted_D
@@ -280,6 +281,30 @@ def test_backward_by_linearity(lmax, C):
     # every weight block is reached
     for _, _, off, K in weight_blocks(lmax, C):
         assert np.abs(gw[off:off + K * K]).max() > 0
+
+
+@pytest.mark.parametrize("lmax,C", [(1, 2), (2, 2), (3, 1)])
+def test_weight_grad_entries_by_one_hot_weights(lmax, C):
+    """Each map-gradient entry, evaluated on its own, equals <G, f(x; e_j)>:
+    the forward with a one-hot weight vector (the operator is linear in the
+    weights), for every entry of every block."""
+    rng = np.random.default_rng(97 + lmax)
+    n, E = 8, 50
+    src, dst, vec = make_graph(rng, n, E)
+    D = edge_wigner(lmax, vec)
+    d = C * (lmax + 1) ** 2
+    x, G = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    nw = weight_numel(lmax, C)
+    got = so2_weight_grad_entries(lmax, C, x, D, G, src, dst, np.arange(nw))
+    want = np.empty(nw)
+    for j in range(nw):
+        e = np.zeros(nw)
+        e[j] = 1.0
+        want[j] = np.vdot(G, so2_forward(lmax, C, x, D, e, src, dst, n))
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12 * np.abs(want).max())
+    # and the whole backward agrees with it
+    _, gw = so2_backward(lmax, C, x, D, rng.standard_normal(nw), G, src, dst, n)
+    np.testing.assert_allclose(gw, want, rtol=0, atol=1e-12 * np.abs(want).max())
 
 
 def test_isolated_nodes_and_no_edges():
