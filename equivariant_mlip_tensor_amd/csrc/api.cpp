@@ -318,7 +318,50 @@ extern "C" tpconv_status tpconv_so2_backward(tpconv_graph_t hg, int lmax, int ch
     const hipError_t he = launch_so2_wgrad(lmax, channels, (int)g.n_nodes, g.n_edges, g.dst_row, g.dst_col,
                                            g.dst_eid, static_cast<const float*>(x), static_cast<const float*>(grad_out),
                                            static_cast<const float*>(D), ws_part,
-                                           static_cast<float*>(grad_weights), stream);
+                                           static_cast<float*>(grad_weights), 0, stream);
+    if (he != hipSuccess)
+      return fail(TPCONV_E_HIP, std::string("SO(2) weight-gradient launch: ") + hipGetErrorString(he));
+  }
+  return TPCONV_OK;
+}
+
+extern "C" tpconv_status tpconv_so2_backward_noalloc(tpconv_graph_t hg, int lmax, int channels, tpconv_dtype dtype,
+                                                     const void* x, const void* D, const void* weights,
+                                                     const void* grad_out, void* grad_x, void* grad_weights,
+                                                     hipStream_t stream) {
+  if (hg == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL graph");
+  if (!so2_supported(lmax, channels) || dtype != TPCONV_F32)
+    return fail(TPCONV_E_UNSUPPORTED, "SO(2) convolution: lmax 1..3, channels 16 or 32, fp32");
+  const Graph& g = *reinterpret_cast<const Graph*>(hg);
+  if (grad_x == nullptr && grad_weights == nullptr) return TPCONV_OK;
+  if (g.n_nodes > 0 && grad_out == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL grad_out");
+  if (grad_x != nullptr && weights == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL weights");
+  if (g.n_edges > 0 && (x == nullptr || D == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL x or D");
+  // the library's device scratch: the transposed maps, then as many blocks'
+  // partial map gradients as fit (fewer blocks than the workspace entry
+  // point uses when the scratch is the limit; each block then takes more edges)
+  float* ws = nullptr;
+  int64_t ws_floats = 0;
+  const hipError_t se = so2_scratch(&ws, &ws_floats);
+  if (se != hipSuccess) return fail(TPCONV_E_HIP, std::string("SO(2) scratch lookup: ") + hipGetErrorString(se));
+  const int64_t nw = so2_weight_numel(lmax, channels);
+  const int64_t max_blocks = ws_floats / nw - 1;
+  if (max_blocks < 1)
+    return fail(TPCONV_E_WORKSPACE, "SO(2) backward (no allocation): the maps (" + std::to_string(nw) +
+                                        " floats) exceed the library scratch (" + std::to_string(ws_floats) +
+                                        " floats)");
+  if (grad_x != nullptr && g.n_nodes > 0) {
+    const hipError_t he = launch_so2_conv(lmax, channels, true, false, (int)g.n_nodes, g.src_row, g.src_col, g.src_eid,
+                                          g.src_order, static_cast<const float*>(grad_out),
+                                          static_cast<const float*>(D), static_cast<const float*>(weights),
+                                          static_cast<float*>(grad_x), ws, nullptr, stream);
+    if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("SO(2) backward launch: ") + hipGetErrorString(he));
+  }
+  if (grad_weights != nullptr) {
+    const hipError_t he = launch_so2_wgrad(lmax, channels, (int)g.n_nodes, g.n_edges, g.dst_row, g.dst_col,
+                                           g.dst_eid, static_cast<const float*>(x), static_cast<const float*>(grad_out),
+                                           static_cast<const float*>(D), ws + nw,
+                                           static_cast<float*>(grad_weights), (int)max_blocks, stream);
     if (he != hipSuccess)
       return fail(TPCONV_E_HIP, std::string("SO(2) weight-gradient launch: ") + hipGetErrorString(he));
   }
@@ -395,7 +438,7 @@ extern "C" tpconv_status tpconv_so2_double_backward(tpconv_graph_t hg, int lmax,
     float* out = static_cast<float*>(grad_weights);
     st = ggx != nullptr
              ? check(launch_so2_wgrad(lmax, channels, (int)g.n_nodes, g.n_edges, g.dst_row, g.dst_col, g.dst_eid,
-                                      static_cast<const float*>(ggx), fG, fD, ws_part, out, stream),
+                                      static_cast<const float*>(ggx), fG, fD, ws_part, out, 0, stream),
                      "SO(2) double backward launch: ")
              : check(launch_so2_fill_zero(nw, out, stream), "SO(2) double backward fill: ");
   }

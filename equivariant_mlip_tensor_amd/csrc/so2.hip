@@ -38,6 +38,7 @@
 //    atomics).
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -638,9 +639,39 @@ hipError_t launch_so2_conv(int L, int C, bool adjoint, bool accumulate, int n_ro
 
 hipError_t launch_so2_wgrad(int L, int C, int n_rows, int64_t n_edges, const int32_t* row_ptr, const int32_t* col,
                             const int32_t* eid, const float* X, const float* G, const float* D, float* part,
-                            float* grad_w, hipStream_t s) {
-  const int nb = so2_wgrad_blocks(n_edges);
+                            float* grad_w, int max_blocks, hipStream_t s) {
+  int nb = so2_wgrad_blocks(n_edges);
+  if (max_blocks > 0 && nb > max_blocks) nb = max_blocks;
   SO2_CASES(wgrad_LC, n_rows, n_edges, nb, row_ptr, col, eid, X, G, D, part, grad_w, s)
+}
+
+// Device scratch of tpconv_so2_backward_noalloc (callers that cannot
+// allocate): the transposed maps, then one partial map gradient per block of
+// edges.  Each device that runs the library holds its own copy until the
+// process ends; every call on a device shares it.
+constexpr int64_t kSo2ScratchFloats = int64_t(1) << 22;  // 16 MiB
+static __device__ __align__(256) float scratch[kSo2ScratchFloats];
+
+// This device's address of the scratch array, looked up once per device (the
+// array's name is a host-side stand-in, not a device address).
+hipError_t so2_scratch(float** ptr, int64_t* n_floats) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *ptr = addr[dev];
+  *n_floats = kSo2ScratchFloats;
+  return hipSuccess;
 }
 
 hipError_t launch_so2_fill_zero(int64_t n, float* p, hipStream_t s) {

@@ -113,9 +113,12 @@ hipError_t launch_so2_conv(int L, int C, bool adjoint, bool accumulate, int n_ro
 hipError_t launch_so2_wigner_backward(int L, bool f64, int64_t n_edges, const void* vec, const void* grad_D,
                                       void* grad_vec, hipStream_t s);
 hipError_t launch_so2_fill_zero(int64_t n, float* p, hipStream_t s);
+// max_blocks > 0 caps the number of edge blocks (and of partial sums in part)
 hipError_t launch_so2_wgrad(int L, int C, int n_rows, int64_t n_edges, const int32_t* row_ptr, const int32_t* col,
                             const int32_t* eid, const float* X, const float* G, const float* D, float* part,
-                            float* grad_w, hipStream_t s);
+                            float* grad_w, int max_blocks, hipStream_t s);
+// the allocation-free backward's device scratch on the current device
+hipError_t so2_scratch(float** ptr, int64_t* n_floats);
 hipError_t launch_sh(int L, bool f64, int64_t n_edges, const void* vec, void* Y, hipStream_t s);
 hipError_t launch_sh_backward(int L, bool f64, int64_t n_edges, const void* vec, const void* grad_Y, void* grad_vec,
                               hipStream_t s);

@@ -31,7 +31,8 @@ EXPORTS = ("tpconv_plan", "tpconv_plan_query", "tpconv_plan_paths", "tpconv_plan
            "tpconv_graph_workspace_bytes", "tpconv_graph_create", "tpconv_graph_export", "tpconv_graph_destroy",
            "tpconv_forward", "tpconv_backward", "tpconv_double_backward", "tpconv_sh", "tpconv_sh_backward",
            "tpconv_positions_backward", "tpconv_so2_weight_numel", "tpconv_so2_rotations", "tpconv_so2_forward",
-           "tpconv_so2_workspace_bytes", "tpconv_so2_backward", "tpconv_so2_double_backward",
+           "tpconv_so2_workspace_bytes", "tpconv_so2_backward", "tpconv_so2_backward_noalloc",
+           "tpconv_so2_double_backward",
            "tpconv_so2_frames_backward", "tpconv_so2_rotations_backward", "tpconv_last_error")
 
 
@@ -77,6 +78,7 @@ def _load():
         "tpconv_so2_workspace_bytes": (sz, [ctypes.c_int, ctypes.c_int, i64]),
         "tpconv_so2_backward": (i32, [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, sz,
                                       vp]),
+        "tpconv_so2_backward_noalloc": (i32, [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int] + [vp] * 7),
         "tpconv_so2_double_backward": (i32, [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int] + [vp] * 10 + [sz, vp]),
         "tpconv_so2_frames_backward": (i32, [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int] + [vp] * 6 + [sz, vp]),
         "tpconv_so2_rotations_backward": (i32, [ctypes.c_int, ctypes.c_int, i64, vp, vp, vp, vp]),
@@ -432,6 +434,28 @@ def tpconv_so2_backward(graph: Graph, lmax: int, channels: int, x, D, weights, g
                                     _ptr(grad_out), _ptr(grad_x), _ptr(grad_weights), _ptr(workspace), ws_bytes,
                                     _stream_handle(stream)))
     return grad_x, grad_weights
+
+
+@_on_launch_stream
+def tpconv_so2_backward_noalloc(graph: Graph, lmax: int, channels: int, x, D, weights, grad_out, grad_x,
+                                grad_weights, stream=None) -> None:
+    """tpconv_so2_backward into caller-given outputs (either may be None), with no
+    workspace: the library's device scratch holds the temporaries, so the call
+    allocates nothing.  Calls that overlap on one device race on that scratch."""
+    N, E = graph.n_nodes, graph.n_edges
+    dn, nd, nw = _so2_sizes(lmax, channels)
+    f = torch.float32
+    _need(x, (N, dn), f, "x")
+    _need(D, (E, nd), f, "D")
+    _need(weights, (nw,), f, "weights")
+    _need(grad_out, (N, dn), f, "grad_out")
+    if grad_x is not None:
+        _need(grad_x, (N, dn), f, "grad_x")
+    if grad_weights is not None:
+        _need(grad_weights, (nw,), f, "grad_weights")
+    _check(_lib.tpconv_so2_backward_noalloc(graph.handle, int(lmax), int(channels), F32, _ptr(x), _ptr(D),
+                                            _ptr(weights), _ptr(grad_out), _ptr(grad_x), _ptr(grad_weights),
+                                            _stream_handle(stream)))
 
 
 @_on_launch_stream

@@ -72,7 +72,7 @@ typedef enum {
   TPCONV_E_IRREPS = 2,      /* irreps string does not parse */
   TPCONV_E_UNSUPPORTED = 3, /* l > TPCONV_MAX_L, repeated l, unequal multiplicities, U > 64 */
   TPCONV_E_NO_PATHS = 4,    /* no admissible (s1, l2, s3) path */
-  TPCONV_E_WORKSPACE = 5,   /* graph workspace too small or misaligned */
+  TPCONV_E_WORKSPACE = 5,   /* workspace (or the library's scratch) too small, or misaligned */
   TPCONV_E_INDEX = 6,       /* some src/dst index outside [0, n_nodes) */
   TPCONV_E_HIP = 7          /* a HIP runtime call or kernel launch failed */
 } tpconv_status;
@@ -316,6 +316,23 @@ size_t tpconv_so2_workspace_bytes(int lmax, int channels, int64_t n_edges);
 tpconv_status tpconv_so2_backward(tpconv_graph_t g, int lmax, int channels, tpconv_dtype dtype, const void* x,
                                   const void* D, const void* weights, const void* grad_out, void* grad_x,
                                   void* grad_weights, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* tpconv_so2_backward_noalloc: tpconv_so2_backward without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).  It
+ * allocates nothing: the transposed maps and the partial map gradients live
+ * in a 16 MiB device array of the library (one per device, held until the
+ * process ends; every l <= 3, C <= 32 map set fits, with at least 92 blocks
+ * of edges).  Same arguments, outputs, results and errors as
+ * tpconv_so2_backward; grad_x is bitwise the same, grad_weights may sum its
+ * blocks of edges differently (fewer blocks when the scratch is the limit).
+ * Maps larger than the scratch get TPCONV_E_WORKSPACE.  The scratch keeps the
+ * last call's contents and holds nothing a call needs at its start; calls
+ * that overlap on one device (two streams, or host threads) race on it and
+ * must be ordered by the caller. */
+tpconv_status tpconv_so2_backward_noalloc(tpconv_graph_t g, int lmax, int channels, tpconv_dtype dtype,
+                                          const void* x, const void* D, const void* weights, const void* grad_out,
+                                          void* grad_x, void* grad_weights, hipStream_t stream);
 
 /* tpconv_so2_double_backward: the backward of tpconv_so2_backward, with the
  * frames D held fixed (the TrimSO(2) abstract counts the double backward

@@ -36,7 +36,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(tp):
     declared = header_functions()
-    assert len(declared) == 24
+    assert len(declared) == 25
     assert sorted(tp.EXPORTS) == declared
     lib = ctypes.CDLL(LIB)
     for name in declared:
@@ -167,6 +167,7 @@ def test_so2_sizes_and_errors_need_no_gpu(tp):
     assert lib.tpconv_so2_rotations(2, 0, 0, None, None, None) == 0       # nothing to do
     assert lib.tpconv_so2_forward(None, 2, 16, 0, None, None, None, None, None) == 1
     assert lib.tpconv_so2_backward(None, 2, 16, 0, *([None] * 7), 0, None) == 1
+    assert lib.tpconv_so2_backward_noalloc(None, 2, 16, 0, *([None] * 7)) == 1
     assert lib.tpconv_so2_double_backward(None, 2, 16, 0, *([None] * 10), 0, None) == 1
     assert lib.tpconv_so2_frames_backward(None, 2, 16, 0, *([None] * 6), 0, None) == 1
     assert lib.tpconv_so2_rotations_backward(5, 0, 1, buf, buf, buf, None) == 3
@@ -176,4 +177,6 @@ def test_so2_sizes_and_errors_need_no_gpu(tp):
     assert lib.tpconv_so2_forward(fake, 4, 16, 0, None, None, None, None, None) == 3
     assert lib.tpconv_so2_forward(fake, 2, 16, 1, None, None, None, None, None) == 3
     assert lib.tpconv_so2_backward(fake, 2, 64, 0, *([None] * 7), 0, None) == 3
+    assert lib.tpconv_so2_backward_noalloc(fake, 2, 64, 0, *([None] * 7)) == 3
+    assert lib.tpconv_so2_backward_noalloc(fake, 2, 16, 1, *([None] * 7)) == 3
 
