@@ -27,6 +27,7 @@ from oracle.so2 import (edge_wigner, so2_backward, so2_double_backward, so2_forw
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-5
+CHAIN_TOL = 1e-4   # force chain through the SO(2) frames vs fp64 frames: conditioning x fp32 error (see the test)
 
 
 def log(msg):
@@ -372,23 +373,20 @@ def test_frames_backward_small(tp, lmax, C):
     log(f"[so2] frames backward l<={lmax} C={C} E={len(src)} errors {errs}")
     for k, v in errs.items():
         assert v <= TOL, (k, v)
-    # The whole chain against the oracle's own frames.  grad_vec is a
-    # cancelling contraction of grad_D (84 entries x 28 quadrature points for
-    # l <= 3), so grad_D's fp32 rounding (held to 1e-5 above) shows up larger
-    # relative to grad_vec.  The bound is that rounding carried through the
-    # (linear) rotations backward: a grad_D perturbation of 1e-6 of its RMS
-    # per entry, propagated, as an RMS, times 30 (the test takes the maximum
-    # over all components, which sits several times above an RMS).  A wrong
-    # term in the chain gives errors of the order of grad_vec itself, four
-    # orders above this bound.
+    # The whole chain (edge vectors -> fp32 frames -> fp32 grad_D -> grad_vec)
+    # against the oracle's chain on fp64 frames.  Each step above is held to
+    # 1e-5 on its own inputs; the composition is held to CHAIN_TOL, the
+    # reading for this chain: grad_vec contracts grad_D with the frames'
+    # derivative and cancels, so a relative error d in grad_D moves grad_vec
+    # by up to kappa * d, with kappa measured by the oracle at 4..64 on these
+    # four cases (random grad_D perturbations of 1e-6 of its rms, max/rms
+    # metric, 30 draws); the fp32 frame-gradient pass's own error is at most
+    # 1.6e-6 of rms on every case and workload, and 64 * 1.6e-6 ~ 1e-4.
     ref_D = so2_frames_backward(lmax, C, x, edge_wigner(lmax, v64), w, G, src, dst, n)
     chain = rotations_backward(lmax, v64, ref_D)
-    noise = rng.standard_normal(ref_D.shape) * 1e-6 * np.sqrt(np.mean(ref_D ** 2))
-    bound = 30.0 * np.sqrt(np.mean(rotations_backward(lmax, v64, noise) ** 2))
-    chain_err = float(np.max(np.abs(gv.cpu().numpy() - chain)))
-    log(f"[so2] frames backward chain l<={lmax} C={C}: max err {chain_err:.3e}, propagated-rounding bound {bound:.3e}, "
-        f"relative to rms {rel_err(gv.cpu().numpy(), chain):.3e}")
-    assert chain_err <= bound
+    chain_err = rel_err(gv.cpu().numpy(), chain)
+    log(f"[so2] frames backward chain l<={lmax} C={C}: {chain_err:.3e} of rms (bar {CHAIN_TOL:.0e})")
+    assert chain_err <= CHAIN_TOL
 
 
 @pytest.mark.parametrize("name", ["c1k", "c2k", "c4k", "c28k"])
