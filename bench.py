@@ -186,6 +186,22 @@ def main():
         tp.tpconv_forward(plan, graph, x, Y, W, out)
         tp.tpconv_backward(plan, graph, x, Y, W, G, dx, dY, dW)
 
+    # achievable bandwidth on this machine: a 1 GiB device-to-device copy (read +
+    # write counted), timed with events, median of 10
+    c_src = torch.ones(2**28, dtype=torch.float32, device=dev)
+    c_dst = torch.empty_like(c_src)
+    c_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(12)]
+    for k in range(12):
+        c_ev[k][0].record()
+        c_dst.copy_(c_src)
+        c_ev[k][1].record()
+    torch.cuda.synchronize()
+    copy_ms = float(np.median([e[0].elapsed_time(e[1]) for e in c_ev[2:]]))
+    copy_gbs = 2 * c_src.numel() * 4 / (copy_ms * 1e-3) / 1e9
+    del c_src, c_dst
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()   # the peak reported is the convolution's own
+
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * 2**20 // 4
         a_src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -385,7 +401,8 @@ def main():
         "upstream": up,
         "so2": so2,
         "hbm": {"fwd_bwd_algorithmic_GBps": round(hbm_fwdbwd, 1), "frac_of_peak": round(hbm_fwdbwd / HBM_PEAK_GBS, 4),
-                "fwd_bytes": int(fwd_bytes), "bwd_bytes": int(bwd_bytes)},
+                "fwd_bytes": int(fwd_bytes), "bwd_bytes": int(bwd_bytes),
+                "copy_1GiB_GBps": round(copy_gbs, 1), "frac_of_copy": round(hbm_fwdbwd / copy_gbs, 4)},
         "roofline": roofline,
         "graph_build_ms": round(graph_ms, 3),
         "graph_rebuild_ms": round(graph_rebuild_ms, 3),
