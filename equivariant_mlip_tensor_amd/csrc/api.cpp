@@ -36,7 +36,8 @@ Launcher pick(Kind k, int L, tpconv_dtype dt) {
 #undef TPCONV_PICK
 }
 
-KernelArgs base_args(const Plan& p, int64_t n_rows) {
+// The launch arguments of a plan, or of one of its passes (ps).
+KernelArgs base_args(const Plan& p, int64_t n_rows, const Pass* ps = nullptr) {
   KernelArgs a{};
   a.n_rows = static_cast<int32_t>(n_rows);
   a.mul = p.mul;
@@ -48,17 +49,17 @@ KernelArgs base_args(const Plan& p, int64_t n_rows) {
   a.d_out = static_cast<int32_t>(p.dim_out);
   a.d_sh = static_cast<int32_t>(p.dim_sh);
   a.wstride = p.weight_numel;
-  a.pmask_lo = p.pmask_lo;
-  a.pmask_hi = p.pmask_hi;
+  a.pmask_lo = ps ? ps->pmask_lo : p.pmask_lo;
+  a.pmask_hi = ps ? ps->pmask_hi : p.pmask_hi;
   for (int l = 0; l <= kMaxL; ++l) {
-    a.in_off[l] = p.in_off[l];
-    a.out_off[l] = p.out_off[l];
+    a.in_off[l] = ps ? ps->in_off[l] : p.in_off[l];
+    a.out_off[l] = ps ? ps->out_off[l] : p.out_off[l];
   }
-  for (int t = 0; t < kMaxTriples; ++t) a.woff[t] = p.woff[t];
+  for (int t = 0; t < kMaxTriples; ++t) a.woff[t] = ps ? ps->woff[t] : p.woff[t];
   // first path into each output l in the forward's (l1, l2, l3) loop order,
   // and first path out of each input l in the backward's (l3, l1, l2) order
   const int L = p.kernel_l;
-  auto on = [&](int t) { return t < 64 ? ((p.pmask_lo >> t) & 1ull) : ((p.pmask_hi >> (t - 64)) & 1ull); };
+  auto on = [&](int t) { return t < 64 ? ((a.pmask_lo >> t) & 1ull) : ((a.pmask_hi >> (t - 64)) & 1ull); };
   auto set = [](uint64_t& lo, uint64_t& hi, int t) { (t < 64 ? lo : hi) |= 1ull << (t < 64 ? t : t - 64); };
   bool seen3[kMaxL + 1] = {}, seen1[kMaxL + 1] = {};
   for (int l1 = 0; l1 <= L; ++l1)
@@ -86,8 +87,63 @@ KernelArgs base_args(const Plan& p, int64_t n_rows) {
     const int par = (l % 2 == 0) ? 1 : -1;
     full = p.in[l].l == l && p.out[l].l == l && p.in[l].p == par && p.out[l].p == par;
   }
-  a.full_plan = full ? 1 : 0;
+  a.full_plan = full && ps == nullptr ? 1 : 0;
   return a;
+}
+
+// The launches of a plan: the plan itself, or its passes ordered so that the
+// first launch writing a group of segments overwrites them and the later
+// ones add into them (KernelArgs::acc).
+struct Launch {
+  const Pass* pass;
+  int acc;
+};
+
+// Launches over output segments (forward, double backward's grad_G): passes
+// grouped by output type; a type no path reaches is written as zeros by one
+// of its passes without paths.
+std::vector<Launch> out_launches(const Plan& p) {
+  if (p.passes.empty()) return {Launch{nullptr, 0}};
+  std::vector<Launch> v;
+  for (int to : {1, -1}) {
+    bool first = true;
+    const Pass* zero = nullptr;
+    for (const Pass& ps : p.passes) {
+      if (ps.t_out != to || ps.n_out == 0) continue;
+      if (ps.n_paths == 0) {
+        if (zero == nullptr) zero = &ps;
+        continue;
+      }
+      v.push_back(Launch{&ps, first ? 0 : 1});
+      first = false;
+    }
+    if (first && zero != nullptr) v.push_back(Launch{zero, 0});
+  }
+  return v;
+}
+
+// Launches over input segments (backward, double backward's second kernel):
+// passes grouped by input type for grad_x (bit 0); every launch after the
+// first adds into grad_Y (bit 1); each pass writes its own paths' grad_W.
+std::vector<Launch> in_launches(const Plan& p) {
+  if (p.passes.empty()) return {Launch{nullptr, 0}};
+  std::vector<Launch> v;
+  for (int ti : {1, -1}) {
+    bool first = true;
+    const Pass* zero = nullptr;
+    for (const Pass& ps : p.passes) {
+      if (ps.t_in != ti || ps.n_in == 0) continue;
+      if (ps.n_paths == 0) {
+        if (zero == nullptr) zero = &ps;
+        continue;
+      }
+      v.push_back(Launch{&ps, first ? 0 : 1});
+      first = false;
+    }
+    if (first && zero != nullptr) v.push_back(Launch{zero, 0});
+  }
+  for (size_t i = 1; i < v.size(); ++i) v[i].acc |= 2;
+  return v;
 }
 
 }  // namespace
@@ -111,19 +167,22 @@ extern "C" tpconv_status tpconv_forward(tpconv_plan_t hp, tpconv_graph_t hg, con
   if (g.n_nodes > 0 && (out == nullptr || x == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL x or out");
   if (g.n_edges > 0 && (Y == nullptr || W == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL Y or W");
   if (g.n_nodes == 0) return TPCONV_OK;
-  KernelArgs a = base_args(p, g.n_nodes);
-  a.row_ptr = g.dst_row;
-  a.col = g.dst_col;
-  a.eid = g.dst_eid;
-  a.order = g.dst_order;
-  a.x = x;
-  a.Y = Y;
-  a.W = W;
-  a.out = out;
   Launcher f = pick(Kind::kFwd, p.kernel_l, p.dtype);
   if (f == nullptr) return fail(TPCONV_E_UNSUPPORTED, "no kernel for this l bound");
-  const hipError_t he = f(a, stream);
-  if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("forward launch: ") + hipGetErrorString(he));
+  for (const Launch& ln : out_launches(p)) {
+    KernelArgs a = base_args(p, g.n_nodes, ln.pass);
+    a.acc = ln.acc;
+    a.row_ptr = g.dst_row;
+    a.col = g.dst_col;
+    a.eid = g.dst_eid;
+    a.order = g.dst_order;
+    a.x = x;
+    a.Y = Y;
+    a.W = W;
+    a.out = out;
+    const hipError_t he = f(a, stream);
+    if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("forward launch: ") + hipGetErrorString(he));
+  }
   return TPCONV_OK;
 }
 
@@ -139,22 +198,25 @@ extern "C" tpconv_status tpconv_backward(tpconv_plan_t hp, tpconv_graph_t hg, co
     return fail(TPCONV_E_INVALID_ARG, "NULL x or grad_out");
   if (g.n_edges > 0 && (Y == nullptr || W == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL Y or W");
   if (g.n_nodes == 0) return TPCONV_OK;
-  KernelArgs a = base_args(p, g.n_nodes);
-  a.row_ptr = g.src_row;
-  a.col = g.src_col;
-  a.eid = g.src_eid;
-  a.order = g.src_order;
-  a.x = x;
-  a.Y = Y;
-  a.W = W;
-  a.G = grad_out;
-  a.out = grad_x;
-  a.dY = grad_Y;
-  a.dW = grad_W;
   Launcher f = pick(Kind::kBwd, p.kernel_l, p.dtype);
   if (f == nullptr) return fail(TPCONV_E_UNSUPPORTED, "no kernel for this l bound");
-  const hipError_t he = f(a, stream);
-  if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("backward launch: ") + hipGetErrorString(he));
+  for (const Launch& ln : in_launches(p)) {
+    KernelArgs a = base_args(p, g.n_nodes, ln.pass);
+    a.acc = ln.acc;
+    a.row_ptr = g.src_row;
+    a.col = g.src_col;
+    a.eid = g.src_eid;
+    a.order = g.src_order;
+    a.x = x;
+    a.Y = Y;
+    a.W = W;
+    a.G = grad_out;
+    a.out = grad_x;
+    a.dY = grad_Y;
+    a.dW = grad_W;
+    const hipError_t he = f(a, stream);
+    if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("backward launch: ") + hipGetErrorString(he));
+  }
   return TPCONV_OK;
 }
 
@@ -176,35 +238,43 @@ extern "C" tpconv_status tpconv_double_backward(tpconv_plan_t hp, tpconv_graph_t
   Launcher ff = pick(Kind::kDDF, p.kernel_l, p.dtype);
   Launcher fb = pick(Kind::kDDB, p.kernel_l, p.dtype);
   if (ff == nullptr || fb == nullptr) return fail(TPCONV_E_UNSUPPORTED, "no kernel for this l bound");
-  KernelArgs a = base_args(p, g.n_nodes);
-  a.x = x;
-  a.Y = Y;
-  a.W = W;
-  a.xa = ggx;
-  a.Yb = ggY;
-  a.Wc = ggW;
+  auto common = [&](const Launch& ln) {
+    KernelArgs a = base_args(p, g.n_nodes, ln.pass);
+    a.acc = ln.acc;
+    a.x = x;
+    a.Y = Y;
+    a.W = W;
+    a.xa = ggx;
+    a.Yb = ggY;
+    a.Wc = ggW;
+    return a;
+  };
   if (want_dst) {
-    KernelArgs f = a;
-    f.row_ptr = g.dst_row;
-    f.col = g.dst_col;
-    f.eid = g.dst_eid;
-    f.order = g.dst_order;
-    f.out = grad_G;
-    const hipError_t he = ff(f, stream);
-    if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("double backward launch: ") + hipGetErrorString(he));
+    for (const Launch& ln : out_launches(p)) {
+      KernelArgs f = common(ln);
+      f.row_ptr = g.dst_row;
+      f.col = g.dst_col;
+      f.eid = g.dst_eid;
+      f.order = g.dst_order;
+      f.out = grad_G;
+      const hipError_t he = ff(f, stream);
+      if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("double backward launch: ") + hipGetErrorString(he));
+    }
   }
   if (want_src) {
-    KernelArgs b = a;
-    b.row_ptr = g.src_row;
-    b.col = g.src_col;
-    b.eid = g.src_eid;
-    b.order = g.src_order;
-    b.G = grad_out;
-    b.out = grad_x;
-    b.dY = grad_Y;
-    b.dW = grad_W;
-    const hipError_t he = fb(b, stream);
-    if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("double backward launch: ") + hipGetErrorString(he));
+    for (const Launch& ln : in_launches(p)) {
+      KernelArgs b = common(ln);
+      b.row_ptr = g.src_row;
+      b.col = g.src_col;
+      b.eid = g.src_eid;
+      b.order = g.src_order;
+      b.G = grad_out;
+      b.out = grad_x;
+      b.dY = grad_Y;
+      b.dW = grad_W;
+      const hipError_t he = fb(b, stream);
+      if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("double backward launch: ") + hipGetErrorString(he));
+    }
   }
   return TPCONV_OK;
 }

@@ -96,17 +96,23 @@ tpconv_status Plan::build(const char* irreps_in, int sh_lmax_, const char* irrep
   p.sh_lmax = sh_lmax_;
   p.dtype = dt;
 
-  // kernel coverage: each l at most once per string, one multiplicity, l <= kMaxL, U <= 64
+  // kernel coverage: each (l, parity) at most once per string, one
+  // multiplicity, l <= kMaxL, U <= 64
   const int U = p.in[0].mul;
   int lmax = sh_lmax_;
+  bool repeated_l = false;
   for (const auto* v : {&p.in, &p.out}) {
-    bool seen[64] = {};
+    bool seen[64][2] = {};
+    bool any[64] = {};
     for (const Segment& sg : *v) {
       if (sg.l > kMaxL)
         return fail(TPCONV_E_UNSUPPORTED, "l = " + std::to_string(sg.l) + " exceeds TPCONV_MAX_L");
-      if (seen[sg.l])
-        return fail(TPCONV_E_UNSUPPORTED, "l = " + std::to_string(sg.l) + " appears twice in one irreps string");
-      seen[sg.l] = true;
+      const int pi = sg.p > 0 ? 0 : 1;
+      if (seen[sg.l][pi])
+        return fail(TPCONV_E_UNSUPPORTED, "l = " + std::to_string(sg.l) + " with one parity appears twice in one irreps string");
+      seen[sg.l][pi] = true;
+      if (any[sg.l]) repeated_l = true;
+      any[sg.l] = true;
       if (sg.mul != U) return fail(TPCONV_E_UNSUPPORTED, "all segments must share one multiplicity");
       lmax = std::max(lmax, sg.l);
     }
@@ -190,6 +196,44 @@ tpconv_status Plan::build(const char* irreps_in, int sh_lmax_, const char* irrep
     else
       p.pmask_hi |= 1ull << (t - 64);
   }
+  if (!repeated_l) return TPCONV_OK;
+
+  // both parities of some l: passes by segment type (t_in, t_out)
+  auto type_of = [](const Segment& sg) { return sg.p * ((sg.l % 2 == 0) ? 1 : -1); };
+  auto seg_offsets = [](const std::vector<Segment>& v, int type, int32_t (&off)[kMaxL + 1], int& n,
+                        int (*tf)(const Segment&)) {
+    for (int l = 0; l <= kMaxL; ++l) off[l] = -1;
+    int o = 0;
+    n = 0;
+    for (const Segment& sg : v) {
+      if (tf(sg) == type) {
+        off[sg.l] = o;
+        ++n;
+      }
+      o += sg.mul * (2 * sg.l + 1);
+    }
+  };
+  int (*tf)(const Segment&) = type_of;
+  for (int ti : {1, -1})
+    for (int to : {1, -1}) {
+      Pass ps;
+      ps.t_in = ti;
+      ps.t_out = to;
+      seg_offsets(p.in, ti, ps.in_off, ps.n_in, tf);
+      seg_offsets(p.out, to, ps.out_off, ps.n_out, tf);
+      for (int t = 0; t < kMaxTriples; ++t) ps.woff[t] = -1;
+      for (const Path& q : p.paths) {
+        if (type_of(p.in[q.s1]) != ti || type_of(p.out[q.s3]) != to) continue;
+        const int t = triple_id(p.kernel_l, p.in[q.s1].l, q.l2, p.out[q.s3].l);
+        ps.woff[t] = static_cast<int32_t>(q.woff);
+        if (t < 64)
+          ps.pmask_lo |= 1ull << t;
+        else
+          ps.pmask_hi |= 1ull << (t - 64);
+        ++ps.n_paths;
+      }
+      p.passes.push_back(ps);
+    }
   return TPCONV_OK;
 }
 

@@ -60,7 +60,8 @@ struct KernelArgs {
   int32_t in_l_mask;    // bit l: some path reads input l
   int32_t full_plan;    // 1: segments l = 0..L in order with parity (-1)^l in and out, SH l <= L,
                         //    so the plan holds every even-sum triple in triple order
-  int32_t pad1;
+  int32_t acc;          // run-time plans: bit 0 adds into `out` instead of overwriting it, bit 1 into dY
+                        //    (the later passes of a plan with both parities of one l)
   const int32_t* row_ptr;
   const int32_t* col;
   const int32_t* eid;

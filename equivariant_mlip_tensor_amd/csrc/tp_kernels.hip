@@ -794,7 +794,14 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
       constexpr int l = I;
       const int off = P::out_off(a, l);
       if (off >= 0) {
-        static_for<2 * l + 1>([&](auto M) { orow[off + u * (2 * l + 1) + M] = static_cast<T>(tot[l * l + M]); });
+        static_for<2 * l + 1>([&](auto M) {
+          T* o = &orow[off + u * (2 * l + 1) + M];
+          if constexpr (P::kFull) {
+            *o = static_cast<T>(tot[l * l + M]);
+          } else {  // a plan's later pass adds into what an earlier one wrote
+            *o = (a.acc & 1) ? static_cast<T>(static_cast<A>(*o) + tot[l * l + M]) : static_cast<T>(tot[l * l + M]);
+          }
+        });
       }
     });
   }
@@ -1348,7 +1355,10 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
         if ((u & plain_mask) == 0 && valid) {
           T* dyr = DY + (int64_t)e * d_sh;
           static_for<NV>([&](auto V) {
-            if (V < nv && base + V < d_sh) dyr[base + V] = dya[V];
+            if (V < nv && base + V < d_sh) {
+              if constexpr (P::kFull) dyr[base + V] = dya[V];
+              else dyr[base + V] = (a.acc & 2) ? dyr[base + V] + dya[V] : dya[V];
+            }
           });
         }
       }
@@ -1436,7 +1446,14 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
         constexpr int l = I;
         const int off = P::in_off(a, l);
         if (off >= 0) {
-          static_for<2 * l + 1>([&](auto M) { drow[off + u * (2 * l + 1) + M] = static_cast<T>(dxa[l * l + M]); });
+          static_for<2 * l + 1>([&](auto M) {
+            T* o = &drow[off + u * (2 * l + 1) + M];
+            if constexpr (P::kFull) {
+              *o = static_cast<T>(dxa[l * l + M]);
+            } else {
+              *o = (a.acc & 1) ? static_cast<T>(static_cast<A>(*o) + dxa[l * l + M]) : static_cast<T>(dxa[l * l + M]);
+            }
+          });
         }
       });
     }

@@ -21,6 +21,20 @@ struct Path {
   int64_t woff;  // first W column of the path
 };
 
+// One launch's share of a plan that holds both parities of some l: the
+// input segments of one type t_in and the output segments of one type t_out,
+// where a segment's type is p (-1)^l (+1 natural, -1 the other), and the
+// plan's paths between them (even l1 + l2 + l3 when the types agree, odd
+// otherwise).  Each l appears at most once on either side of a pass.
+struct Pass {
+  int t_in = 1, t_out = 1;
+  int32_t in_off[kMaxL + 1];
+  int32_t out_off[kMaxL + 1];
+  int32_t woff[kMaxTriples];
+  uint64_t pmask_lo = 0, pmask_hi = 0;
+  int n_in = 0, n_out = 0, n_paths = 0;  // segments and paths in the pass
+};
+
 struct Plan {
   std::vector<Segment> in, out;
   int sh_lmax = 0;
@@ -39,6 +53,9 @@ struct Plan {
   int32_t out_off[kMaxL + 1];
   int32_t woff[kMaxTriples];
   uint64_t pmask_lo = 0, pmask_hi = 0;
+  // plans with both parities of some l run as up to four passes (empty for
+  // the others, which run as one launch with the fields above)
+  std::vector<Pass> passes;
 
   static tpconv_status build(const char* irreps_in, int sh_lmax, const char* irreps_out, tpconv_dtype dt,
                              Plan& p);

@@ -44,11 +44,14 @@
  *  - Results are deterministic: the reductions use no floating-point
  *    atomics, so repeated calls give bitwise identical outputs.
  *
- * Kernel coverage: every irreps string may hold each l at most once, all
- * segments of irreps_in and irreps_out share one multiplicity U with
- * 1 <= U <= 64 (one 64-lane wavefront holds a channel per lane), and every l
- * (inputs, outputs, SH) is at most TPCONV_MAX_L.  Other plans are rejected
- * with TPCONV_E_UNSUPPORTED.
+ * Kernel coverage: every irreps string may hold each (l, parity) at most
+ * once (an l may appear with both parities, e.g. 32x1o+32x1e), all segments
+ * of irreps_in and irreps_out share one multiplicity U with 1 <= U <= 64 (one
+ * 64-lane wavefront holds a channel per lane), and every l (inputs, outputs,
+ * SH) is at most TPCONV_MAX_L.  Other plans are rejected with
+ * TPCONV_E_UNSUPPORTED.  A plan holding both parities of some l runs as up to
+ * four launches per kernel (segments grouped by the type p (-1)^l on each
+ * side), the later ones adding into the outputs the earlier ones wrote.
  */
 #ifndef TPCONV_H
 #define TPCONV_H
@@ -70,7 +73,7 @@ typedef enum {
   TPCONV_OK = 0,
   TPCONV_E_INVALID_ARG = 1, /* NULL pointer, negative size, bad dtype, size mismatch */
   TPCONV_E_IRREPS = 2,      /* irreps string does not parse */
-  TPCONV_E_UNSUPPORTED = 3, /* l > TPCONV_MAX_L, repeated l, unequal multiplicities, U > 64 */
+  TPCONV_E_UNSUPPORTED = 3, /* l > TPCONV_MAX_L, repeated (l, parity), unequal multiplicities, U > 64 */
   TPCONV_E_NO_PATHS = 4,    /* no admissible (s1, l2, s3) path */
   TPCONV_E_WORKSPACE = 5,   /* workspace (or the library's scratch) too small, or misaligned */
   TPCONV_E_INDEX = 6,       /* some src/dst index outside [0, n_nodes) */

@@ -47,6 +47,8 @@ CASES = [(w.irreps_in, w.sh_lmax, w.irreps_out, w.dtype) for w in workloads.WORK
     ("3x1o+3x0e", 2, "3x1e+3x2o+3x0o", "f64"),        # odd paths, unsorted segments
     ("5x0e+5x2e", 1, "5x1o+5x2e+5x3o", "f32"),        # missing l, sh below the l bound
     ("1x4e", 4, "1x0e+1x4e", "f64"),
+    ("4x0e+4x1o+4x1e+4x2e", 2, "4x0e+4x0o+4x1o+4x1e+4x2e+4x2o", "f32"),   # both parities of one l
+    ("2x1e+2x0e+2x1o", 1, "2x1o+2x1e", "f64"),                           # both parities, unsorted
 ]
 
 
@@ -102,7 +104,6 @@ def test_survey_sizes(tp):
     ("0x1o", 1, "4x1o", "f32", "TPCONV_E_IRREPS"),
     ("4x5e", 1, "4x5e", "f32", "TPCONV_E_UNSUPPORTED"),
     ("4x1o", 5, "4x1o", "f32", "TPCONV_E_UNSUPPORTED"),
-    ("4x1o+4x1e", 1, "4x1o", "f32", "TPCONV_E_UNSUPPORTED"),
     ("4x1o+4x1o", 1, "4x1o", "f32", "TPCONV_E_UNSUPPORTED"),
     ("4x0e", 1, "8x1o", "f32", "TPCONV_E_UNSUPPORTED"),
     ("128x0e", 0, "128x0e", "f32", "TPCONV_E_UNSUPPORTED"),

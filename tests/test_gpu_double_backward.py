@@ -211,6 +211,19 @@ def test_irreps_variants(tp, spec):
     check_full(tp, spec, 37, src, dst, seed=3, label="variant")
 
 
+@pytest.mark.parametrize("spec", [
+    ("8x0e+8x1o+8x1e+8x2e", 2, "8x0e+8x0o+8x1o+8x1e+8x2e+8x2o", "f32"),
+    ("16x1e+16x0e+16x1o", 1, "16x1o+16x1e", "f64"),
+    ("8x2o+8x2e", 1, "8x1e+8x2e", "f64"),
+])
+def test_both_parities_of_one_l(tp, spec):
+    """Plans with both parities of some l (passes by segment type, the later
+    adding into grad_G, grad_x and grad_Y) against the oracle."""
+    rng = np.random.default_rng(zlib.crc32(repr(spec).encode()) + 1)
+    src, dst = small_graph(rng, 41, 0.2)
+    check_full(tp, spec, 41, src, dst, seed=5, label="both-parities")
+
+
 def test_partial_outputs(tp):
     rng = np.random.default_rng(34)
     src, dst = small_graph(rng, 30, 0.3)

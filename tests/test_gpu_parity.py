@@ -229,6 +229,29 @@ def test_irreps_variants(tp, spec):
     check_full(tp, spec, 37, src, dst, label="variant")
 
 
+BOTH_PARITIES = [
+    ("8x0e+8x1o+8x1e+8x2e", 2, "8x0e+8x0o+8x1o+8x1e+8x2e+8x2o", "f32"),   # both parities in and out
+    ("16x1e+16x0e+16x1o", 1, "16x1o+16x1e", "f64"),                        # unsorted segments
+    ("32x0e+32x0o+32x1o+32x1e+32x2e+32x2o+32x3o+32x3e", 3, "32x0e+32x1o+32x2e+32x3o", "f32"),  # every l twice in
+    ("4x1o", 2, "4x1o+4x1e+4x2e+4x2o", "f64"),                             # both output parities of one input
+    ("8x2o+8x2e", 1, "8x1e+8x2e", "f32"),                                  # an input no path reads (2e)
+]
+
+
+@pytest.mark.parametrize("spec", BOTH_PARITIES)
+def test_both_parities_of_one_l(tp, spec):
+    """Plans holding both parities of some l run as passes by segment type;
+    every output (forward out, grad_x, grad_Y, grad_W) against the oracle,
+    on a graph with a 60-in / 45-out hub and an isolated node."""
+    rng = np.random.default_rng(zlib.crc32(repr(spec).encode()))
+    n = 61
+    src, dst = small_graph(rng, n - 1, 0.15)
+    src = np.concatenate([src, np.arange(1, n - 1), np.zeros(45, np.int32)]).astype(np.int32)
+    dst = np.concatenate([dst, np.zeros(n - 2, np.int32), rng.integers(1, n - 1, 45)]).astype(np.int32)
+    out, dx, dY, dW, _ = check_full(tp, spec, n, src, dst, seed=4, label="both-parities")
+    assert np.all(out[n - 1] == 0) and np.all(dx[n - 1] == 0)   # node n-1 has no edges
+
+
 def test_backward_partial_outputs(tp):
     rng = np.random.default_rng(6)
     src, dst = small_graph(rng, 30, 0.3)
