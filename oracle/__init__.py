@@ -42,4 +42,5 @@ from .tp import TPProblem, tp_forward, tp_backward, tp_double_backward  # noqa: 
 from .forces import sh_and_jacobian, sh_edges, sh_backward, positions_backward  # noqa: F401
 from .so2 import (edge_rotation, wigner_D, edge_wigner, so2_forward, so2_backward,  # noqa: F401
                   so2_double_backward, so2_frames_backward, rotations_backward,
+                  rotations_jvp, so2_frames_double_backward,
                   weight_numel as so2_weight_numel)

@@ -357,3 +357,77 @@ def rotations_backward(lmax, vec, grad_D):
         dLdR = dLdq.T @ pts                                   # [3, 3]: sum_k dLdq[k, a] p_k[b]
         out[e] = np.einsum("ab,jab->j", dLdR, dR)
     return out
+
+
+def rotations_jvp(lmax, vec, dvec):
+    """dD [E, sum (2l+1)^2]: the directional derivative of edge_wigner(lmax, vec)
+    along dvec (per edge), from the same quadrature as wigner_D,
+        dD^l[m][n] = (1/4 pi) sum_k w_k (grad Y_lm(R p_k) . dR p_k) Y_ln(p_k),
+    with dR = sum_j dvec_j dR/dvec_j by the complex step on the Rodrigues
+    formula (as in rotations_backward).  Vectors along the z axis (the zero
+    vector included), where the frame is set by convention, get zero."""
+    from .forces import sh_and_jacobian
+    vec = np.asarray(vec, dtype=np.float64).reshape(-1, 3)
+    dvec = np.asarray(dvec, dtype=np.float64).reshape(-1, 3)
+    pts, w = sphere_quadrature(2 * lmax)
+    Yp = sh_real(lmax, pts)                                   # [K, (L+1)^2]
+    out = np.zeros((len(vec), sum((2 * l + 1) ** 2 for l in range(lmax + 1))))
+    hstep = 1e-30
+    for e, v in enumerate(vec):
+        if np.hypot(v[0], v[1]) == 0.0:
+            continue
+        R = _rotation_of(v)
+        dR = _rotation_of(v + 1j * hstep * dvec[e]).imag / hstep   # [3, 3]
+        q = pts @ R.T                                         # R p_k
+        dq = pts @ dR.T                                       # dR p_k
+        _, J = sh_and_jacobian(lmax, q)                       # [K, (L+1)^2, 3]
+        dY = np.einsum("kma,ka->km", J, dq)                   # derivative of Y(R p_k) along dR
+        blocks = []
+        for l in range(lmax + 1):
+            sl = slice(l * l, (l + 1) ** 2)
+            blocks.append(np.einsum("k,km,kn->mn", w, dY[:, sl], Yp[:, sl]).reshape(-1) / (4.0 * np.pi))
+        out[e] = np.concatenate(blocks)
+    return out
+
+
+def so2_frames_double_backward(lmax, C, x, D, weights, G, dD, src, dst, n_nodes):
+    """Gradients of S = <dD, so2_frames_backward(lmax, C, x, D, weights, G, ...)>
+    with respect to x, the weights and G (the frames D held fixed): the mixed
+    second derivatives that training on forces through the frames needs (dD
+    is the frames' derivative along the force cotangent, rotations_jvp).
+    grad_D_e = dx~ x^T + y~ g^T per block is linear in x, G and the maps, and
+    moving the maps across each term,
+        S = sum_e <dD_e g, SO2(D_e x)> + <D_e g, SO2(dD_e x)>
+    (g = G[dst e], x = x[src e]), so
+        grad_G[dst] += dD_e^T SO2(D_e x) + D_e^T SO2(dD_e x)
+        grad_x[src] += D_e^T SO2^T(dD_e g) + dD_e^T SO2^T(D_e g)
+        grad_w       = the map gradients of the pairs (dD_e g, D_e x) and
+                       (D_e g, dD_e x), as in so2_backward.
+    Returns (grad_x, grad_w, grad_G)."""
+    x = np.asarray(x, dtype=np.float64)
+    G = np.asarray(G, dtype=np.float64)
+    src, dst = np.asarray(src, np.int64), np.asarray(dst, np.int64)
+    A, B = _maps(lmax, C, weights)
+    Dl = unpack_D(D, lmax)
+    Cl = unpack_D(dD, lmax)
+    xs, gd = _split(x[src], lmax, C), _split(G[dst], lmax, C)
+    xD, xC = _rotate(xs, Dl), _rotate(xs, Cl)
+    gD, gC = _rotate(gd, Dl), _rotate(gd, Cl)
+    d = C * (lmax + 1) ** 2
+    grad_G = np.zeros((n_nodes, d))
+    np.add.at(grad_G, dst, _join(_rotate(_so2_apply(xD, lmax, C, A, B), Cl, transpose=True))
+              + _join(_rotate(_so2_apply(xC, lmax, C, A, B), Dl, transpose=True)))
+    grad_x = np.zeros((n_nodes, d))
+    np.add.at(grad_x, src, _join(_rotate(_so2_apply(gC, lmax, C, A, B, adjoint=True), Dl, transpose=True))
+              + _join(_rotate(_so2_apply(gD, lmax, C, A, B, adjoint=True), Cl, transpose=True)))
+    gw = np.zeros(weight_numel(lmax, C))
+    for gt, xt in ((gC, xD), (gD, xC)):
+        for name, m, off, K in weight_blocks(lmax, C):
+            if m == 0:
+                blk = _gather_m(gt, lmax, 0, 0).T @ _gather_m(xt, lmax, 0, 0)
+            else:
+                gp, gm = _gather_m(gt, lmax, m, +1), _gather_m(gt, lmax, m, -1)
+                xp, xm = _gather_m(xt, lmax, m, +1), _gather_m(xt, lmax, m, -1)
+                blk = gp.T @ xp + gm.T @ xm if name == "A" else gm.T @ xp - gp.T @ xm
+            gw[off:off + K * K] += blk.reshape(-1)
+    return grad_x, gw, grad_G

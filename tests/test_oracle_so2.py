@@ -412,3 +412,54 @@ def test_force_through_the_frames():
         assert np.vdot(gvec, dv) == pytest.approx(fd, rel=1e-6, abs=1e-8)
     # radial invariance: the frames depend on the direction only
     np.testing.assert_allclose(np.einsum("ej,ej->e", gvec, vec), 0.0, atol=1e-9)
+
+
+@pytest.mark.parametrize("lmax", [1, 3])
+def test_rotations_jvp_by_differences_and_adjoint(lmax):
+    """The frames' directional derivative against central differences of
+    edge_wigner, and its adjoint relation with rotations_backward (pinned by
+    differences above): <jvp(dv), gD> = <dv, backward(gD)> per edge."""
+    from oracle.so2 import rotations_backward, rotations_jvp
+    rng = np.random.default_rng(130 + lmax)
+    vec = rng.standard_normal((10, 3)) * 2.0
+    vec[3] = [0.0, 0.0, 1.5]                         # on the z axis: convention, zero
+    dv = rng.standard_normal(vec.shape)
+    jv = rotations_jvp(lmax, vec, dv)
+    h = 1e-6
+    fd = (edge_wigner(lmax, vec + h * dv) - edge_wigner(lmax, vec - h * dv)) / (2 * h)
+    keep = np.arange(len(vec)) != 3
+    np.testing.assert_allclose(jv[keep], fd[keep], rtol=1e-6, atol=1e-7)
+    assert np.all(jv[3] == 0)
+    gD = rng.standard_normal(jv.shape)
+    np.testing.assert_allclose(np.sum(jv * gD, axis=1), np.sum(dv * rotations_backward(lmax, vec, gD), axis=1),
+                               rtol=1e-10, atol=1e-12)
+    # radial invariance: moving the vector along itself does not change the frame
+    np.testing.assert_allclose(rotations_jvp(lmax, vec, vec), 0.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("lmax,C", [(1, 2), (3, 2)])
+def test_frames_double_backward_by_linearity(lmax, C):
+    """S = <dD, so2_frames_backward(x, w, G)> is linear in x, in the weights
+    and in G separately, so S(v + u) - S(v) = <grad_v, u> exactly (up to
+    rounding) for each of them, against the pinned so2_frames_backward."""
+    from oracle.so2 import so2_frames_backward, so2_frames_double_backward
+    rng = np.random.default_rng(140 + lmax)
+    n, E = 7, 30
+    src, dst, vec = make_graph(rng, n, E)
+    d = C * (lmax + 1) ** 2
+    D = edge_wigner(lmax, vec)
+    x, G = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    w = rng.standard_normal(weight_numel(lmax, C))
+    dD = rng.standard_normal(D.shape)
+    gx, gw, gG = so2_frames_double_backward(lmax, C, x, D, w, G, dD, src, dst, n)
+    S = lambda x_, w_, G_: np.vdot(dD, so2_frames_backward(lmax, C, x_, D, w_, G_, src, dst, n))  # noqa: E731
+    s0 = S(x, w, G)
+    for _ in range(2):
+        ux, uw, uG = rng.standard_normal(x.shape), rng.standard_normal(w.shape), rng.standard_normal(G.shape)
+        assert S(x + ux, w, G) - s0 == pytest.approx(np.vdot(gx, ux), rel=1e-9, abs=1e-9)
+        assert S(x, w + uw, G) - s0 == pytest.approx(np.vdot(gw, uw), rel=1e-9, abs=1e-9)
+        assert S(x, w, G + uG) - s0 == pytest.approx(np.vdot(gG, uG), rel=1e-9, abs=1e-9)
+    # with dD = D the mixed terms are the two halves of the first derivative
+    # in D taken along itself: S = 2 <G, out>, so grad_G = 2 out
+    _, _, gG2 = so2_frames_double_backward(lmax, C, x, D, w, G, D, src, dst, n)
+    np.testing.assert_allclose(gG2, 2.0 * so2_forward(lmax, C, x, D, w, src, dst, n), rtol=1e-10, atol=1e-10)
