@@ -275,12 +275,20 @@ def test_bitwise_deterministic(tp):
         assert np.array_equal(u, v)
 
 
-def test_graph_layout_matches_stable_sort(tp):
+@pytest.mark.parametrize("n,E,hub", [(500, 6000, 0), (1, 7, 0), (70000, 300000, 120000), (3, 0, 0)])
+def test_graph_layout_matches_stable_sort(tp, n, E, hub):
+    """Both CSR views against numpy's stable sort: random edges, one node,
+    no edges, and 60 000 in-edges plus 60 000 out-edges at one node (rows
+    far past the 1024 degree buckets and a node count past 2^16)."""
     import torch
     rng = np.random.default_rng(8)
-    n, E = 500, 6000
     src = rng.integers(0, n, E).astype(np.int32)
     dst = rng.integers(0, n, E).astype(np.int32)
+    if hub:
+        src[:hub // 2 * 2:2] = 17
+        dst[1:hub // 2 * 2:2] = 17
+        perm = rng.permutation(E)
+        src, dst = src[perm], dst[perm]
     g = tp.tpconv_graph_create(n, torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda())
     drow, dcol, deid, srow, scol, seid = tp.tpconv_graph_export(g)
     o = np.argsort(dst, kind="stable")
