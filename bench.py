@@ -331,7 +331,13 @@ def main():
         dd2 = [torch.empty_like(x2), torch.empty_like(w2), torch.empty_like(x2)]
         gD2 = torch.empty_like(D2)
         gv2 = torch.empty_like(vec2)
-        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.so2_reps + 2)]
+        dvec2 = torch.randn(vec2.shape, dtype=torch.float32, device=dev,
+                            generator=torch.Generator(device=dev).manual_seed(7))
+        dD2 = torch.empty_like(D2)
+        fdd2 = [torch.empty_like(x2), torch.empty_like(w2), torch.empty_like(x2)]
+        wsf2 = torch.empty(tp.tpconv_so2_frames_double_backward_workspace_bytes(L2, C2, N, E), dtype=torch.uint8,
+                           device=dev)
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(10)] for _ in range(args.so2_reps + 2)]
         for k in range(args.so2_reps + 2):   # the first two are warm-up
             sev[k][0].record(stream)
             tp.tpconv_so2_rotations(L2, vec2, D2)
@@ -349,8 +355,12 @@ def main():
             sev[k][6].record(stream)
             tp.tpconv_so2_rotations_backward(L2, vec2, gD2, gv2)
             sev[k][7].record(stream)
+            tp.tpconv_so2_rotations_jvp(L2, vec2, dvec2, dD2)
+            sev[k][8].record(stream)
+            tp.tpconv_so2_frames_double_backward(graph, L2, C2, x2, D2, w2, G2, dD2, *fdd2, workspace=wsf2)
+            sev[k][9].record(stream)
         torch.cuda.synchronize()
-        med = [float(np.median([e[i].elapsed_time(e[i + 1]) for e in sev[2:]])) for i in range(7)]
+        med = [float(np.median([e[i].elapsed_time(e[i + 1]) for e in sev[2:]])) for i in range(9)]
         fl = so2_flops_per_edge(L2, C2) * E
         tf = lambda ms: round(fl / (ms * 1e-3) / 1e12, 2)   # noqa: E731
         so2 = {"shape": f"l<={L2}, {C2} channels, {N} nodes, {E} edges, fp32",
@@ -367,8 +377,11 @@ def main():
                "double_backward_TFLOPs": round(4 * fl / (med[4] * 1e-3) / 1e12, 2),
                "frames_backward_ms_median": round(med[5], 4),
                "rotations_backward_ms_median": round(med[6], 4),
+               "rotations_jvp_ms_median": round(med[7], 4),
+               "frames_double_backward_ms_median": round(med[8], 4),
+               "frames_double_backward_TFLOPs": round(6 * fl / (med[8] * 1e-3) / 1e12, 2),
                "reps": args.so2_reps}
-        del vec2, x2, w2, G2, D2, o2, gx2, gw2, ws2, ggx2, ggw2, dd2, gD2, gv2
+        del vec2, x2, w2, G2, D2, o2, gx2, gw2, ws2, ggx2, ggw2, dd2, gD2, gv2, dvec2, dD2, fdd2, wsf2
 
     b = 4 if w.dtype == "f32" else 8
     fwd_bytes, bwd_bytes = algorithmic_bytes(plan, N, E, b)

@@ -546,6 +546,119 @@ extern "C" tpconv_status tpconv_so2_frames_backward(tpconv_graph_t hg, int lmax,
   return TPCONV_OK;
 }
 
+extern "C" tpconv_status tpconv_so2_rotations_jvp(int lmax, tpconv_dtype dtype, int64_t n_edges, const void* vec,
+                                                  const void* dvec, void* dD, hipStream_t stream) {
+  if (n_edges < 0) return fail(TPCONV_E_INVALID_ARG, "n_edges < 0");
+  if (lmax < 0 || lmax > 4) return fail(TPCONV_E_UNSUPPORTED, "SO(2) rotations: lmax must be 0..4");
+  if (dtype != TPCONV_F32 && dtype != TPCONV_F64) return fail(TPCONV_E_INVALID_ARG, "unknown dtype");
+  if (n_edges > 0 && (vec == nullptr || dvec == nullptr || dD == nullptr))
+    return fail(TPCONV_E_INVALID_ARG, "NULL vec, dvec or dD");
+  const hipError_t he = launch_so2_wigner_jvp(lmax, dtype == TPCONV_F64, n_edges, vec, dvec, dD, stream);
+  if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("SO(2) rotations jvp launch: ") + hipGetErrorString(he));
+  return TPCONV_OK;
+}
+
+namespace {
+// Workspace of tpconv_so2_frames_double_backward: dD with the frames' roll
+// projected out, the two terms of the map gradient, then the backward's
+// workspace (transposed maps, block partials).
+struct FddLayout {
+  size_t ddp, wa, wb, so2, total;
+};
+
+FddLayout fdd_layout(int lmax, int C, int64_t n_edges) {
+  FddLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = (o + bytes + 255) / 256 * 256;
+    return at;
+  };
+  const int64_t nw = so2_weight_numel(lmax, C);
+  const int64_t nd = int64_t(lmax + 1) * (2 * lmax + 1) * (2 * lmax + 3) / 3;
+  L.ddp = take(sizeof(float) * nd * n_edges);
+  L.wa = take(sizeof(float) * nw);
+  L.wb = take(sizeof(float) * nw);
+  L.so2 = take(tpconv_so2_workspace_bytes(lmax, C, n_edges));
+  L.total = o;
+  return L;
+}
+}  // namespace
+
+extern "C" size_t tpconv_so2_frames_double_backward_workspace_bytes(int lmax, int channels, int64_t n_nodes,
+                                                                    int64_t n_edges) {
+  if (!so2_supported(lmax, channels) || n_nodes < 0 || n_edges < 0) return 0;
+  return fdd_layout(lmax, channels, n_edges).total;
+}
+
+extern "C" tpconv_status tpconv_so2_frames_double_backward(tpconv_graph_t hg, int lmax, int channels,
+                                                           tpconv_dtype dtype, const void* x, const void* D,
+                                                           const void* weights, const void* grad_out, const void* dD,
+                                                           void* grad_x, void* grad_weights, void* grad_G,
+                                                           void* workspace, size_t workspace_bytes,
+                                                           hipStream_t stream) {
+  if (hg == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL graph");
+  if (!so2_supported(lmax, channels) || dtype != TPCONV_F32)
+    return fail(TPCONV_E_UNSUPPORTED, "SO(2) convolution: lmax 1..3, channels 16 or 32, fp32");
+  const Graph& g = *reinterpret_cast<const Graph*>(hg);
+  if (grad_x == nullptr && grad_weights == nullptr && grad_G == nullptr) return TPCONV_OK;
+  const FddLayout L = fdd_layout(lmax, channels, g.n_edges);
+  if (workspace == nullptr || workspace_bytes < L.total)
+    return fail(TPCONV_E_WORKSPACE,
+                "SO(2) frames double backward: workspace smaller than tpconv_so2_frames_double_backward_workspace_bytes()");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(TPCONV_E_WORKSPACE, "SO(2) frames double backward: workspace must be 256-byte aligned");
+  if (g.n_nodes > 0 && (x == nullptr || grad_out == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL x or grad_out");
+  if (weights == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL weights");
+  if (reinterpret_cast<uintptr_t>(weights) % 16 != 0)
+    return fail(TPCONV_E_INVALID_ARG, "SO(2) weights must be 16-byte aligned");
+  if (g.n_edges > 0 && (D == nullptr || dD == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL D or dD");
+  char* base = static_cast<char*>(workspace);
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
+  const int64_t nw = so2_weight_numel(lmax, channels);
+  const float* fx = static_cast<const float*>(x);
+  const float* fG = static_cast<const float*>(grad_out);
+  const float* fW = static_cast<const float*>(weights);
+  const float* fD = static_cast<const float*>(D);
+  float* ws_maps = F(L.so2);
+  float* ws_part = ws_maps + nw;
+  const int n = (int)g.n_nodes;
+  // the same second derivatives from dD less its roll component (exact; the
+  // terms of a frames' derivative then no longer cancel)
+  const float* fdD = F(L.ddp);
+  hipError_t he = launch_so2_unroll(lmax, g.n_edges, fD, static_cast<const float*>(dD), F(L.ddp), stream);
+  // grad_G over the destination rows: dD^T SO2(D x), then (adding) D^T SO2(dD x)
+  if (he == hipSuccess && grad_G != nullptr && n > 0) {
+    float* out = static_cast<float*>(grad_G);
+    he = launch_so2_conv(lmax, channels, false, false, n, g.dst_row, g.dst_col, g.dst_eid, g.dst_order, fx, fD, fW,
+                         out, nullptr, nullptr, stream, fdD);
+    if (he == hipSuccess)
+      he = launch_so2_conv(lmax, channels, false, true, n, g.dst_row, g.dst_col, g.dst_eid, g.dst_order, fx, fdD, fW,
+                           out, nullptr, nullptr, stream, fD);
+  }
+  // grad_x over the source rows: D^T SO2^T(dD g), then (adding) dD^T SO2^T(D g)
+  if (he == hipSuccess && grad_x != nullptr && n > 0) {
+    float* out = static_cast<float*>(grad_x);
+    he = launch_so2_conv(lmax, channels, true, false, n, g.src_row, g.src_col, g.src_eid, g.src_order, fG, fdD, fW,
+                         out, ws_maps, nullptr, stream, fD);
+    if (he == hipSuccess)
+      he = launch_so2_conv(lmax, channels, true, true, n, g.src_row, g.src_col, g.src_eid, g.src_order, fG, fD, fW,
+                           out, ws_maps, nullptr, stream, fdD);
+  }
+  // grad_weights: the map gradients of (dD g, D x) and (D g, dD x)
+  if (he == hipSuccess && grad_weights != nullptr) {
+    he = launch_so2_wgrad(lmax, channels, n, g.n_edges, g.dst_row, g.dst_col, g.dst_eid, fx, fG, fD, ws_part, F(L.wa),
+                          0, stream, fdD);
+    if (he == hipSuccess)
+      he = launch_so2_wgrad(lmax, channels, n, g.n_edges, g.dst_row, g.dst_col, g.dst_eid, fx, fG, fdD, ws_part,
+                            F(L.wb), 0, stream, fD);
+    if (he == hipSuccess) he = launch_so2_add(nw, F(L.wa), F(L.wb), static_cast<float*>(grad_weights), stream);
+  }
+  if (he != hipSuccess)
+    return fail(TPCONV_E_HIP, std::string("SO(2) frames double backward launch: ") + hipGetErrorString(he));
+  return TPCONV_OK;
+}
+
 extern "C" tpconv_status tpconv_so2_rotations_backward(int lmax, tpconv_dtype dtype, int64_t n_edges, const void* vec,
                                                        const void* grad_D, void* grad_vec, hipStream_t stream) {
   if (n_edges < 0) return fail(TPCONV_E_INVALID_ARG, "n_edges < 0");

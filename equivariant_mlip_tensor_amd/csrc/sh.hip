@@ -437,6 +437,88 @@ __global__ __launch_bounds__(64) void k_so2_wigner_backward(int64_t n, const T* 
   o[2] = T(gz);
 }
 
+// The frames' directional derivative along dvec: the same dual numbers as
+// the gradient above, contracted with dvec instead of with grad_D,
+//   dD^l[m][n] = sum_k w_k (2l+1) (dvec . dS_lm(R p_k)/dvec) S_ln(p_k).
+// Vectors on the z axis (the zero vector included) get zero.
+template <typename T, int L>
+__global__ __launch_bounds__(64) void k_so2_wigner_jvp(int64_t n, const T* __restrict__ vec,
+                                                       const T* __restrict__ dvec, T* __restrict__ dD) {
+  using D3 = Dual<double>;
+  constexpr int NS = (L + 1) * (L + 1);
+  constexpr int ND = (L + 1) * (2 * L + 1) * (2 * L + 3) / 3;
+  __shared__ FrameQuad<L> Q;
+  frame_quad_fill<L>(Q);
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  const double vx = vec[3 * e], vy = vec[3 * e + 1], vz = vec[3 * e + 2];
+  T* o = dD + e * ND;
+  if (vx == 0.0 && vy == 0.0) {
+    for (int q = 0; q < ND; ++q) o[q] = T(0);
+    return;
+  }
+  const double tx = dvec[3 * e], ty = dvec[3 * e + 1], tz = dvec[3 * e + 2];
+  const D3 X{vx, 1.0, 0.0, 0.0}, Yv{vy, 0.0, 1.0, 0.0}, Z{vz, 0.0, 0.0, 1.0};
+  const D3 r = dsqrt(dsum(dsum(dmul(X, X), dmul(Yv, Yv)), dmul(Z, Z)));
+  const D3 ux = ddiv(X, r), uy = ddiv(Yv, r), uz = ddiv(Z, r);
+  const D3 sn = dsqrt(dsum(dmul(ux, ux), dmul(uy, uy)));
+  const D3 kx = ddiv(uy, sn), ky = dscale(-1.0, ddiv(ux, sn));
+  const D3 zero{0.0, 0.0, 0.0, 0.0};
+  const D3 one_m_c = dlin(1.0, D3{1.0, 0.0, 0.0, 0.0}, -1.0, uz);
+  const D3 K[3][3] = {{zero, zero, ky}, {zero, zero, dscale(-1.0, kx)}, {dscale(-1.0, ky), kx, zero}};
+  D3 R[3][3];
+  for (int a = 0; a < 3; ++a)
+    for (int b = 0; b < 3; ++b) {
+      D3 k2 = zero;
+      for (int q = 0; q < 3; ++q) k2 = dsum(k2, dmul(K[a][q], K[q][b]));
+      R[a][b] = dsum(dsum(D3{a == b ? 1.0 : 0.0, 0.0, 0.0, 0.0}, dmul(sn, K[a][b])), dmul(one_m_c, k2));
+    }
+  double acc[ND];
+  for (int q = 0; q < ND; ++q) acc[q] = 0.0;
+  for (int k = 0; k < FrameQuad<L>::NQ; ++k) {
+    {
+      const double p[3] = {Q.p[k][0], Q.p[k][1], Q.p[k][2]};
+      D3 q[3];
+      for (int a = 0; a < 3; ++a) q[a] = dsum(dsum(dscale(p[0], R[a][0]), dscale(p[1], R[a][1])), dscale(p[2], R[a][2]));
+      const D3 q2 = dsum(dsum(dmul(q[0], q[0]), dmul(q[1], q[1])), dmul(q[2], q[2]));
+      const double* Sp = Q.S[k];
+      D3 Sq[NS];
+      solid_harmonics<L, D3, DualOps<double>>(q[0], q[1], q[2], q2, D3{1.0, 0.0, 0.0, 0.0}, Sq);
+      const double w = Q.w[k];
+      sh_for<L + 1>([&](auto IL) {
+        constexpr int l = IL, n2 = 2 * l + 1, off = l * (2 * l - 1) * (2 * l + 1) / 3;
+        const double wl = w * n2;
+        sh_for<n2>([&](auto M) {
+          const D3& sq = Sq[l * l + M];
+          const double a = wl * (tx * sq.dx + ty * sq.dy + tz * sq.dz);
+          sh_for<n2>([&](auto N) { acc[off + M * n2 + N] += a * Sp[l * l + N]; });
+        });
+      });
+    }
+  }
+  for (int q = 0; q < ND; ++q) o[q] = T(acc[q]);
+}
+
+template <typename T, int L>
+hipError_t wigner_jvp_T(int64_t n, const void* vec, const void* dvec, void* dD, hipStream_t s) {
+  const int64_t blocks = (n + 63) / 64;
+  hipLaunchKernelGGL((k_so2_wigner_jvp<T, L>), dim3((unsigned)blocks), dim3(64), 0, s, n,
+                     static_cast<const T*>(vec), static_cast<const T*>(dvec), static_cast<T*>(dD));
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t wigner_jvp_dispatch(int L, int64_t n, const void* vec, const void* dvec, void* dD, hipStream_t s) {
+  switch (L) {
+    case 0: return wigner_jvp_T<T, 0>(n, vec, dvec, dD, s);
+    case 1: return wigner_jvp_T<T, 1>(n, vec, dvec, dD, s);
+    case 2: return wigner_jvp_T<T, 2>(n, vec, dvec, dD, s);
+    case 3: return wigner_jvp_T<T, 3>(n, vec, dvec, dD, s);
+    case 4: return wigner_jvp_T<T, 4>(n, vec, dvec, dD, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename T, int L>
 hipError_t wigner_bwd_T(int64_t n, const void* vec, const void* gD, void* gvec, hipStream_t s) {
   const int64_t blocks = (n + 63) / 64;
@@ -529,6 +611,13 @@ hipError_t launch_so2_wigner_backward(int L, bool f64, int64_t n_edges, const vo
   if (n_edges <= 0) return hipSuccess;
   return f64 ? wigner_bwd_dispatch<double>(L, n_edges, vec, grad_D, grad_vec, s)
              : wigner_bwd_dispatch<float>(L, n_edges, vec, grad_D, grad_vec, s);
+}
+
+hipError_t launch_so2_wigner_jvp(int L, bool f64, int64_t n_edges, const void* vec, const void* dvec, void* dD,
+                                 hipStream_t s) {
+  if (n_edges <= 0) return hipSuccess;
+  return f64 ? wigner_jvp_dispatch<double>(L, n_edges, vec, dvec, dD, s)
+             : wigner_jvp_dispatch<float>(L, n_edges, vec, dvec, dD, s);
 }
 
 hipError_t launch_pos_backward(bool f64, int64_t n_nodes, const int32_t* src_row, const int32_t* src_eid,

@@ -38,6 +38,7 @@
 //    atomics).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 #include <utility>
@@ -297,17 +298,24 @@ __device__ __forceinline__ void so2_maps(float* tile, const float* __restrict__ 
 //   gD[e]^l[m][n] (+)= sum_c tile[e][l][c][m] V[l][c][n],
 // which is grad_D's y~ G^T (resp. dx~ x^T) term: out is then gD [E][ND],
 // indexed by edge id, overwritten or (accumulate) added to.
-template <int L, int C, bool ADJ, bool FRAMES>
+//
+// TWO: the inverse rotation uses other blocks, Dr, than the rotation on
+// gather (D_e^T replaced by Dr_e^T): the terms of the mixed second
+// derivatives through the frames, where one of the two places holds the
+// frames' derivative.
+template <int L, int C, bool ADJ, bool FRAMES, bool TWO = false>
 __global__ __launch_bounds__(128, 2) void k_so2_conv(const int32_t* __restrict__ row_ptr,
                                                      const int32_t* __restrict__ col, const int32_t* __restrict__ eid,
                                                      const int32_t* __restrict__ order, const float* __restrict__ X,
                                                      const float* __restrict__ Dm, const float* __restrict__ W,
                                                      float* __restrict__ out, const int accumulate,
-                                                     const float* __restrict__ V) {
+                                                     const float* __restrict__ V, const float* __restrict__ Dr) {
   using S = So2Shape<L, C>;
   static_assert(S::NACC * 64 <= S::kEdges * S::PAD, "row-sum exchange must fit the tile");
+  static_assert(!(TWO && FRAMES), "two rotations only in the plain convolution");
   __shared__ float tile[S::kEdges * S::PAD];
   __shared__ float dl[S::kEdges * S::NDP];
+  __shared__ float dl2[TWO ? S::kEdges * S::NDP : 1];
   __shared__ float vrow[FRAMES ? S::DN : 1];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -326,6 +334,7 @@ __global__ __launch_bounds__(128, 2) void k_so2_conv(const int32_t* __restrict__
     // the chunk's Wigner rows (zeros past the row end, so those edges rotate to zero)
     const int my_id = lane < ne ? eid[k0 + lane] : 0;
     load_wigner<L, C, 128>(threadIdx.x, ne, my_id, Dm, dl);
+    if constexpr (TWO) load_wigner<L, C, 128>(threadIdx.x, ne, my_id, Dr, dl2);
     __syncthreads();
     for (int e0 = 8 * wave; e0 < 8 * wave + 8; e0 += 4) {  // wave-uniform; four edges' loads issued together
       float xv[4][S::NC];
@@ -370,7 +379,7 @@ __global__ __launch_bounds__(128, 2) void k_so2_conv(const int32_t* __restrict__
     const int e_end = min(ne, 8 * wave + 8);
     for (int e = 8 * wave; e < e_end; ++e) {  // wave-uniform
       const float* te = &tile[e * S::PAD];
-      const float* dle = &dl[e * S::NDP];
+      const float* dle = TWO ? &dl2[e * S::NDP] : &dl[e * S::NDP];
       so2_for<L + 1>([&](auto IL) {
         constexpr int l = IL, n2 = 2 * l + 1;
         float yv[n2];
@@ -413,6 +422,74 @@ __global__ __launch_bounds__(256) void k_so2_fill_zero(int64_t n, float* __restr
   if (i < n) p[i] = 0.f;
 }
 
+// out = a + b (the two terms of the map gradient of the mixed second
+// derivatives through the frames)
+__global__ __launch_bounds__(256) void k_so2_add(int64_t n, const float* __restrict__ a, const float* __restrict__ b,
+                                                 float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) out[i] = a[i] + b[i];
+}
+
+// dDp_e = dD_e - c_e J D_e, with J the generator of rolls about the edge
+// axis on each degree-l block ((J v)[l - m] = m v[l + m] and
+// (J v)[l + m] = -m v[l - m] for m > 0) and c_e = <dD_e, J D_e> / |J D_e|^2,
+// computed in fp64 and rounded once.  A roll of an edge's frame about its
+// axis leaves the convolution unchanged, so the derivatives through the
+// frames are blind to any dD along J D_e: the mixed second derivatives with
+// dDp equal those with dD exactly (for any c_e), and dDp no longer carries
+// the roll rate of a frames' derivative, which grows without bound near the
+// frame construction's pole and whose two terms cancel.  Edges in blocks of
+// 64, staged through LDS so that the global accesses are coalesced; the first
+// wavefront projects one edge per lane.
+template <int L>
+__global__ __launch_bounds__(256) void k_so2_unroll(int64_t n_edges, const float* __restrict__ D,
+                                                    const float* __restrict__ dD, float* __restrict__ out) {
+  constexpr int ND = (L + 1) * (2 * L + 1) * (2 * L + 3) / 3;
+  constexpr int EB = 64;
+  __shared__ float sD[EB * ND];
+  __shared__ float sd[EB * ND];
+  const int64_t e0 = (int64_t)blockIdx.x * EB;
+  const int ne = (int)min((int64_t)EB, n_edges - e0);
+  const int64_t base = e0 * ND;
+  const int cnt = ne * ND;
+  for (int i = threadIdx.x; i < cnt; i += 256) {
+    sD[i] = D[base + i];
+    sd[i] = dD[base + i];
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < ne) {
+    const float* a = sD + threadIdx.x * ND;
+    float* b = sd + threadIdx.x * ND;
+    double num = 0.0, den = 0.0;
+    so2_for<L>([&](auto lm1) {
+      constexpr int l = decltype(lm1)::value + 1;
+      constexpr int off = l * (2 * l - 1) * (2 * l + 1) / 3;
+      constexpr int w = 2 * l + 1;
+      for (int m = 1; m <= l; ++m)
+        for (int n = 0; n < w; ++n) {
+          const double ap = a[off + (l + m) * w + n], am = a[off + (l - m) * w + n];
+          num += m * ((double)b[off + (l - m) * w + n] * ap - (double)b[off + (l + m) * w + n] * am);
+          den += (double)(m * m) * (ap * ap + am * am);
+        }
+    });
+    const double c = den > 0.0 ? num / den : 0.0;
+    so2_for<L>([&](auto lm1) {
+      constexpr int l = decltype(lm1)::value + 1;
+      constexpr int off = l * (2 * l - 1) * (2 * l + 1) / 3;
+      constexpr int w = 2 * l + 1;
+      for (int m = 1; m <= l; ++m)
+        for (int n = 0; n < w; ++n) {
+          const double ap = a[off + (l + m) * w + n], am = a[off + (l - m) * w + n];
+          const double bp = b[off + (l + m) * w + n], bm = b[off + (l - m) * w + n];
+          b[off + (l + m) * w + n] = (float)(bp + c * m * am);
+          b[off + (l - m) * w + n] = (float)(bm - c * m * ap);
+        }
+    });
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < cnt; i += 256) out[base + i] = sd[i];
+}
+
 // Each map block of W transposed in place of itself: Wt[off + n K + k] =
 // W[off + k K + n] (the adjoint kernel's weights).
 template <int L, int C>
@@ -447,12 +524,12 @@ __device__ __forceinline__ int slot_row(const int32_t* __restrict__ row_ptr, int
   return lo;
 }
 
-template <int L, int C, int WV>
+template <int L, int C, int WV, bool TWO>
 __device__ __forceinline__ void wgrad_wave(int n_rows, int64_t s0, int64_t s1, const int32_t* __restrict__ row_ptr,
                                            const int32_t* __restrict__ col, const int32_t* __restrict__ eid,
                                            const float* __restrict__ X, const float* __restrict__ G,
-                                           const float* __restrict__ Dm, float* __restrict__ part, float* xt,
-                                           float* gt, float* dl) {
+                                           const float* __restrict__ Dm, const float* __restrict__ Dg,
+                                           float* __restrict__ part, float* xt, float* gt, float* dl, float* dl2) {
   using S = So2Shape<L, C>;
   constexpr int NMINE = So2Jobs<L, C>::value.nmine[WV];
   const int lane = threadIdx.x & 63;
@@ -479,6 +556,7 @@ __device__ __forceinline__ void wgrad_wave(int n_rows, int64_t s0, int64_t s1, c
     }
     cur = __builtin_amdgcn_readlane(my_d, ne - 1);
     load_wigner<L, C, 64 * S::kWaves>(threadIdx.x, ne, my_id, Dm, dl);
+    if constexpr (TWO) load_wigner<L, C, 64 * S::kWaves>(threadIdx.x, ne, my_id, Dg, dl2);
     __syncthreads();
     {  // this wavefront's two edges, x and grad_out rows loaded together
       float xv[2][S::NC], gv[2][S::NC];
@@ -490,7 +568,7 @@ __device__ __forceinline__ void wgrad_wave(int n_rows, int64_t s0, int64_t s1, c
       so2_for<2>([&](auto I) {
         constexpr int e = WV + S::kWaves * int(I);
         rotate_in<L, C>(xv[I], &dl[e * S::NDP], &xt[e * S::PADW], c, h);
-        rotate_in<L, C>(gv[I], &dl[e * S::NDP], &gt[e * S::PADW], c, h);
+        rotate_in<L, C>(gv[I], TWO ? &dl2[e * S::NDP] : &dl[e * S::NDP], &gt[e * S::PADW], c, h);
       });
     }
     __syncthreads();
@@ -529,27 +607,31 @@ __device__ __forceinline__ void wgrad_wave(int n_rows, int64_t s0, int64_t s1, c
   });
 }
 
-template <int L, int C>
+// TWO: grad_out rotated by other blocks, Dg, than x (the mixed second
+// derivatives through the frames).
+template <int L, int C, bool TWO = false>
 __global__ __launch_bounds__(512) void k_so2_wgrad(int n_rows, int64_t n_slots, int64_t per_block,
                                                    const int32_t* __restrict__ row_ptr,
                                                    const int32_t* __restrict__ col, const int32_t* __restrict__ eid,
                                                    const float* __restrict__ X, const float* __restrict__ G,
-                                                   const float* __restrict__ Dm, float* __restrict__ part) {
+                                                   const float* __restrict__ Dm, const float* __restrict__ Dg,
+                                                   float* __restrict__ part) {
   using S = So2Shape<L, C>;
   __shared__ float xt[S::kEdges * S::PADW];
   __shared__ float gt[S::kEdges * S::PADW];
   __shared__ float dl[S::kEdges * S::NDP];
+  __shared__ float dl2[TWO ? S::kEdges * S::NDP : 1];
   const int64_t s0 = (int64_t)blockIdx.x * per_block;
   const int64_t s1 = min(n_slots, s0 + per_block);
   switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
-    case 0: wgrad_wave<L, C, 0>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, part, xt, gt, dl); break;
-    case 1: wgrad_wave<L, C, 1>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, part, xt, gt, dl); break;
-    case 2: wgrad_wave<L, C, 2>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, part, xt, gt, dl); break;
-    case 3: wgrad_wave<L, C, 3>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, part, xt, gt, dl); break;
-    case 4: wgrad_wave<L, C, 4>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, part, xt, gt, dl); break;
-    case 5: wgrad_wave<L, C, 5>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, part, xt, gt, dl); break;
-    case 6: wgrad_wave<L, C, 6>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, part, xt, gt, dl); break;
-    default: wgrad_wave<L, C, 7>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, part, xt, gt, dl); break;
+    case 0: wgrad_wave<L, C, 0, TWO>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, Dg, part, xt, gt, dl, dl2); break;
+    case 1: wgrad_wave<L, C, 1, TWO>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, Dg, part, xt, gt, dl, dl2); break;
+    case 2: wgrad_wave<L, C, 2, TWO>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, Dg, part, xt, gt, dl, dl2); break;
+    case 3: wgrad_wave<L, C, 3, TWO>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, Dg, part, xt, gt, dl, dl2); break;
+    case 4: wgrad_wave<L, C, 4, TWO>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, Dg, part, xt, gt, dl, dl2); break;
+    case 5: wgrad_wave<L, C, 5, TWO>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, Dg, part, xt, gt, dl, dl2); break;
+    case 6: wgrad_wave<L, C, 6, TWO>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, Dg, part, xt, gt, dl, dl2); break;
+    default: wgrad_wave<L, C, 7, TWO>(n_rows, s0, s1, row_ptr, col, eid, X, G, Dm, Dg, part, xt, gt, dl, dl2); break;
   }
 }
 
@@ -567,38 +649,49 @@ __global__ __launch_bounds__(256) void k_so2_wsum(int nb, int64_t nw, const floa
 template <int L, int C>
 hipError_t conv_LC(bool adjoint, bool accumulate, int n_rows, const int32_t* row_ptr, const int32_t* col,
                    const int32_t* eid, const int32_t* order, const float* X, const float* D, const float* W,
-                   float* out, float* Wt, const float* V, hipStream_t s) {
+                   float* out, float* Wt, const float* V, const float* Dr, hipStream_t s) {
   using S = So2Shape<L, C>;
+  const dim3 grid((unsigned)n_rows), block(128);
+  const int acc = (int)accumulate;
   if (adjoint) {
     hipLaunchKernelGGL((k_so2_transpose<L, C>), dim3((unsigned)((S::NW + 255) / 256)), dim3(256), 0, s, W, Wt);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (V != nullptr)
-      hipLaunchKernelGGL((k_so2_conv<L, C, true, true>), dim3((unsigned)n_rows), dim3(128), 0, s, row_ptr, col, eid,
-                         order, X, D, Wt, out, (int)accumulate, V);
+      hipLaunchKernelGGL((k_so2_conv<L, C, true, true>), grid, block, 0, s, row_ptr, col, eid, order, X, D, Wt, out,
+                         acc, V, Dr);
+    else if (Dr != nullptr)
+      hipLaunchKernelGGL((k_so2_conv<L, C, true, false, true>), grid, block, 0, s, row_ptr, col, eid, order, X, D,
+                         Wt, out, acc, V, Dr);
     else
-      hipLaunchKernelGGL((k_so2_conv<L, C, true, false>), dim3((unsigned)n_rows), dim3(128), 0, s, row_ptr, col, eid,
-                         order, X, D, Wt, out, (int)accumulate, V);
-  }
-  else
+      hipLaunchKernelGGL((k_so2_conv<L, C, true, false>), grid, block, 0, s, row_ptr, col, eid, order, X, D, Wt, out,
+                         acc, V, Dr);
+  } else {
     if (V != nullptr)
-      hipLaunchKernelGGL((k_so2_conv<L, C, false, true>), dim3((unsigned)n_rows), dim3(128), 0, s, row_ptr, col, eid,
-                         order, X, D, W, out, (int)accumulate, V);
+      hipLaunchKernelGGL((k_so2_conv<L, C, false, true>), grid, block, 0, s, row_ptr, col, eid, order, X, D, W, out,
+                         acc, V, Dr);
+    else if (Dr != nullptr)
+      hipLaunchKernelGGL((k_so2_conv<L, C, false, false, true>), grid, block, 0, s, row_ptr, col, eid, order, X, D,
+                         W, out, acc, V, Dr);
     else
-      hipLaunchKernelGGL((k_so2_conv<L, C, false, false>), dim3((unsigned)n_rows), dim3(128), 0, s, row_ptr, col, eid,
-                         order, X, D, W, out, (int)accumulate, V);
+      hipLaunchKernelGGL((k_so2_conv<L, C, false, false>), grid, block, 0, s, row_ptr, col, eid, order, X, D, W, out,
+                         acc, V, Dr);
+  }
   return hipGetLastError();
 }
 
 template <int L, int C>
 hipError_t wgrad_LC(int n_rows, int64_t n_slots, int nb, const int32_t* row_ptr, const int32_t* col,
-                    const int32_t* eid, const float* X, const float* G, const float* D, float* part, float* gw,
-                    hipStream_t s) {
+                    const int32_t* eid, const float* X, const float* G, const float* D, const float* Dg, float* part,
+                    float* gw, hipStream_t s) {
   using S = So2Shape<L, C>;
   const int64_t per_block = (n_slots + nb - 1) / nb;
-  hipLaunchKernelGGL((k_so2_wgrad<L, C>), dim3((unsigned)nb), dim3(64 * S::kWaves), 0, s, n_rows, n_slots, per_block,
-                     row_ptr,
-                     col, eid, X, G, D, part);
+  if (Dg != nullptr)
+    hipLaunchKernelGGL((k_so2_wgrad<L, C, true>), dim3((unsigned)nb), dim3(64 * S::kWaves), 0, s, n_rows, n_slots,
+                       per_block, row_ptr, col, eid, X, G, D, Dg, part);
+  else
+    hipLaunchKernelGGL((k_so2_wgrad<L, C>), dim3((unsigned)nb), dim3(64 * S::kWaves), 0, s, n_rows, n_slots,
+                       per_block, row_ptr, col, eid, X, G, D, D, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_so2_wsum, dim3((unsigned)((S::NW + 255) / 256)), dim3(256), 0, s, nb, (int64_t)S::NW, part,
@@ -632,17 +725,18 @@ int so2_wgrad_blocks(int64_t n_edges) {
 
 hipError_t launch_so2_conv(int L, int C, bool adjoint, bool accumulate, int n_rows, const int32_t* row_ptr,
                            const int32_t* col, const int32_t* eid, const int32_t* order, const float* X,
-                           const float* D, const float* W, float* out, float* Wt, const float* V, hipStream_t s) {
+                           const float* D, const float* W, float* out, float* Wt, const float* V, hipStream_t s,
+                           const float* Dr) {
   if (n_rows <= 0) return hipSuccess;
-  SO2_CASES(conv_LC, adjoint, accumulate, n_rows, row_ptr, col, eid, order, X, D, W, out, Wt, V, s)
+  SO2_CASES(conv_LC, adjoint, accumulate, n_rows, row_ptr, col, eid, order, X, D, W, out, Wt, V, Dr, s)
 }
 
 hipError_t launch_so2_wgrad(int L, int C, int n_rows, int64_t n_edges, const int32_t* row_ptr, const int32_t* col,
                             const int32_t* eid, const float* X, const float* G, const float* D, float* part,
-                            float* grad_w, int max_blocks, hipStream_t s) {
+                            float* grad_w, int max_blocks, hipStream_t s, const float* Dg) {
   int nb = so2_wgrad_blocks(n_edges);
   if (max_blocks > 0 && nb > max_blocks) nb = max_blocks;
-  SO2_CASES(wgrad_LC, n_rows, n_edges, nb, row_ptr, col, eid, X, G, D, part, grad_w, s)
+  SO2_CASES(wgrad_LC, n_rows, n_edges, nb, row_ptr, col, eid, X, G, D, Dg, part, grad_w, s)
 }
 
 // Device scratch of tpconv_so2_backward_noalloc (callers that cannot
@@ -672,6 +766,24 @@ hipError_t so2_scratch(float** ptr, int64_t* n_floats) {
   *ptr = addr[dev];
   *n_floats = kSo2ScratchFloats;
   return hipSuccess;
+}
+
+hipError_t launch_so2_add(int64_t n, const float* a, const float* b, float* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_so2_add, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n, a, b, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_so2_unroll(int L, int64_t n_edges, const float* D, const float* dD, float* out, hipStream_t s) {
+  if (n_edges <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((n_edges + 63) / 64)), block(256);
+  switch (L) {
+    case 1: hipLaunchKernelGGL(k_so2_unroll<1>, grid, block, 0, s, n_edges, D, dD, out); break;
+    case 2: hipLaunchKernelGGL(k_so2_unroll<2>, grid, block, 0, s, n_edges, D, dD, out); break;
+    case 3: hipLaunchKernelGGL(k_so2_unroll<3>, grid, block, 0, s, n_edges, D, dD, out); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_so2_fill_zero(int64_t n, float* p, hipStream_t s) {

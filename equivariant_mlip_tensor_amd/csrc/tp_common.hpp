@@ -108,16 +108,27 @@ int so2_wgrad_blocks(int64_t n_edges);
 // accumulate: out += instead of out = (each row has one writer, so still deterministic).
 // Wt: adjoint only, weight_numel floats.  V non-null: the frame-gradient mode, out = grad_D
 // [E][sum (2l+1)^2] by edge id, V the rows' own vectors (grad_out, or x for the adjoint).
+// Dr non-null (V null): the inverse rotation uses Dr instead of D.
 hipError_t launch_so2_conv(int L, int C, bool adjoint, bool accumulate, int n_rows, const int32_t* row_ptr,
                            const int32_t* col, const int32_t* eid, const int32_t* order, const float* X,
-                           const float* D, const float* W, float* out, float* Wt, const float* V, hipStream_t s);
+                           const float* D, const float* W, float* out, float* Wt, const float* V, hipStream_t s,
+                           const float* Dr = nullptr);
 hipError_t launch_so2_wigner_backward(int L, bool f64, int64_t n_edges, const void* vec, const void* grad_D,
                                       void* grad_vec, hipStream_t s);
+// the frames' directional derivative along dvec [E][3]: dD [E][sum (2l+1)^2]
+hipError_t launch_so2_wigner_jvp(int L, bool f64, int64_t n_edges, const void* vec, const void* dvec, void* dD,
+                                 hipStream_t s);
+// out = a + b
+hipError_t launch_so2_add(int64_t n, const float* a, const float* b, float* out, hipStream_t s);
+// dDp = dD minus, per edge, its component along the frame's roll about the
+// edge axis (fp64 projection), lmax 1..3.
+hipError_t launch_so2_unroll(int L, int64_t n_edges, const float* D, const float* dD, float* out, hipStream_t s);
 hipError_t launch_so2_fill_zero(int64_t n, float* p, hipStream_t s);
-// max_blocks > 0 caps the number of edge blocks (and of partial sums in part)
+// max_blocks > 0 caps the number of edge blocks (and of partial sums in part); Dg non-null:
+// grad_out rotated by Dg instead of D
 hipError_t launch_so2_wgrad(int L, int C, int n_rows, int64_t n_edges, const int32_t* row_ptr, const int32_t* col,
                             const int32_t* eid, const float* X, const float* G, const float* D, float* part,
-                            float* grad_w, int max_blocks, hipStream_t s);
+                            float* grad_w, int max_blocks, hipStream_t s, const float* Dg = nullptr);
 // the allocation-free backward's device scratch on the current device
 hipError_t so2_scratch(float** ptr, int64_t* n_floats);
 hipError_t launch_sh(int L, bool f64, int64_t n_edges, const void* vec, void* Y, hipStream_t s);

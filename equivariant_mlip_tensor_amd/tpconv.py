@@ -33,7 +33,9 @@ EXPORTS = ("tpconv_plan", "tpconv_plan_query", "tpconv_plan_paths", "tpconv_plan
            "tpconv_positions_backward", "tpconv_so2_weight_numel", "tpconv_so2_rotations", "tpconv_so2_forward",
            "tpconv_so2_workspace_bytes", "tpconv_so2_backward", "tpconv_so2_backward_noalloc",
            "tpconv_so2_double_backward",
-           "tpconv_so2_frames_backward", "tpconv_so2_rotations_backward", "tpconv_last_error")
+           "tpconv_so2_frames_backward", "tpconv_so2_rotations_backward", "tpconv_so2_rotations_jvp",
+           "tpconv_so2_frames_double_backward_workspace_bytes", "tpconv_so2_frames_double_backward",
+           "tpconv_last_error")
 
 
 class TPConvError(RuntimeError):
@@ -82,6 +84,10 @@ def _load():
         "tpconv_so2_double_backward": (i32, [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int] + [vp] * 10 + [sz, vp]),
         "tpconv_so2_frames_backward": (i32, [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int] + [vp] * 6 + [sz, vp]),
         "tpconv_so2_rotations_backward": (i32, [ctypes.c_int, ctypes.c_int, i64, vp, vp, vp, vp]),
+        "tpconv_so2_rotations_jvp": (i32, [ctypes.c_int, ctypes.c_int, i64, vp, vp, vp, vp]),
+        "tpconv_so2_frames_double_backward_workspace_bytes": (sz, [ctypes.c_int, ctypes.c_int, i64, i64]),
+        "tpconv_so2_frames_double_backward": (i32, [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int] + [vp] * 9 +
+                                              [sz, vp]),
         "tpconv_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -536,3 +542,59 @@ def tpconv_so2_rotations_backward(lmax: int, vec, grad_D, grad_vec=None, stream=
                                               _ptr(grad_D), _ptr(grad_vec), _stream_handle(stream)))
     return grad_vec
 
+
+
+@_on_launch_stream
+def tpconv_so2_rotations_jvp(lmax: int, vec, dvec, dD=None, stream=None) -> torch.Tensor:
+    """dD [E, sum (2l+1)^2]: the frames' derivative along dvec [E, 3] (dtype of vec)."""
+    E = vec.shape[0] if vec.dim() == 2 else -1
+    dt = vec.dtype
+    _need(vec, (E, 3), dt, "vec")
+    _need(dvec, (E, 3), dt, "dvec")
+    nd = (lmax + 1) * (2 * lmax + 1) * (2 * lmax + 3) // 3
+    if dD is None:
+        dD = torch.empty((E, nd), dtype=dt, device=vec.device)
+    _need(dD, (E, nd), dt, "dD")
+    _check(_lib.tpconv_so2_rotations_jvp(int(lmax), F64 if dt == torch.float64 else F32, E, _ptr(vec), _ptr(dvec),
+                                         _ptr(dD), _stream_handle(stream)))
+    return dD
+
+
+def tpconv_so2_frames_double_backward_workspace_bytes(lmax: int, channels: int, n_nodes: int, n_edges: int) -> int:
+    return int(_lib.tpconv_so2_frames_double_backward_workspace_bytes(int(lmax), int(channels), int(n_nodes),
+                                                                       int(n_edges)))
+
+
+@_on_launch_stream
+def tpconv_so2_frames_double_backward(graph: Graph, lmax: int, channels: int, x, D, weights, grad_out, dD,
+                                      grad_x=None, grad_weights=None, grad_G=None, need=(True, True, True),
+                                      workspace=None, stream=None):
+    """(grad_x, grad_weights, grad_G) of <dD, tpconv_so2_frames_backward(...)>; None where `need` is off."""
+    N, E = graph.n_nodes, graph.n_edges
+    dn, nd, nw = _so2_sizes(lmax, channels)
+    f = torch.float32
+    _need(x, (N, dn), f, "x")
+    _need(D, (E, nd), f, "D")
+    _need(weights, (nw,), f, "weights")
+    _need(grad_out, (N, dn), f, "grad_out")
+    _need(dD, (E, nd), f, "dD")
+    dev = x.device
+    if need[0] and grad_x is None:
+        grad_x = torch.empty((N, dn), dtype=f, device=dev)
+    if need[1] and grad_weights is None:
+        grad_weights = torch.empty((nw,), dtype=f, device=dev)
+    if need[2] and grad_G is None:
+        grad_G = torch.empty((N, dn), dtype=f, device=dev)
+    for t, shape, name in ((grad_x, (N, dn), "grad_x"), (grad_weights, (nw,), "grad_weights"),
+                           (grad_G, (N, dn), "grad_G")):
+        if t is not None:
+            _need(t, shape, f, name)
+    if workspace is None:
+        workspace = torch.empty(max(tpconv_so2_frames_double_backward_workspace_bytes(lmax, channels, N, E), 256),
+                                dtype=torch.uint8, device=dev)
+    _check(_lib.tpconv_so2_frames_double_backward(graph.handle, int(lmax), int(channels), F32, _ptr(x), _ptr(D),
+                                                  _ptr(weights), _ptr(grad_out), _ptr(dD), _ptr(grad_x),
+                                                  _ptr(grad_weights), _ptr(grad_G), _ptr(workspace),
+                                                  workspace.numel() * workspace.element_size(),
+                                                  _stream_handle(stream)))
+    return grad_x, grad_weights, grad_G

@@ -380,6 +380,46 @@ tpconv_status tpconv_so2_frames_backward(tpconv_graph_t g, int lmax, int channel
 tpconv_status tpconv_so2_rotations_backward(int lmax, tpconv_dtype dtype, int64_t n_edges, const void* vec,
                                             const void* grad_D, void* grad_vec, hipStream_t stream);
 
+/* tpconv_so2_rotations_jvp: dD [E][sum (2l+1)^2] (overwritten), the
+ * directional derivative of tpconv_so2_rotations(vec) along dvec [E][3]
+ * per edge -- the same dual numbers as tpconv_so2_rotations_backward,
+ * contracted with dvec.  With dvec the cotangent of the edge-vector gradient
+ * (e.g. of forces), dD is the cotangent that
+ * tpconv_so2_frames_double_backward takes.  Vectors on the z axis (and the
+ * zero vector) get zero.  Errors as tpconv_so2_rotations. */
+tpconv_status tpconv_so2_rotations_jvp(int lmax, tpconv_dtype dtype, int64_t n_edges, const void* vec,
+                                       const void* dvec, void* dD, hipStream_t stream);
+
+/* tpconv_so2_frames_double_backward: the mixed second derivatives through
+ * the edge frames that training on forces needs (the TrimSO(2) abstract asks
+ * for the higher-order differentiation of training).  With grad_D =
+ * tpconv_so2_frames_backward(x, D, weights, grad_out) and a cotangent dD of
+ * the same shape, it returns the gradients of S = <dD, grad_D> with respect
+ * to x, the weights and grad_out (frames D held fixed):
+ *   grad_G[dst]  += dD_e^T SO2(D_e x) + D_e^T SO2(dD_e x)
+ *   grad_x[src]  += D_e^T SO2^T(dD_e g) + dD_e^T SO2^T(D_e g)
+ *   grad_weights  = the map gradients of (dD_e g, D_e x) and (D_e g, dD_e x)
+ * (g = grad_out[dst], x = x[src]): each term one pass of the forward, the
+ * adjoint or the map-gradient kernel with different blocks in its two
+ * rotation places (the second of each pair adds into the first's output;
+ * each row has one writer).  dD is first replaced, per edge, by dD minus its
+ * least-squares component along J D (J the generator of rolls about the edge
+ * axis), in fp64: the convolution does not change when an edge's frame rolls
+ * about its axis, so this changes no result in exact arithmetic, and it
+ * removes the roll rate of a frames' derivative, which is unbounded for
+ * edges near the frames' pole and whose two terms cancel in fp32.  Outputs (grad_x, grad_G [N][C (L+1)^2],
+ * grad_weights [weight_numel]) are overwritten; NULL skips one.  workspace:
+ * at least tpconv_so2_frames_double_backward_workspace_bytes(...), 256-byte
+ * aligned, caller-owned; weights 16-byte aligned.  Errors:
+ * TPCONV_E_INVALID_ARG, TPCONV_E_UNSUPPORTED (as tpconv_so2_forward),
+ * TPCONV_E_WORKSPACE, TPCONV_E_HIP. */
+size_t tpconv_so2_frames_double_backward_workspace_bytes(int lmax, int channels, int64_t n_nodes, int64_t n_edges);
+tpconv_status tpconv_so2_frames_double_backward(tpconv_graph_t g, int lmax, int channels, tpconv_dtype dtype,
+                                                const void* x, const void* D, const void* weights,
+                                                const void* grad_out, const void* dD, void* grad_x,
+                                                void* grad_weights, void* grad_G, void* workspace,
+                                                size_t workspace_bytes, hipStream_t stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* tpconv_last_error(void);
 

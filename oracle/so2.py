@@ -390,7 +390,7 @@ def rotations_jvp(lmax, vec, dvec):
     return out
 
 
-def so2_frames_double_backward(lmax, C, x, D, weights, G, dD, src, dst, n_nodes):
+def so2_frames_double_backward(lmax, C, x, D, weights, G, dD, src, dst, n_nodes, parts=False):
     """Gradients of S = <dD, so2_frames_backward(lmax, C, x, D, weights, G, ...)>
     with respect to x, the weights and G (the frames D held fixed): the mixed
     second derivatives that training on forces through the frames needs (dD
@@ -403,7 +403,12 @@ def so2_frames_double_backward(lmax, C, x, D, weights, G, dD, src, dst, n_nodes)
         grad_x[src] += D_e^T SO2^T(dD_e g) + dD_e^T SO2^T(D_e g)
         grad_w       = the map gradients of the pairs (dD_e g, D_e x) and
                        (D_e g, dD_e x), as in so2_backward.
-    Returns (grad_x, grad_w, grad_G)."""
+    Returns (grad_x, grad_w, grad_G); with parts=True each is instead the
+    pair of its two terms in the order written above (first the one with dD
+    on the output side or on g), whose sum is the gradient.  The pair shows
+    how much the two terms cancel: for frames' derivatives dD = Omega D with
+    Omega antisymmetric they cancel exactly in the part of Omega that
+    commutes with the SO(2) maps (the rotation about the edge axis)."""
     x = np.asarray(x, dtype=np.float64)
     G = np.asarray(G, dtype=np.float64)
     src, dst = np.asarray(src, np.int64), np.asarray(dst, np.int64)
@@ -414,14 +419,15 @@ def so2_frames_double_backward(lmax, C, x, D, weights, G, dD, src, dst, n_nodes)
     xD, xC = _rotate(xs, Dl), _rotate(xs, Cl)
     gD, gC = _rotate(gd, Dl), _rotate(gd, Cl)
     d = C * (lmax + 1) ** 2
-    grad_G = np.zeros((n_nodes, d))
-    np.add.at(grad_G, dst, _join(_rotate(_so2_apply(xD, lmax, C, A, B), Cl, transpose=True))
-              + _join(_rotate(_so2_apply(xC, lmax, C, A, B), Dl, transpose=True)))
-    grad_x = np.zeros((n_nodes, d))
-    np.add.at(grad_x, src, _join(_rotate(_so2_apply(gC, lmax, C, A, B, adjoint=True), Dl, transpose=True))
-              + _join(_rotate(_so2_apply(gD, lmax, C, A, B, adjoint=True), Cl, transpose=True)))
-    gw = np.zeros(weight_numel(lmax, C))
+    gG1, gG2 = np.zeros((n_nodes, d)), np.zeros((n_nodes, d))
+    np.add.at(gG1, dst, _join(_rotate(_so2_apply(xD, lmax, C, A, B), Cl, transpose=True)))
+    np.add.at(gG2, dst, _join(_rotate(_so2_apply(xC, lmax, C, A, B), Dl, transpose=True)))
+    gx1, gx2 = np.zeros((n_nodes, d)), np.zeros((n_nodes, d))
+    np.add.at(gx1, src, _join(_rotate(_so2_apply(gC, lmax, C, A, B, adjoint=True), Dl, transpose=True)))
+    np.add.at(gx2, src, _join(_rotate(_so2_apply(gD, lmax, C, A, B, adjoint=True), Cl, transpose=True)))
+    gws = []
     for gt, xt in ((gC, xD), (gD, xC)):
+        gw = np.zeros(weight_numel(lmax, C))
         for name, m, off, K in weight_blocks(lmax, C):
             if m == 0:
                 blk = _gather_m(gt, lmax, 0, 0).T @ _gather_m(xt, lmax, 0, 0)
@@ -429,5 +435,8 @@ def so2_frames_double_backward(lmax, C, x, D, weights, G, dD, src, dst, n_nodes)
                 gp, gm = _gather_m(gt, lmax, m, +1), _gather_m(gt, lmax, m, -1)
                 xp, xm = _gather_m(xt, lmax, m, +1), _gather_m(xt, lmax, m, -1)
                 blk = gp.T @ xp + gm.T @ xm if name == "A" else gm.T @ xp - gp.T @ xm
-            gw[off:off + K * K] += blk.reshape(-1)
-    return grad_x, gw, grad_G
+            gw[off:off + K * K] = blk.reshape(-1)
+        gws.append(gw)
+    if parts:
+        return (gx1, gx2), (gws[0], gws[1]), (gG1, gG2)
+    return gx1 + gx2, gws[0] + gws[1], gG1 + gG2

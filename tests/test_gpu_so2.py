@@ -413,3 +413,119 @@ def test_frames_backward_workload(tp, name):
     log(f"[so2] frames backward workload {name} errors {errs}")
     for k, v in errs.items():
         assert v <= TOL, (k, v)
+
+
+@pytest.mark.parametrize("lmax", [1, 2, 3, 4])
+@pytest.mark.parametrize("dt", ["f32", "f64"])
+def test_rotations_jvp(tp, lmax, dt):
+    """The frames' directional derivative against the oracle's (quadrature
+    differentiated through the complex step), z-axis and zero vectors included."""
+    import torch
+    from oracle.so2 import rotations_jvp
+    rng = np.random.default_rng(500 + 10 * lmax + (dt == "f64"))
+    npdt = np.float32 if dt == "f32" else np.float64
+    vec = (rng.standard_normal((300, 3)) * rng.uniform(0.5, 4.0, (300, 1))).astype(npdt)
+    vec[0] = [0.0, 0.0, 2.0]
+    vec[1] = [0.0, 0.0, -1.0]
+    vec[2] = 0.0
+    dvec = rng.standard_normal((300, 3)).astype(npdt)
+    got = tp.tpconv_so2_rotations_jvp(lmax, dev(vec), dev(dvec))
+    torch.cuda.synchronize()
+    ref = rotations_jvp(lmax, vec.astype(np.float64), dvec.astype(np.float64))
+    err = rel_err(got.cpu().numpy(), ref)
+    log(f"[so2] rotations jvp l<={lmax} {dt}: {err:.3e}")
+    assert err <= (TOL if dt == "f32" else 1e-11)
+    assert np.all(got.cpu().numpy()[:3] == 0)
+
+
+def fdd_errors(got, ref):
+    return {name: rel_err(g, r) for name, g, r in zip(("grad_x", "grad_w", "grad_G"), got, ref)}
+
+
+def fdd_cotangent(tp, kind, lmax, vec, rng):
+    """dD: a general cotangent (random blocks) or the frames' derivative along
+    random edge-vector cotangents (the case force training gives).  In the
+    second the two terms of each output cancel in the frames' roll about the
+    edge axis, whose rate is unbounded near the frames' pole (the workload
+    graphs hold such edges); the library removes that component first, which
+    changes no result exactly, and both kinds are held to the same bar."""
+    if kind == "random":
+        nd = (lmax + 1) * (2 * lmax + 1) * (2 * lmax + 3) // 3
+        return dev(rng.standard_normal((len(vec), nd)).astype(np.float32))
+    return tp.tpconv_so2_rotations_jvp(lmax, dev(vec), dev(rng.standard_normal(vec.shape).astype(np.float32)))
+
+
+@pytest.mark.parametrize("kind", ["random", "jvp"])
+@pytest.mark.parametrize("lmax,C", [(1, 16), (2, 32), (3, 16), (3, 32)])
+def test_frames_double_backward_small(tp, lmax, C, kind):
+    """The mixed second derivatives through the frames against the oracle on
+    the same fp32 frames and dD, every element; a hub row, an isolated node;
+    partial outputs agree with the full call."""
+    import torch
+    from oracle.so2 import so2_frames_double_backward
+    rng = np.random.default_rng(520 + 10 * lmax + C)
+    n = 35
+    dst = np.concatenate([np.full(21, 3), rng.integers(0, n, 160)])
+    src = rng.integers(0, n, len(dst))
+    keep = (src != 6) & (dst != 6)
+    src, dst = src[keep].astype(np.int32), dst[keep].astype(np.int32)
+    vec = (rng.standard_normal((len(src), 3)) * 2.0).astype(np.float32)
+    d, nw = C * (lmax + 1) ** 2, weight_numel(lmax, C)
+    x, G = rng.standard_normal((n, d)).astype(np.float32), rng.standard_normal((n, d)).astype(np.float32)
+    w = (rng.standard_normal(nw) / np.sqrt(2 * C * (lmax + 1))).astype(np.float32)
+    g = tp.tpconv_graph_create(n, dev(src), dev(dst))
+    D = tp.tpconv_so2_rotations(lmax, dev(vec))
+    dD = fdd_cotangent(tp, kind, lmax, vec, rng)
+    gx, gw, gG = tp.tpconv_so2_frames_double_backward(g, lmax, C, dev(x), D, dev(w), dev(G), dD)
+    torch.cuda.synchronize()
+    Dn, dDn = D.cpu().numpy().astype(np.float64), dD.cpu().numpy().astype(np.float64)
+    ref = so2_frames_double_backward(lmax, C, x, Dn, w, G, dDn, src, dst, n)
+    errs = fdd_errors([t.cpu().numpy() for t in (gx, gw, gG)], ref)
+    log(f"[so2] frames double backward l<={lmax} C={C} dD={kind} E={len(src)} errors {errs}")
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)
+    assert np.all(gx.cpu().numpy()[6] == 0) and np.all(gG.cpu().numpy()[6] == 0)
+    for need in ((True, False, False), (False, True, False), (False, False, True)):
+        part = tp.tpconv_so2_frames_double_backward(g, lmax, C, dev(x), D, dev(w), dev(G), dD, need=need)
+        for full, p in zip((gx, gw, gG), part):
+            if p is not None:
+                assert torch.equal(full, p)
+
+
+def test_frames_double_backward_no_edges(tp):
+    import torch
+    lmax, C, n = 2, 16, 5
+    e = np.zeros(0, np.int32)
+    d, nw = C * (lmax + 1) ** 2, weight_numel(lmax, C)
+    g = tp.tpconv_graph_create(n, dev(e), dev(e))
+    nd = (lmax + 1) * (2 * lmax + 1) * (2 * lmax + 3) // 3
+    z = torch.zeros((0, nd), dtype=torch.float32, device="cuda")
+    gx, gw, gG = tp.tpconv_so2_frames_double_backward(g, lmax, C, dev(np.ones((n, d), np.float32)), z,
+                                                      dev(np.ones(nw, np.float32)), dev(np.ones((n, d), np.float32)),
+                                                      z)
+    torch.cuda.synchronize()
+    assert torch.all(gx == 0) and torch.all(gw == 0) and torch.all(gG == 0)
+
+
+@pytest.mark.parametrize("name,kind", [("c1k", "random"), ("c1k", "jvp"), ("c4k", "jvp")])
+def test_frames_double_backward_workload(tp, name, kind):
+    """Full size, every element against the oracle (on the GPU's frames and
+    dD), in the launch configuration of the other SO(2) passes."""
+    import torch
+    from oracle.so2 import so2_frames_double_backward
+    w = workloads.WORKLOADS[name]
+    lmax, C = workloads.SO2_SHAPES[name]
+    inp = workloads.make_so2_inputs(w, weight_numel(lmax, C))
+    src, dst, vec, n = inp["src"], inp["dst"], inp["vec"].astype(np.float32), inp["n_nodes"]
+    g = tp.tpconv_graph_create(n, dev(src), dev(dst))
+    D = tp.tpconv_so2_rotations(lmax, dev(vec))
+    dD = fdd_cotangent(tp, kind, lmax, vec, np.random.default_rng(530))
+    gx, gw, gG = tp.tpconv_so2_frames_double_backward(g, lmax, C, dev(inp["x"]), D, dev(inp["weights"]),
+                                                      dev(inp["G"]), dD)
+    torch.cuda.synchronize()
+    ref = so2_frames_double_backward(lmax, C, inp["x"], D.cpu().numpy().astype(np.float64), inp["weights"],
+                                     inp["G"], dD.cpu().numpy().astype(np.float64), src, dst, n)
+    errs = fdd_errors([t.cpu().numpy() for t in (gx, gw, gG)], ref)
+    log(f"[so2] frames double backward workload {name} dD={kind} E={len(src)} errors {errs}")
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)

@@ -463,3 +463,53 @@ def test_frames_double_backward_by_linearity(lmax, C):
     # in D taken along itself: S = 2 <G, out>, so grad_G = 2 out
     _, _, gG2 = so2_frames_double_backward(lmax, C, x, D, w, G, D, src, dst, n)
     np.testing.assert_allclose(gG2, 2.0 * so2_forward(lmax, C, x, D, w, src, dst, n), rtol=1e-10, atol=1e-10)
+    # the two terms of each gradient swap when D and dD swap, and the grad_G
+    # terms sum to the polarisation of the (quadratic in D) forward
+    p1 = so2_frames_double_backward(lmax, C, x, D, w, G, dD, src, dst, n, parts=True)
+    p2 = so2_frames_double_backward(lmax, C, x, dD, w, G, D, src, dst, n, parts=True)
+    for (a1, b1), (a2, b2), full in zip(p1, p2, (gx, gw, gG)):
+        np.testing.assert_allclose(a1, b2, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(b1, a2, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(a1 + b1, full, rtol=1e-12, atol=1e-12)
+    fwd = lambda D_: so2_forward(lmax, C, x, D_, w, src, dst, n)  # noqa: E731
+    np.testing.assert_allclose(fwd(D + dD) - fwd(D - dD), 2.0 * (p1[2][0] + p1[2][1]), rtol=1e-10, atol=1e-10)
+
+
+def roll_generator(l):
+    """Generator of rotations about the edge axis on the real degree-l
+    harmonics: the (m, -m) pair turns at rate m."""
+    J = np.zeros((2 * l + 1, 2 * l + 1))
+    for m in range(1, l + 1):
+        J[l - m, l + m] = m
+        J[l + m, l - m] = -m
+    return J
+
+
+@pytest.mark.parametrize("lmax,C", [(1, 2), (3, 2)])
+def test_roll_direction_is_invisible_to_the_frame_gradients(lmax, C):
+    """Rolling a frame about its edge axis leaves the convolution unchanged
+    (test_roll_invariance), so with J the roll generator (checked against the
+    Wigner blocks of small rolls): grad_D of each edge is orthogonal to J D_e,
+    and the mixed second derivatives do not change when dD_e moves along
+    J D_e, whatever dD is."""
+    from oracle.so2 import so2_frames_backward, so2_frames_double_backward
+    rng = np.random.default_rng(150 + lmax)
+    h = 1e-6
+    Dp, Dm = wigner_D(lmax, rot_z(h)[None]), wigner_D(lmax, rot_z(-h)[None])
+    for l in range(lmax + 1):
+        np.testing.assert_allclose((Dp[l][0] - Dm[l][0]) / (2 * h), roll_generator(l), atol=1e-8)
+    n, E = 7, 30
+    src, dst, vec = make_graph(rng, n, E)
+    d = C * (lmax + 1) ** 2
+    D = edge_wigner(lmax, vec)
+    x, G = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    w = rng.standard_normal(weight_numel(lmax, C))
+    JD = pack_D([roll_generator(l)[None] @ b for l, b in enumerate(unpack_D(D, lmax))])
+    gD = so2_frames_backward(lmax, C, x, D, w, G, src, dst, n)
+    assert np.max(np.abs(np.sum(gD * JD, axis=1))) <= 1e-11 * np.max(np.abs(gD)) * np.max(np.abs(JD)) * D.shape[1]
+    dD = rng.standard_normal(D.shape)
+    c = rng.standard_normal((E, 1)) * 50.0
+    a = so2_frames_double_backward(lmax, C, x, D, w, G, dD, src, dst, n)
+    b = so2_frames_double_backward(lmax, C, x, D, w, G, dD + c * JD, src, dst, n)
+    for u, v in zip(a, b):
+        np.testing.assert_allclose(u, v, rtol=0, atol=1e-10 * np.max(np.abs(u)) * 50)
