@@ -29,6 +29,8 @@ Modules:
   so2     -- the SO(2) convolution (edge-frame rotation, per-|m| dense maps,
              inverse rotation on reduction), its backward and double backward,
              and the gradient through the edge frames to the edge vectors.
+  radial  -- per-edge weights from the radial network's last layer, W = h M,
+             and the convolution's gradients with respect to h and M.
 
 Every function here is pinned by a test in ``tests/test_oracle_*.py`` against
 mathematics it does not itself use (library routines, closed forms,
@@ -40,6 +42,7 @@ from .cg import cg_complex, real_basis_U, cg_real  # noqa: F401
 from .sh import sh_complex, sh_real  # noqa: F401
 from .tp import TPProblem, tp_forward, tp_backward, tp_double_backward  # noqa: F401
 from .forces import sh_and_jacobian, sh_edges, sh_backward, positions_backward  # noqa: F401
+from .radial import radial_weights, radial_forward, radial_backward  # noqa: F401
 from .so2 import (edge_rotation, wigner_D, edge_wigner, so2_forward, so2_backward,  # noqa: F401
                   so2_double_backward, so2_frames_backward, rotations_backward,
                   rotations_jvp, so2_frames_double_backward,
