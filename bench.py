@@ -55,6 +55,10 @@ def parse():
                    help="timed calls of the edge-harmonics / position-gradient kernels (0 skips); reported as upstream")
     p.add_argument("--so2-reps", type=int, default=20,
                    help="timed calls of each SO(2)-convolution pass on the same graph (0 skips); reported as so2")
+    p.add_argument("--radial-reps", type=int, default=20,
+                   help="timed calls of the convolution with weights from the radial network's last layer, "
+                        "fused and unfused (0 skips); reported as radial")
+    p.add_argument("--radial-hidden", type=int, default=64)
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="also run one plain device copy of this many MiB (scales rocprofv3 FETCH/WRITE_SIZE)")
     return p.parse_args()
@@ -383,6 +387,63 @@ def main():
                "reps": args.so2_reps}
         del vec2, x2, w2, G2, D2, o2, gx2, gw2, ws2, ggx2, ggw2, dd2, gD2, gv2, dvec2, dD2, fdd2, wsf2
 
+    radial = None
+    if args.radial_reps > 0 and w.dtype == "f32":
+        # W = h M from the radial network's last layer: generated inside the
+        # kernels (fused) against the chain that materialises W (a GEMM, the
+        # convolution, and the GEMMs for the gradients of h and M)
+        H = args.radial_hidden
+        gr = torch.Generator(device=dev).manual_seed(11)
+        hh = torch.randn((E, H), dtype=torch.float32, device=dev, generator=gr)
+        MM = torch.randn((H, plan.weight_numel), dtype=torch.float32, device=dev,
+                         generator=gr) / float(np.sqrt(H * plan.n_paths))
+        r_out, r_dx, r_dY = torch.empty_like(out), torch.empty_like(dx), torch.empty_like(dY)
+        r_dh, r_dW, r_dM = torch.empty_like(hh), torch.empty_like(dW), torch.empty_like(MM)
+        Wu = torch.empty_like(dW)
+        nev = 11
+        rev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.radial_reps + 2)]
+        for k in range(args.radial_reps + 2):   # the first two are warm-up
+            ev = rev[k]
+            ev[0].record(stream)
+            tp.tpconv_radial_forward(plan, graph, x, Y, hh, MM, r_out)
+            ev[1].record(stream)
+            tp.tpconv_radial_backward(plan, graph, x, Y, hh, MM, G, r_dx, r_dY, r_dh, need=(True, True, True, False))
+            ev[2].record(stream)
+            tp.tpconv_radial_backward(plan, graph, x, Y, hh, MM, G, r_dx, r_dY, r_dh, r_dW)
+            ev[3].record(stream)
+            torch.matmul(hh.t(), r_dW, out=r_dM)
+            ev[4].record(stream)
+            torch.matmul(hh, MM, out=Wu)
+            ev[5].record(stream)
+            tp.tpconv_forward(plan, graph, x, Y, Wu, out)
+            ev[6].record(stream)
+            tp.tpconv_backward(plan, graph, x, Y, Wu, G, dx, dY, dW)
+            ev[7].record(stream)
+            torch.matmul(dW, MM.t(), out=r_dh)
+            ev[8].record(stream)
+            torch.matmul(hh.t(), dW, out=r_dM)
+            ev[9].record(stream)
+        torch.cuda.synchronize()
+        rm = [float(np.median([e[i].elapsed_time(e[i + 1]) for e in rev[2:]])) for i in range(9)]
+        fused_inf = rm[0] + rm[1]
+        unfused_inf = rm[4] + rm[5] + rm[6] + rm[7]
+        fused_train = rm[0] + rm[2] + rm[3]
+        unfused_train = unfused_inf + rm[8]
+        gemm_flops = 2.0 * E * H * plan.weight_numel
+        radial = {"hidden": H, "weight_columns": plan.weight_numel, "reps": args.radial_reps,
+                  "fused": {"forward_ms": round(rm[0], 4), "backward_x_Y_h_ms": round(rm[1], 4),
+                            "backward_x_Y_h_W_ms": round(rm[2], 4), "grad_M_gemm_ms": round(rm[3], 4)},
+                  "unfused": {"W_gemm_ms": round(rm[4], 4), "forward_ms": round(rm[5], 4),
+                              "backward_ms": round(rm[6], 4), "grad_h_gemm_ms": round(rm[7], 4),
+                              "grad_M_gemm_ms": round(rm[8], 4)},
+                  "inference_ms": {"fused": round(fused_inf, 4), "unfused": round(unfused_inf, 4),
+                                   "speedup": round(unfused_inf / fused_inf, 3)},
+                  "training_ms": {"fused": round(fused_train, 4), "unfused": round(unfused_train, 4),
+                                  "speedup": round(unfused_train / fused_train, 3)},
+                  "fused_forward_W_TFLOPs": round(gemm_flops / (rm[0] * 1e-3) / 1e12, 2),
+                  "W_bytes_not_moved": int(E * plan.weight_numel * 4)}
+        del hh, MM, r_out, r_dx, r_dY, r_dh, r_dW, r_dM, Wu
+
     b = 4 if w.dtype == "f32" else 8
     fwd_bytes, bwd_bytes = algorithmic_bytes(plan, N, E, b)
     f_avg, b_avg = float(fwd_ms.mean()), float(bwd_ms.mean())
@@ -413,6 +474,7 @@ def main():
         "double_backward": dd,
         "upstream": up,
         "so2": so2,
+        "radial": radial,
         "hbm": {"fwd_bwd_algorithmic_GBps": round(hbm_fwdbwd, 1), "frac_of_peak": round(hbm_fwdbwd / HBM_PEAK_GBS, 4),
                 "fwd_bytes": int(fwd_bytes), "bwd_bytes": int(bwd_bytes),
                 "copy_1GiB_GBps": round(copy_gbs, 1), "frac_of_copy": round(hbm_fwdbwd / copy_gbs, 4)},

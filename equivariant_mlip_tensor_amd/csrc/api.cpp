@@ -220,6 +220,101 @@ extern "C" tpconv_status tpconv_backward(tpconv_plan_t hp, tpconv_graph_t hg, co
   return TPCONV_OK;
 }
 
+namespace {
+using RadialLauncher = hipError_t (*)(bool, const KernelArgs&, const float*, const float*, float*, int, hipStream_t);
+
+RadialLauncher pick_radial(int L) {
+  switch (L) {
+    case 0: return launch_radial_l0_f32;
+    case 1: return launch_radial_l1_f32;
+    case 2: return launch_radial_l2_f32;
+    case 3: return launch_radial_l3_f32;
+    case 4: return launch_radial_l4_f32;
+    default: return nullptr;
+  }
+}
+
+// Checks shared by the two radial entry points; lgH = log2(hidden) on success.
+tpconv_status radial_check(const Plan& p, const KernelArgs& a, int hidden, const void* h, const void* M,
+                           int64_t n_edges, int& lgH) {
+  if (p.dtype != TPCONV_F32 || !a.full_plan || (p.mul != 16 && p.mul != 32 && p.mul != 64) || !p.passes.empty())
+    return fail(TPCONV_E_UNSUPPORTED,
+                "radial weights: fp32 plans with segments l = 0..L in order, natural parity, SH up to L and "
+                "U in {16, 32, 64}");
+  lgH = 0;
+  while ((1 << lgH) < hidden) ++lgH;
+  if (hidden < 16 || hidden > 128 || (1 << lgH) != hidden)
+    return fail(TPCONV_E_UNSUPPORTED, "radial weights: hidden width must be 16, 32, 64 or 128");
+  if (n_edges > 0 && (h == nullptr || M == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL h or M");
+  if (reinterpret_cast<uintptr_t>(M) % 16 != 0 || reinterpret_cast<uintptr_t>(h) % 16 != 0)
+    return fail(TPCONV_E_INVALID_ARG, "radial weights: h and M must be 16-byte aligned");
+  return TPCONV_OK;
+}
+}  // namespace
+
+extern "C" tpconv_status tpconv_radial_forward(tpconv_plan_t hp, tpconv_graph_t hg, int hidden, const void* x,
+                                               const void* Y, const void* h, const void* M, void* out,
+                                               hipStream_t stream) {
+  if (hp == nullptr || hg == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL plan or graph");
+  const Plan& p = *reinterpret_cast<const Plan*>(hp);
+  const Graph& g = *reinterpret_cast<const Graph*>(hg);
+  KernelArgs a = base_args(p, g.n_nodes);
+  int lgH = 0;
+  const tpconv_status st = radial_check(p, a, hidden, h, M, g.n_edges, lgH);
+  if (st != TPCONV_OK) return st;
+  if (g.n_nodes > 0 && (out == nullptr || x == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL x or out");
+  if (g.n_edges > 0 && Y == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL Y");
+  if (g.n_nodes == 0) return TPCONV_OK;
+  RadialLauncher f = pick_radial(p.kernel_l);
+  if (f == nullptr) return fail(TPCONV_E_UNSUPPORTED, "no kernel for this l bound");
+  a.row_ptr = g.dst_row;
+  a.col = g.dst_col;
+  a.eid = g.dst_eid;
+  a.order = g.dst_order;
+  a.x = x;
+  a.Y = Y;
+  a.out = out;
+  const hipError_t he = f(true, a, static_cast<const float*>(h), static_cast<const float*>(M), nullptr, lgH, stream);
+  if (he == hipErrorInvalidValue) return fail(TPCONV_E_UNSUPPORTED, "radial weights: this plan's W tile exceeds LDS");
+  if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("radial forward launch: ") + hipGetErrorString(he));
+  return TPCONV_OK;
+}
+
+extern "C" tpconv_status tpconv_radial_backward(tpconv_plan_t hp, tpconv_graph_t hg, int hidden, const void* x,
+                                                const void* Y, const void* h, const void* M, const void* grad_out,
+                                                void* grad_x, void* grad_Y, void* grad_h, void* grad_W,
+                                                hipStream_t stream) {
+  if (hp == nullptr || hg == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL plan or graph");
+  const Plan& p = *reinterpret_cast<const Plan*>(hp);
+  const Graph& g = *reinterpret_cast<const Graph*>(hg);
+  KernelArgs a = base_args(p, g.n_nodes);
+  int lgH = 0;
+  const tpconv_status st = radial_check(p, a, hidden, h, M, g.n_edges, lgH);
+  if (st != TPCONV_OK) return st;
+  const bool want_edges = g.n_edges > 0 && (grad_Y != nullptr || grad_h != nullptr || grad_W != nullptr);
+  if (grad_x == nullptr && !want_edges) return TPCONV_OK;
+  if (g.n_nodes > 0 && (x == nullptr || grad_out == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL x or grad_out");
+  if (g.n_edges > 0 && Y == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL Y");
+  if (g.n_nodes == 0) return TPCONV_OK;
+  RadialLauncher f = pick_radial(p.kernel_l);
+  if (f == nullptr) return fail(TPCONV_E_UNSUPPORTED, "no kernel for this l bound");
+  a.row_ptr = g.src_row;
+  a.col = g.src_col;
+  a.eid = g.src_eid;
+  a.order = g.src_order;
+  a.x = x;
+  a.Y = Y;
+  a.G = grad_out;
+  a.out = grad_x;
+  a.dY = grad_Y;
+  a.dW = grad_W;
+  const hipError_t he = f(false, a, static_cast<const float*>(h), static_cast<const float*>(M),
+                          static_cast<float*>(grad_h), lgH, stream);
+  if (he == hipErrorInvalidValue) return fail(TPCONV_E_UNSUPPORTED, "radial weights: this plan's W tile exceeds LDS");
+  if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("radial backward launch: ") + hipGetErrorString(he));
+  return TPCONV_OK;
+}
+
 extern "C" tpconv_status tpconv_double_backward(tpconv_plan_t hp, tpconv_graph_t hg, const void* x, const void* Y,
                                                 const void* W, const void* grad_out, const void* ggx,
                                                 const void* ggY, const void* ggW, void* grad_x, void* grad_Y,

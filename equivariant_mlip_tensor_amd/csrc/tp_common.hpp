@@ -83,7 +83,9 @@ struct KernelArgs {
 
 // Launchers, one per (lmax, dtype), defined by tp_kernels.hip compiled once
 // per (lmax, dtype, TPCONV_DD): fwd/bwd with TPCONV_DD=0, and the double
-// backward's two passes ddf (grad_G) / ddb (grad_x, grad_Y, grad_W) with 1.
+// backward's two passes ddf (grad_G) / ddb (grad_x, grad_Y, grad_W) with 1;
+// radial: the forward (fwd) or backward with W = h M generated in-kernel
+// (fp32 units with TPCONV_DD=0, compile-time plans only).
 #define TPCONV_DECLARE_LAUNCHERS(L)                                                \
   hipError_t launch_fwd_l##L##_f32(const KernelArgs& a, hipStream_t s);            \
   hipError_t launch_fwd_l##L##_f64(const KernelArgs& a, hipStream_t s);            \
@@ -92,7 +94,9 @@ struct KernelArgs {
   hipError_t launch_ddf_l##L##_f32(const KernelArgs& a, hipStream_t s);            \
   hipError_t launch_ddf_l##L##_f64(const KernelArgs& a, hipStream_t s);            \
   hipError_t launch_ddb_l##L##_f32(const KernelArgs& a, hipStream_t s);            \
-  hipError_t launch_ddb_l##L##_f64(const KernelArgs& a, hipStream_t s);
+  hipError_t launch_ddb_l##L##_f64(const KernelArgs& a, hipStream_t s);            \
+  hipError_t launch_radial_l##L##_f32(bool fwd, const KernelArgs& a, const float* h, const float* M,  \
+                                      float* dh, int lgH, hipStream_t s);
 
 TPCONV_DECLARE_LAUNCHERS(0)
 TPCONV_DECLARE_LAUNCHERS(1)

@@ -1460,6 +1460,390 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
   }
 }
 
+#if !TPCONV_DD && !TPCONV_DOUBLE
+// ------------------------------------------- weights from the radial network
+// W = h M, with h [E][H] the edges' hidden features and M [H][P U] the radial
+// network's last layer (columns in W's order), generated chunk by chunk on
+// the matrix cores into LDS and consumed there, so W never reaches HBM (the
+// TrimSO(2) abstract names materialised per-edge tensors as the cost to
+// avoid).  One CSR row per block of four wavefronts (eight for U = 64;
+// compile-time plans).
+// Per chunk of 16 of the row's edges:
+//   1. the chunk's h rows go to LDS (zero rows past the row's end);
+//   2. v_mfma_f32_16x16x4f32 with M = the 16 edges, N = W's columns, K = H:
+//      wavefront w takes the column tiles w, w + 4, ...; K runs in units of
+//      16 (step s of unit g uses k = 16 g + 4 kq + s), so a lane's four A
+//      values of a unit are one 16-byte LDS read; B (rows of M) comes from
+//      L2, the next tile's values in flight while a tile runs; the results
+//      fill an LDS tile [edge][column];
+//   3. the tensor product of the chunk's edges, the wavefront's slots side
+//      by side as in the forward kernel, with the weights read from the tile.
+// The backward walks the source-sorted rows the same way: each edge's dW
+// overwrites its W in the tile (a lane reads all of its weights before it
+// writes any), and then dh = dW M^T runs on the matrix cores (M = edges,
+// N = hidden, K = W's columns in units of 16, 16-byte loads of M's rows);
+// dW also goes to HBM when asked for (the layer's own gradient
+// dM = h^T dW is then a plain product outside).  Row sums are fp64 per lane;
+// the wavefronts' sums meet in LDS at the row's end.
+typedef float rv4f __attribute__((ext_vector_type(4)));
+
+// M's address, opaque to the compiler at each use: M's values are the same
+// for every chunk, and without this the loads of every chunk's products are
+// hoisted out of the chunk loop and held in (spilled) registers
+__device__ __forceinline__ const float* radial_opaque(const float* p) {
+  int z;
+  asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+  return p + z;
+}
+
+__device__ __forceinline__ rv4f rmfma(float a, float b, rv4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+constexpr int kRMaxLgH = 7;  // H = 16 .. 128; the h tile [16][H + 4] is dynamic LDS
+
+template <int L, int U>
+struct RShape {
+  static constexpr int WS = U * even_count(L);  // W's columns
+  static constexpr int SW = WS + 4;             // LDS row stride of the W tile (floats)
+  static constexpr int NTILE = WS / 16;
+  // wavefronts per block: the W tile of U = 64 fills most of a CU's LDS, so
+  // its block has eight wavefronts (two per SIMD) instead of four
+  static constexpr int NW = U == 64 ? 8 : 4;
+  static constexpr bool kFits = (16 * SW + 16 * ((1 << kRMaxLgH) + 4)) * 4 <= 160 * 1024;
+  static_assert(WS % 16 == 0, "W's columns come in tiles of 16");
+};
+
+// the chunk's h rows (cn of them) into sH; zero rows after them
+__device__ __forceinline__ void radial_stage_h(float* sH, const float* __restrict__ hp, int lgH,
+                                               const int32_t* __restrict__ eid, int c0, int cn) {
+  const int H = 1 << lgH;
+  for (int i = threadIdx.x; i < 16 * H; i += blockDim.x) {
+    const int r = i >> lgH, k = i & (H - 1);
+    sH[r * (H + 4) + k] = r < cn ? hp[(int64_t)eid[c0 + r] * H + k] : 0.f;
+  }
+}
+
+// sW[e][c] = sum_k sH[e][k] M[k][c] for this wavefront's column tiles
+// (wave, wave + nw, ...)
+template <int WS, int SW, int HQ>
+__device__ __forceinline__ void radial_gen_w(float* sW, const float* sH, const float* __restrict__ Mw, int wave,
+                                             int nw, int lane) {
+  constexpr int NTILE = WS / 16;
+  Mw = radial_opaque(Mw);
+  const int er = lane & 15, kq = lane >> 4;
+  rv4f af[HQ];
+  static_for<HQ>([&](auto G) {
+    af[G] = *reinterpret_cast<const rv4f*>(&sH[er * (16 * HQ + 4) + 16 * int(G) + 4 * kq]);
+  });
+  auto load_b = [&](int n, float (&b)[4 * HQ]) {
+    const float* mc = Mw + 16 * n + er;
+    static_for<HQ>([&](auto G) {
+      static_for<4>([&](auto S) { b[4 * G + S] = mc[(int64_t)(16 * int(G) + 4 * kq + int(S)) * WS]; });
+    });
+  };
+  // the next tile's B values are loaded once this tile's products are issued
+  float b[4 * HQ];
+  if (wave < NTILE) load_b(wave, b);
+  for (int n = wave; n < NTILE; n += nw) {
+    rv4f acc = {0.f, 0.f, 0.f, 0.f};
+    static_for<HQ>([&](auto G) {
+      static_for<4>([&](auto S) { acc = rmfma(af[G][int(S)], b[4 * G + S], acc); });
+    });
+    if (n + nw < NTILE) load_b(n + nw, b);
+    static_for<4>([&](auto R) { sW[(4 * kq + int(R)) * SW + 16 * n + er] = acc[int(R)]; });
+  }
+}
+
+template <int WS, int SW>
+__device__ __forceinline__ void radial_gen_w_any(float* sW, const float* sH, const float* __restrict__ Mw, int lgH,
+                                                 int wave, int nw, int lane) {
+  switch (lgH) {
+    case 4: radial_gen_w<WS, SW, 1>(sW, sH, Mw, wave, nw, lane); break;
+    case 5: radial_gen_w<WS, SW, 2>(sW, sH, Mw, wave, nw, lane); break;
+    case 6: radial_gen_w<WS, SW, 4>(sW, sH, Mw, wave, nw, lane); break;
+    default: radial_gen_w<WS, SW, 8>(sW, sH, Mw, wave, nw, lane); break;
+  }
+}
+
+// dh[e][j] = sum_c sW[e][c] M[j][c] for the chunk's cn edges; wavefront w
+// takes the hidden tiles w, w + nw, ...
+template <int WS, int SW>
+__device__ __forceinline__ void radial_gen_dh(const float* sW, const float* __restrict__ Mw,
+                                              float* __restrict__ dh, int lgH, const int32_t* __restrict__ eid,
+                                              int c0, int cn, int wave, int nw, int lane) {
+  const int er = lane & 15, kq = lane >> 4;
+  const int H = 1 << lgH;
+  Mw = radial_opaque(Mw);
+  for (int n = wave; n < (H >> 4); n += nw) {
+    rv4f acc = {0.f, 0.f, 0.f, 0.f};
+    const float* mrow = Mw + (int64_t)(16 * n + er) * WS + 4 * kq;
+    const float* arow = sW + er * SW + 4 * kq;
+    // four units of K per trip, the trips kept rolled (a fully unrolled loop
+    // reads the whole tile row into registers up front)
+    constexpr int NG = WS / 16;
+#pragma unroll 1
+    for (int g0 = 0; g0 < NG; g0 += 4) {
+      static_for<4>([&](auto I) {
+        const int g = g0 + int(I);
+        if (NG % 4 == 0 || g < NG) {
+          const rv4f bv = *reinterpret_cast<const rv4f*>(mrow + 16 * g);
+          const rv4f av = *reinterpret_cast<const rv4f*>(arow + 16 * g);
+          static_for<4>([&](auto S) { acc = rmfma(av[int(S)], bv[int(S)], acc); });
+        }
+      });
+    }
+    static_for<4>([&](auto R) {
+      const int r = 4 * kq + int(R);
+      if (r < cn) dh[(int64_t)eid[c0 + r] * H + 16 * n + er] = acc[int(R)];
+    });
+  }
+}
+
+// Forward with W = h M: out = the convolution (destination-sorted rows).
+template <int L, int U>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, 64 * RShape<L, U>::NW))) void rfwd_kernel(const KernelArgs a, const float* __restrict__ hp,
+                                                   const float* __restrict__ Mw, int lgH) {
+  using P = FullPlan<L, U>;
+  using F = Fwd<float, L, P>;
+  using S = RShape<L, U>;
+  constexpr int NL = F::NL, NT = F::NT;
+  constexpr int NSL = 64 >> P::kLg;
+  __shared__ __attribute__((aligned(16))) float sW[16 * S::SW];
+  extern __shared__ __attribute__((aligned(16))) float sH[];  // [16][H + 4], sized at launch
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int node = a.order[blockIdx.x];
+  const int slot = lane >> P::kLg, u = lane & (U - 1);
+  const float* __restrict__ X = static_cast<const float*>(a.x);
+  const float* __restrict__ Yp = static_cast<const float*>(a.Y);
+  const int beg = a.row_ptr[node], end = a.row_ptr[node + 1];
+  double rs[NL];
+  static_for<NL>([&](auto I) { rs[I] = 0.0; });
+  // (Requesting a step's inputs before the products, as the backward does,
+  // costs the registers of a third wavefront per SIMD here and measured
+  // slower.)
+  for (int c0 = beg; c0 < end; c0 += 16) {
+    const int cn = min(16, end - c0);
+    radial_stage_h(sH, hp, lgH, a.eid, c0, cn);
+    __syncthreads();
+    radial_gen_w_any<S::WS, S::SW>(sW, sH, Mw, lgH, wave, S::NW, lane);
+    __syncthreads();
+#pragma unroll 1
+    for (int q0 = 0; q0 < cn; q0 += S::NW * NSL) {
+      const int q = q0 + wave * NSL + slot;
+      if (q < cn) {
+        const int e = a.eid[c0 + q], j = a.col[c0 + q];
+        float x[NL], y[NL], w[NT];
+        const float* xr = X + (int64_t)j * P::kD;
+        static_for<L + 1>([&](auto I) {
+          constexpr int l = I;
+          static_for<2 * l + 1>([&](auto M) { x[l * l + M] = xr[U * l * l + u * (2 * l + 1) + M]; });
+        });
+        const float* yr = Yp + (int64_t)e * NL;
+        static_for<NL>([&](auto I) { y[I] = ldg_stream(yr + I); });
+        const float* wr = sW + q * S::SW + u;
+        static_for<NT>([&](auto I) {
+          if constexpr (P::template on<I>(a)) w[I] = wr[P::template woff<I>(a)];
+          else w[I] = 0.f;
+        });
+        float te[NL];
+        F::edge(a, __builtin_amdgcn_readfirstlane(e), x, y, w, te);
+        static_for<NL>([&](auto I) { rs[I] += static_cast<double>(te[I]); });
+      }
+    }
+    __syncthreads();  // the next chunk overwrites sH and sW
+  }
+  // the wavefronts' row sums meet in LDS (over the W tile, or a buffer
+  // of its own where the tile is too small), then the slots' by shuffles
+  constexpr bool kAlias = 16 * S::SW * 4 >= S::NW * NL * 64 * 8;
+  __shared__ double s_red[kAlias ? 1 : S::NW * NL * 64];
+  double* red = kAlias ? reinterpret_cast<double*>(sW) : s_red;
+  static_for<NL>([&](auto I) { red[(wave * NL + I) * 64 + lane] = rs[I]; });
+  __syncthreads();
+  if (wave != 0) return;
+  static_for<NL>([&](auto I) {
+    double t = red[I * 64 + lane];
+    static_for<S::NW - 1>([&](auto V) { t += red[((int(V) + 1) * NL + I) * 64 + lane]; });
+    rs[I] = t;
+  });
+  for (int off = U; off < 64; off <<= 1) {
+    static_for<NL>([&](auto I) { rs[I] += __shfl_xor(rs[I], off, 64); });
+  }
+  if (slot == 0) {
+    float* orow = static_cast<float*>(a.out) + (int64_t)node * P::kD;
+    static_for<L + 1>([&](auto I) {
+      constexpr int l = I;
+      static_for<2 * l + 1>([&](auto M) { orow[U * l * l + u * (2 * l + 1) + M] = static_cast<float>(rs[l * l + M]); });
+    });
+  }
+}
+
+// Backward with W = h M (source-sorted rows): grad_x (a.out), grad_Y
+// (a.dY), dh, and grad_W (a.dW) when not null; each output may be null.
+template <int L, int U>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, 64 * RShape<L, U>::NW))) void rbwd_kernel(const KernelArgs a, const float* __restrict__ hp,
+                                                   const float* __restrict__ Mw, float* __restrict__ dh, int lgH) {
+  using P = FullPlan<L, U>;
+  using B = Bwd<float, L, P>;
+  using S = RShape<L, U>;
+  constexpr int NL = B::NL, NT = B::NT;
+  constexpr int NV = pow2_ceil(NL);
+  constexpr int NSL = 64 >> P::kLg;
+  __shared__ __attribute__((aligned(16))) float sW[16 * S::SW];
+  extern __shared__ __attribute__((aligned(16))) float sH[];  // [16][H + 4], sized at launch
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int node = a.order[blockIdx.x];
+  const int slot = lane >> P::kLg, u = lane & (U - 1);
+  const float* __restrict__ Yp = static_cast<const float*>(a.Y);
+  const float* __restrict__ Gp = static_cast<const float*>(a.G);
+  float* __restrict__ DX = static_cast<float*>(a.out);
+  float* __restrict__ DY = static_cast<float*>(a.dY);
+  float* __restrict__ DW = static_cast<float*>(a.dW);
+  float x[NL];
+  {
+    const float* xr = static_cast<const float*>(a.x) + (int64_t)node * P::kD;
+    static_for<L + 1>([&](auto I) {
+      constexpr int l = I;
+      static_for<2 * l + 1>([&](auto M) { x[l * l + M] = xr[U * l * l + u * (2 * l + 1) + M]; });
+    });
+  }
+  double dxa[NL];
+  static_for<NL>([&](auto I) { dxa[I] = 0.0; });
+  const int beg = a.row_ptr[node], end = a.row_ptr[node + 1];
+  // A slot past the chunk's end works on the chunk's first edge (valid
+  // addresses) and stores nothing, so the dY shuffles stay converged; a
+  // wavefront with no edge left skips the step.
+  auto load_in = [&](int c0, int q, int& e, float (&g)[NL], float (&y)[NL]) {
+    e = a.eid[c0 + q];
+    const float* gr = Gp + (int64_t)a.col[c0 + q] * P::kD;
+    static_for<L + 1>([&](auto I) {
+      constexpr int l = I;
+      static_for<2 * l + 1>([&](auto M) { g[l * l + M] = gr[U * l * l + u * (2 * l + 1) + M]; });
+    });
+    const float* yr = Yp + (int64_t)e * NL;
+    static_for<NL>([&](auto I) { y[I] = ldg_stream(yr + I); });
+  };
+  auto step = [&](int q, bool valid, int e, const float (&g)[NL], const float (&y)[NL]) {
+    float w[NT];
+    float* wr = sW + q * S::SW + u;
+    static_for<NT>([&](auto I) {
+      if constexpr (P::template on<I>(a)) w[I] = wr[P::template woff<I>(a)];
+      else w[I] = 0.f;
+    });
+    float dya[NV], dxe[NL];
+    static_for<NV>([&](auto I) { dya[I] = 0.f; });
+    B::edge(a, __builtin_amdgcn_readfirstlane(e), x, y, g, w, dxe, dya, valid, wr);  // dW over W in the tile
+    static_for<NL>([&](auto I) { dxa[I] += valid ? static_cast<double>(dxe[I]) : 0.0; });
+    if (DY != nullptr) {
+      // reduce-scatter of the NV dY values over the slot's U lanes (as in
+      // the backward kernel): lanes with bit b set keep the upper half
+      int base = 0, nv = NV;
+      static_for<6>([&](auto SS) {
+        constexpr int s = SS;
+        const int b = U >> (s + 1);
+        if (b >= 1) {
+          if constexpr ((NV >> s) > 1) {
+            constexpr int hh = NV >> (s + 1);
+            const bool upper = (u & b) != 0;
+            static_for<hh>([&](auto V) {
+              float lo = dya[V], hi = dya[V + hh];
+              pin_vgpr(lo);
+              pin_vgpr(hi);
+              const float keep = upper ? hi : lo;
+              const float send = upper ? lo : hi;
+              dya[V] = keep + __shfl_xor(send, b, 64);
+            });
+            if (upper) base += hh;
+            nv = hh;
+          } else {
+            dya[0] += __shfl_xor(dya[0], b, 64);
+          }
+        }
+      });
+      const int plain_mask = U > NV ? U / NV - 1 : 0;
+      if ((u & plain_mask) == 0 && valid) {
+        float* dyr = DY + (int64_t)e * NL;
+        static_for<NV>([&](auto V) {
+          if (V < nv && base + V < NL) dyr[base + V] = dya[V];
+        });
+      }
+    }
+  };
+  for (int c0 = beg; c0 < end; c0 += 16) {
+    const int cn = min(16, end - c0);
+    // the first step's inputs are requested before the products
+    const bool w0 = wave * NSL < cn;  // wavefront-uniform
+    const int q_0 = wave * NSL + slot;
+    const bool v_0 = q_0 < cn;
+    int e0 = 0;
+    float g0[NL], y0[NL];
+    if (w0) load_in(c0, v_0 ? q_0 : 0, e0, g0, y0);
+    radial_stage_h(sH, hp, lgH, a.eid, c0, cn);
+    __syncthreads();
+    radial_gen_w_any<S::WS, S::SW>(sW, sH, Mw, lgH, wave, S::NW, lane);
+    __syncthreads();
+    if (w0) step(v_0 ? q_0 : 0, v_0, e0, g0, y0);
+#pragma unroll 1
+    for (int q0 = S::NW * NSL; q0 + wave * NSL < cn; q0 += S::NW * NSL) {
+      const int q = q0 + wave * NSL + slot;
+      const bool valid = q < cn;
+      int e;
+      float g[NL], y[NL];
+      load_in(c0, valid ? q : 0, e, g, y);
+      step(valid ? q : 0, valid, e, g, y);
+    }
+    __syncthreads();  // the chunk's dW is complete in the tile
+    if (DW != nullptr) {
+      for (int t = threadIdx.x; t < cn * S::WS; t += 64 * S::NW) {
+        const int r = t / S::WS, c = t - r * S::WS;
+        __builtin_nontemporal_store(sW[r * S::SW + c], DW + (int64_t)a.eid[c0 + r] * S::WS + c);
+      }
+    }
+    if (dh != nullptr) radial_gen_dh<S::WS, S::SW>(sW, Mw, dh, lgH, a.eid, c0, cn, wave, S::NW, lane);
+    __syncthreads();  // the next chunk overwrites sH and sW
+  }
+  if (DX == nullptr) return;  // block-uniform
+  constexpr bool kAlias = 16 * S::SW * 4 >= S::NW * NL * 64 * 8;
+  __shared__ double s_red[kAlias ? 1 : S::NW * NL * 64];
+  double* red = kAlias ? reinterpret_cast<double*>(sW) : s_red;
+  static_for<NL>([&](auto I) { red[(wave * NL + I) * 64 + lane] = dxa[I]; });
+  __syncthreads();
+  if (wave != 0) return;
+  static_for<NL>([&](auto I) {
+    double t = red[I * 64 + lane];
+    static_for<S::NW - 1>([&](auto V) { t += red[((int(V) + 1) * NL + I) * 64 + lane]; });
+    dxa[I] = t;
+  });
+  for (int off = U; off < 64; off <<= 1) {
+    static_for<NL>([&](auto I) { dxa[I] += __shfl_xor(dxa[I], off, 64); });
+  }
+  if (slot == 0) {
+    float* drow = DX + (int64_t)node * P::kD;
+    static_for<L + 1>([&](auto I) {
+      constexpr int l = I;
+      static_for<2 * l + 1>([&](auto M) { drow[U * l * l + u * (2 * l + 1) + M] = static_cast<float>(dxa[l * l + M]); });
+    });
+  }
+}
+
+template <int U>
+hipError_t launch_radial_u(bool fwd, const KernelArgs& a, const float* h, const float* M, float* dh, int lgH,
+                           hipStream_t s) {
+  if constexpr (RShape<TPCONV_L, U>::kFits) {
+    const size_t lds_h = sizeof(float) * 16 * ((1 << lgH) + 4);
+    if (fwd)
+      hipLaunchKernelGGL((rfwd_kernel<TPCONV_L, U>), dim3(a.n_rows), dim3(64 * RShape<TPCONV_L, U>::NW), lds_h, s,
+                         a, h, M, lgH);
+    else
+      hipLaunchKernelGGL((rbwd_kernel<TPCONV_L, U>), dim3(a.n_rows), dim3(64 * RShape<TPCONV_L, U>::NW), lds_h, s,
+                         a, h, M, dh, lgH);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+#endif
+
 // ---------------------------------------------------------------- launchers
 constexpr bool kDD = TPCONV_DD != 0;
 
@@ -1553,6 +1937,17 @@ hipError_t TPCONV_LNAME(launch_bwd_l, _f64)(const KernelArgs& a, hipStream_t s) 
 #else
 hipError_t TPCONV_LNAME(launch_fwd_l, _f32)(const KernelArgs& a, hipStream_t s) { return dispatch<float, true>(a, s); }
 hipError_t TPCONV_LNAME(launch_bwd_l, _f32)(const KernelArgs& a, hipStream_t s) { return dispatch<float, false>(a, s); }
+hipError_t TPCONV_LNAME(launch_radial_l, _f32)(bool fwd, const KernelArgs& a, const float* h, const float* M,
+                                                float* dh, int lgH, hipStream_t s) {
+  if (a.n_rows <= 0) return hipSuccess;
+  if (!a.full_plan || lgH < 4 || lgH > kRMaxLgH) return hipErrorInvalidValue;
+  switch (a.mul) {
+    case 16: return launch_radial_u<16>(fwd, a, h, M, dh, lgH, s);
+    case 32: return launch_radial_u<32>(fwd, a, h, M, dh, lgH, s);
+    case 64: return launch_radial_u<64>(fwd, a, h, M, dh, lgH, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 #endif
 #endif
 

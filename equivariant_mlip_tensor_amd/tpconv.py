@@ -29,7 +29,8 @@ STATUS = {0: "TPCONV_OK", 1: "TPCONV_E_INVALID_ARG", 2: "TPCONV_E_IRREPS", 3: "T
 
 EXPORTS = ("tpconv_plan", "tpconv_plan_query", "tpconv_plan_paths", "tpconv_plan_table", "tpconv_plan_destroy",
            "tpconv_graph_workspace_bytes", "tpconv_graph_create", "tpconv_graph_export", "tpconv_graph_destroy",
-           "tpconv_forward", "tpconv_backward", "tpconv_double_backward", "tpconv_sh", "tpconv_sh_backward",
+           "tpconv_forward", "tpconv_backward", "tpconv_double_backward", "tpconv_radial_forward",
+           "tpconv_radial_backward", "tpconv_sh", "tpconv_sh_backward",
            "tpconv_positions_backward", "tpconv_so2_weight_numel", "tpconv_so2_rotations", "tpconv_so2_forward",
            "tpconv_so2_workspace_bytes", "tpconv_so2_backward", "tpconv_so2_backward_noalloc",
            "tpconv_so2_double_backward",
@@ -68,6 +69,8 @@ def _load():
         "tpconv_graph_create": (i32, [i64, i64, vp, vp, vp, sz, vp, ctypes.POINTER(vp)]),
         "tpconv_graph_export": (i32, [vp, vp, vp, vp, vp, vp, vp, vp]),
         "tpconv_graph_destroy": (None, [vp]),
+        "tpconv_radial_forward": (i32, [vp, vp, i32, vp, vp, vp, vp, vp, vp]),
+        "tpconv_radial_backward": (i32, [vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "tpconv_forward": (i32, [vp, vp, vp, vp, vp, vp, vp]),
         "tpconv_backward": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "tpconv_double_backward": (i32, [vp] * 14),
@@ -285,6 +288,51 @@ def tpconv_backward(plan: Plan, graph: Graph, x, Y, W, grad_out, grad_x=None, gr
     _check(_lib.tpconv_backward(plan.handle, graph.handle, _ptr(x), _ptr(Y), _ptr(W), _ptr(grad_out),
                                 _ptr(grad_x), _ptr(grad_Y), _ptr(grad_W), _stream_handle(stream)))
     return grad_x, grad_Y, grad_W
+
+
+@_on_launch_stream
+def tpconv_radial_forward(plan: Plan, graph: Graph, x, Y, h, M, out=None, stream=None) -> torch.Tensor:
+    """out = tpconv_forward(x, Y, W = h @ M) with W generated inside the kernel.
+    h: [E, hidden], M: [hidden, weight_numel], fp32, hidden in 16/32/64/128."""
+    N, E, dt = graph.n_nodes, graph.n_edges, plan.torch_dtype
+    H = int(M.shape[0])
+    _need(x, (N, plan.dim_in), dt, "x")
+    _need(Y, (E, plan.dim_sh), dt, "Y")
+    _need(h, (E, H), dt, "h")
+    _need(M, (H, plan.weight_numel), dt, "M")
+    if out is None:
+        out = torch.empty((N, plan.dim_out), dtype=dt, device=x.device)
+    _need(out, (N, plan.dim_out), dt, "out")
+    _check(_lib.tpconv_radial_forward(plan.handle, graph.handle, H, _ptr(x), _ptr(Y), _ptr(h), _ptr(M), _ptr(out),
+                                      _stream_handle(stream)))
+    return out
+
+
+@_on_launch_stream
+def tpconv_radial_backward(plan: Plan, graph: Graph, x, Y, h, M, grad_out, grad_x=None, grad_Y=None, grad_h=None,
+                           grad_W=None, need=(True, True, True, False),
+                           stream=None) -> Tuple[Optional[torch.Tensor], ...]:
+    """(grad_x, grad_Y, grad_h, grad_W) of <grad_out, tpconv_radial_forward(...)>;
+    grad_W (for the caller's grad_M = h^T grad_W) only when need[3]; an output
+    is None when `need` turns it off."""
+    N, E, dt = graph.n_nodes, graph.n_edges, plan.torch_dtype
+    H = int(M.shape[0])
+    _need(x, (N, plan.dim_in), dt, "x")
+    _need(Y, (E, plan.dim_sh), dt, "Y")
+    _need(h, (E, H), dt, "h")
+    _need(M, (H, plan.weight_numel), dt, "M")
+    _need(grad_out, (N, plan.dim_out), dt, "grad_out")
+    dev = x.device
+    shapes = ((N, plan.dim_in), (E, plan.dim_sh), (E, H), (E, plan.weight_numel))
+    outs = [grad_x, grad_Y, grad_h, grad_W]
+    for k, (t, shp, nm) in enumerate(zip(outs, shapes, ("grad_x", "grad_Y", "grad_h", "grad_W"))):
+        if need[k] and t is None:
+            outs[k] = t = torch.empty(shp, dtype=dt, device=dev)
+        if t is not None:
+            _need(t, shp, dt, nm)
+    _check(_lib.tpconv_radial_backward(plan.handle, graph.handle, H, _ptr(x), _ptr(Y), _ptr(h), _ptr(M),
+                                       _ptr(grad_out), *[_ptr(t) for t in outs], _stream_handle(stream)))
+    return tuple(outs)
 
 
 @_on_launch_stream

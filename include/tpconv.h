@@ -217,6 +217,39 @@ tpconv_status tpconv_double_backward(tpconv_plan_t plan, tpconv_graph_t g, const
                                      const void* ggW, void* grad_x, void* grad_Y, void* grad_W, void* grad_G,
                                      hipStream_t stream);
 
+/* ------------------------------------ weights from the radial network --
+ * The per-edge weights W [E][weight_numel] are the widest tensor of the
+ * layer (the TrimSO(2) abstract names materialised per-edge tensors as the
+ * cost to avoid).  In a potential they come from a radial network; its last,
+ * linear layer is W = h M, with h [E][hidden] the edges' hidden features
+ * (the output of the network's earlier, narrow layers on the edge lengths,
+ * computed by the caller) and M [hidden][weight_numel] (columns in W's
+ * order; a bias is a constant feature in h).  These two calls take h and M
+ * instead of W and generate W inside the kernels, chunk by chunk on the
+ * matrix cores into LDS: W is never written to or read from device memory.
+ *
+ * Supported: fp32 plans whose segments are l = 0..L in order with natural
+ * parity on both sides and SH up to L, one multiplicity U in {16, 32, 64},
+ * hidden in {16, 32, 64, 128}; h and M device pointers, 16-byte aligned.
+ * Other plans or widths: TPCONV_E_UNSUPPORTED (use tpconv_forward /
+ * tpconv_backward with W = h M formed by the caller).
+ *
+ * tpconv_radial_forward: out = tpconv_forward(x, Y, W = h M), overwritten.
+ * Errors as tpconv_forward, plus TPCONV_E_UNSUPPORTED as above. */
+tpconv_status tpconv_radial_forward(tpconv_plan_t plan, tpconv_graph_t g, int hidden, const void* x,
+                                    const void* Y, const void* h, const void* M, void* out, hipStream_t stream);
+
+/* tpconv_radial_backward: gradients of <G, out> for G = grad_out, with
+ * W = h M generated in-kernel: grad_x [N][D_in], grad_Y [E][D_sh] and
+ * grad_h [E][hidden] = grad_W M^T; and, when grad_W is not NULL, grad_W
+ * [E][weight_numel] itself, from which the caller forms the layer's own
+ * gradient grad_M = h^T grad_W (training; inference with forces needs only
+ * grad_x, grad_Y and grad_h).  Each output is overwritten; NULL skips one.
+ * Errors as tpconv_radial_forward. */
+tpconv_status tpconv_radial_backward(tpconv_plan_t plan, tpconv_graph_t g, int hidden, const void* x,
+                                     const void* Y, const void* h, const void* M, const void* grad_out,
+                                     void* grad_x, void* grad_Y, void* grad_h, void* grad_W, hipStream_t stream);
+
 /* ------------------------------------------- upstream: harmonics, forces --
  * The step before the convolution in a force field: the edge harmonics Y
  * from the edge vectors, and the chain rule from grad_Y back to the edge

@@ -36,7 +36,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(tp):
     declared = header_functions()
-    assert len(declared) == 28
+    assert len(declared) == 30
     assert sorted(tp.EXPORTS) == declared
     lib = ctypes.CDLL(LIB)
     for name in declared:
@@ -180,4 +180,23 @@ def test_so2_sizes_and_errors_need_no_gpu(tp):
     assert lib.tpconv_so2_backward(fake, 2, 64, 0, *([None] * 7), 0, None) == 3
     assert lib.tpconv_so2_backward_noalloc(fake, 2, 64, 0, *([None] * 7)) == 3
     assert lib.tpconv_so2_backward_noalloc(fake, 2, 16, 1, *([None] * 7)) == 3
+
+
+def test_radial_refusals_need_no_gpu(tp):
+    # a zeroed graph struct: no nodes, no edges (nothing is launched)
+    lib = tp._lib
+    buf = (ctypes.c_uint8 * 256)()
+    g = ctypes.c_void_p(ctypes.addressof(buf))
+    f32 = tp.tpconv_plan("16x0e+16x1o", 1, "16x0e+16x1o", "f32")
+    f64 = tp.tpconv_plan("16x0e+16x1o", 1, "16x0e+16x1o", "f64")
+    odd = tp.tpconv_plan("8x0e+8x1o", 1, "8x0e+8x1o", "f32")
+    assert lib.tpconv_radial_forward(None, g, 16, *([None] * 5), None) == 1
+    assert lib.tpconv_radial_forward(f32.handle, g, 16, *([None] * 5), None) == 0       # nothing to do
+    assert lib.tpconv_radial_forward(f64.handle, g, 16, *([None] * 5), None) == 3
+    assert lib.tpconv_radial_forward(odd.handle, g, 16, *([None] * 5), None) == 3       # U = 8
+    for H in (8, 24, 48, 256):
+        assert lib.tpconv_radial_forward(f32.handle, g, H, *([None] * 5), None) == 3
+        assert lib.tpconv_radial_backward(f32.handle, g, H, *([None] * 9), None) == 3
+    assert lib.tpconv_radial_backward(f32.handle, g, 64, *([None] * 9), None) == 0
+    assert "hidden" in tp.tpconv_last_error() or tp.tpconv_last_error()
 
