@@ -315,7 +315,6 @@ __global__ __launch_bounds__(128, 2) void k_so2_conv(const int32_t* __restrict__
   static_assert(!(TWO && FRAMES), "two rotations only in the plain convolution");
   __shared__ float tile[S::kEdges * S::PAD];
   __shared__ float dl[S::kEdges * S::NDP];
-  __shared__ float dl2[TWO ? S::kEdges * S::NDP : 1];
   __shared__ float vrow[FRAMES ? S::DN : 1];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -334,7 +333,6 @@ __global__ __launch_bounds__(128, 2) void k_so2_conv(const int32_t* __restrict__
     // the chunk's Wigner rows (zeros past the row end, so those edges rotate to zero)
     const int my_id = lane < ne ? eid[k0 + lane] : 0;
     load_wigner<L, C, 128>(threadIdx.x, ne, my_id, Dm, dl);
-    if constexpr (TWO) load_wigner<L, C, 128>(threadIdx.x, ne, my_id, Dr, dl2);
     __syncthreads();
     for (int e0 = 8 * wave; e0 < 8 * wave + 8; e0 += 4) {  // wave-uniform; four edges' loads issued together
       float xv[4][S::NC];
@@ -347,6 +345,9 @@ __global__ __launch_bounds__(128, 2) void k_so2_conv(const int32_t* __restrict__
       });
     }
     __syncthreads();
+    // TWO: the inverse rotation's blocks replace the gather's in LDS (no
+    // wavefront reads them again this chunk), loaded while the maps run
+    if constexpr (TWO) load_wigner<L, C, 128>(threadIdx.x, ne, my_id, Dr, dl);
     if (wave == 0)
       so2_maps<L, C, ADJ, 0>(tile, W, lane);
     else
@@ -379,7 +380,7 @@ __global__ __launch_bounds__(128, 2) void k_so2_conv(const int32_t* __restrict__
     const int e_end = min(ne, 8 * wave + 8);
     for (int e = 8 * wave; e < e_end; ++e) {  // wave-uniform
       const float* te = &tile[e * S::PAD];
-      const float* dle = TWO ? &dl2[e * S::NDP] : &dl[e * S::NDP];
+      const float* dle = &dl[e * S::NDP];  // TWO: the blocks of Dr by now
       so2_for<L + 1>([&](auto IL) {
         constexpr int l = IL, n2 = 2 * l + 1;
         float yv[n2];
