@@ -11,7 +11,9 @@ kernel's roofline point, and the fp64 CPU oracle timed on a bounded sample
 of the same workload.  Outside the timed steps it also reports cold-cache
 kernel times (1 GiB read before each step), the double backward's two
 kernels (tpconv_double_backward with seeded cotangents), the upstream
-kernels (edge harmonics, their gradient, the position gradient) and the SO(2)
+kernels (edge harmonics, their gradient, the position gradient; and the
+convolution with the harmonics inside its kernels against that three-kernel
+chain) and the SO(2)
 convolution on the same graph (its rotations, forward, grad_x,
 map-gradient, double-backward and frame-gradient passes, against the fp32
 matrix-core peak).
@@ -281,6 +283,36 @@ def main():
                      "algorithmic_GBps": round(bb / (m * 1e-3) / 1e9, 1)}
               for name, m, bb in zip(("tpconv_sh", "tpconv_sh_backward", "tpconv_positions_backward"), med, ub)}
         up["reps"] = args.upstream_reps
+        # the force chain's convolution with the harmonics inside its kernels
+        # (tpconv_forward_vec, tpconv_backward_vec) against the three-kernel
+        # chain around tpconv_forward / tpconv_backward, interleaved
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.upstream_reps + 2)]
+        for k in range(args.upstream_reps + 2):   # the first two are warm-up
+            e_ = fev[k]
+            e_[0].record(stream)
+            tp.tpconv_sh(plan, vec_t, Y_t)
+            e_[1].record(stream)
+            tp.tpconv_forward(plan, graph, x, Y_t, W, out)
+            e_[2].record(stream)
+            tp.tpconv_backward(plan, graph, x, Y_t, W, G, dx, dY, dW)
+            e_[3].record(stream)
+            tp.tpconv_sh_backward(plan, vec_t, dY, gv_t)
+            e_[4].record(stream)
+            tp.tpconv_forward_vec(plan, graph, x, vec_t, W, out)
+            e_[5].record(stream)
+            tp.tpconv_backward_vec(plan, graph, x, vec_t, W, G, dx, gv_t, dW)
+            e_[6].record(stream)
+        torch.cuda.synchronize()
+        fm = lambda i, j: float(np.median([e_[i].elapsed_time(e_[j]) for e_ in fev[2:]]))  # noqa: E731
+        chain_ms, fused_ms = fm(0, 4), fm(4, 6)
+        up["harmonics_in_kernels"] = {
+            "three_kernel_chain_ms_median": round(chain_ms, 4),
+            "fused_ms_median": round(fused_ms, 4),
+            "forward_ms_median": round(fm(1, 2), 4), "backward_ms_median": round(fm(2, 3), 4),
+            "forward_vec_ms_median": round(fm(4, 5), 4), "backward_vec_ms_median": round(fm(5, 6), 4),
+            "chain_edges_per_s": round(E / (chain_ms * 1e-3), 1), "fused_edges_per_s": round(E / (fused_ms * 1e-3), 1),
+            "chain": "tpconv_sh + tpconv_forward + tpconv_backward + tpconv_sh_backward",
+            "fused": "tpconv_forward_vec + tpconv_backward_vec"}
         del vec_t, Y_t, gv_t, gp_t
 
     dd = None

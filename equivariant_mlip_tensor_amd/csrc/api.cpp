@@ -221,6 +221,80 @@ extern "C" tpconv_status tpconv_backward(tpconv_plan_t hp, tpconv_graph_t hg, co
 }
 
 namespace {
+// Plans the kernels that evaluate the harmonics themselves cover: every plan
+// that runs as one launch per direction (not those holding both parities of
+// some l, which run as passes adding into shared outputs).
+tpconv_status vec_check(const Plan& p) {
+  if (!p.passes.empty())
+    return fail(TPCONV_E_UNSUPPORTED,
+                "harmonics from edge vectors: plans holding both parities of one l run as several passes; use "
+                "tpconv_sh, tpconv_forward, tpconv_backward and tpconv_sh_backward");
+  return TPCONV_OK;
+}
+}  // namespace
+
+extern "C" tpconv_status tpconv_forward_vec(tpconv_plan_t hp, tpconv_graph_t hg, const void* x, const void* vec,
+                                            const void* W, void* out, hipStream_t stream) {
+  if (hp == nullptr || hg == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL plan or graph");
+  const Plan& p = *reinterpret_cast<const Plan*>(hp);
+  const Graph& g = *reinterpret_cast<const Graph*>(hg);
+  KernelArgs a = base_args(p, g.n_nodes);
+  const tpconv_status st = vec_check(p);
+  if (st != TPCONV_OK) return st;
+  if (g.n_nodes > 0 && (out == nullptr || x == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL x or out");
+  if (g.n_edges > 0 && (vec == nullptr || W == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL vec or W");
+  if (g.n_nodes == 0) return TPCONV_OK;
+  Launcher f = pick(Kind::kFwd, p.kernel_l, p.dtype);
+  if (f == nullptr) return fail(TPCONV_E_UNSUPPORTED, "no kernel for this l bound");
+  a.row_ptr = g.dst_row;
+  a.col = g.dst_col;
+  a.eid = g.dst_eid;
+  a.order = g.dst_order;
+  a.x = x;
+  a.W = W;
+  a.out = out;
+  a.from_vec = 1;
+  a.vec = vec;
+  const hipError_t he = f(a, stream);
+  if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("forward launch: ") + hipGetErrorString(he));
+  return TPCONV_OK;
+}
+
+extern "C" tpconv_status tpconv_backward_vec(tpconv_plan_t hp, tpconv_graph_t hg, const void* x, const void* vec,
+                                             const void* W, const void* grad_out, void* grad_x, void* grad_vec,
+                                             void* grad_W, hipStream_t stream) {
+  if (hp == nullptr || hg == nullptr) return fail(TPCONV_E_INVALID_ARG, "NULL plan or graph");
+  const Plan& p = *reinterpret_cast<const Plan*>(hp);
+  const Graph& g = *reinterpret_cast<const Graph*>(hg);
+  KernelArgs a = base_args(p, g.n_nodes);
+  const tpconv_status st = vec_check(p);
+  if (st != TPCONV_OK) return st;
+  const bool want_edges = g.n_edges > 0 && (grad_vec != nullptr || grad_W != nullptr);
+  if (grad_x == nullptr && !want_edges) return TPCONV_OK;
+  if (g.n_nodes > 0 && (x == nullptr || grad_out == nullptr))
+    return fail(TPCONV_E_INVALID_ARG, "NULL x or grad_out");
+  if (g.n_edges > 0 && (vec == nullptr || W == nullptr)) return fail(TPCONV_E_INVALID_ARG, "NULL vec or W");
+  if (g.n_nodes == 0) return TPCONV_OK;
+  Launcher f = pick(Kind::kBwd, p.kernel_l, p.dtype);
+  if (f == nullptr) return fail(TPCONV_E_UNSUPPORTED, "no kernel for this l bound");
+  a.row_ptr = g.src_row;
+  a.col = g.src_col;
+  a.eid = g.src_eid;
+  a.order = g.src_order;
+  a.x = x;
+  a.W = W;
+  a.G = grad_out;
+  a.out = grad_x;
+  a.dW = grad_W;
+  a.from_vec = 1;
+  a.vec = vec;
+  a.gvec = g.n_edges > 0 ? grad_vec : nullptr;
+  const hipError_t he = f(a, stream);
+  if (he != hipSuccess) return fail(TPCONV_E_HIP, std::string("backward launch: ") + hipGetErrorString(he));
+  return TPCONV_OK;
+}
+
+namespace {
 using RadialLauncher = hipError_t (*)(bool, const KernelArgs&, const float*, const float*, float*, int, hipStream_t);
 
 RadialLauncher pick_radial(int L) {

@@ -1,22 +1,14 @@
-// sh.hip -- the step upstream of the convolution on gfx950: edge spherical
-// harmonics from edge vectors, their gradient, and the position gradient
-// (forces).  Small streaming kernels, kept apart from the convolution kernels
-// on purpose: those are bound by VALU issue, and evaluating the harmonics
-// inside them would cost every channel lane the same ~100-500 operations per
-// edge to save 16 values of HBM traffic per edge.
+// sh.hip -- the step upstream of the convolution on gfx950 as separate
+// streaming kernels: edge spherical harmonics from edge vectors, their
+// gradient, and the position gradient (forces).  The convolution kernels can
+// also evaluate the harmonics of their edges themselves (tpconv_forward_vec,
+// tpconv_backward_vec); both use the device functions of sh_eval.hpp, so the
+// values agree.
 //
 // Also the SO(2) convolution's edge frames: the real Wigner blocks of each
 // edge's frame rotation (k_so2_wigner) and their gradient with respect to
 // the edge vector (k_so2_wigner_backward), both from an exact sphere
-// quadrature of the harmonics below.
-//
-// Harmonics: component-normalised real SH, Y_lm(r) = sqrt(2l+1) S_lm(r / |r|),
-// with S_lm the real solid harmonics in Racah normalisation, built by their
-// standard recurrences in l (sectoral terms from (x, y) and S_ll, S_l,-l; the
-// rest from z S_lm and r^2 S_l-1,m).  This basis and sign convention equals
-// the one of the real CG tables (real basis U^l over Condon-Shortley complex
-// harmonics; Y_1 = sqrt(3) (y, z, x)).  A zero vector gets Y = (1, 0, ...)
-// and a zero gradient.
+// quadrature of the same harmonics.
 //
 // Arithmetic is fp64 for both data types (fp32 inputs are widened, results
 // rounded once on store): the gradient is the small tangential remainder of
@@ -28,167 +20,39 @@
 #include <type_traits>
 #include <utility>
 
+#include "sh_eval.hpp"
 #include "tp_common.hpp"
 
 namespace tpconv {
 namespace {
 
-template <typename F, int... I>
-__device__ __forceinline__ void sh_sf(F& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void sh_for(F&& f) {
-  if constexpr (N > 0) sh_sf(f, std::make_integer_sequence<int, N>{});
-}
-
-constexpr int lm_index(int l, int m) { return l * l + l + m; }
-
-// recurrence coefficients (compile time)
-constexpr double sect_coef(int l) {  // S_{l+1,+-(l+1)} from S_{l,+-l}
-  return cg::csqrt((l == 0 ? 2.0 : 1.0) * (2 * l + 1) / (2.0 * l + 2.0));
-}
-constexpr double zc_coef(int l, int m) {  // (2l+1) / sqrt((l+m+1)(l-m+1))
-  return (2.0 * l + 1.0) / cg::csqrt(double((l + m + 1) * (l - m + 1)));
-}
-constexpr double rc_coef(int l, int m) {  // sqrt((l+m)(l-m)) / sqrt((l+m+1)(l-m+1))
-  return cg::csqrt(double((l + m) * (l - m))) / cg::csqrt(double((l + m + 1) * (l - m + 1)));
-}
-
-// A value and its gradient in (x, y, z): forward-mode derivatives through the
-// recurrence, which treats x, y, z as free variables (r^2 = x^2 + y^2 + z^2),
-// so each S_lm is the homogeneous polynomial and its gradient is exact.
-template <typename T>
-struct Dual {
-  T v, dx, dy, dz;
-};
-template <typename T>
-__device__ __forceinline__ Dual<T> dmul(const Dual<T>& a, const Dual<T>& b) {
-  return {a.v * b.v, a.dx * b.v + a.v * b.dx, a.dy * b.v + a.v * b.dy, a.dz * b.v + a.v * b.dz};
-}
-template <typename T>
-__device__ __forceinline__ Dual<T> dlin(T ca, const Dual<T>& a, T cb, const Dual<T>& b) {  // ca*a + cb*b
-  return {ca * a.v + cb * b.v, ca * a.dx + cb * b.dx, ca * a.dy + cb * b.dy, ca * a.dz + cb * b.dz};
-}
-template <typename T>
-__device__ __forceinline__ Dual<T> dscale(T c, const Dual<T>& a) {
-  return {c * a.v, c * a.dx, c * a.dy, c * a.dz};
-}
-
-template <typename T>
-struct PlainOps {
-  static __device__ __forceinline__ T mul(T a, T b) { return a * b; }
-  static __device__ __forceinline__ T lin(double ca, T a, double cb, T b) { return T(ca) * a + T(cb) * b; }
-  static __device__ __forceinline__ T scale(double c, T a) { return T(c) * a; }
-};
-template <typename T>
-struct DualOps {
-  static __device__ __forceinline__ Dual<T> mul(const Dual<T>& a, const Dual<T>& b) { return dmul(a, b); }
-  static __device__ __forceinline__ Dual<T> lin(double ca, const Dual<T>& a, double cb, const Dual<T>& b) {
-    return dlin(T(ca), a, T(cb), b);
-  }
-  static __device__ __forceinline__ Dual<T> scale(double c, const Dual<T>& a) { return dscale(T(c), a); }
-};
-
-// S[lm] for l <= L at (x, y, z), r2 standing for x^2 + y^2 + z^2; N is T or
-// Dual<T> and Ops supplies its product and linear combinations.
-template <int L, typename N, class Ops>
-__device__ __forceinline__ void solid_harmonics(const N& x, const N& y, const N& z, const N& r2, const N& one,
-                                                N (&S)[(L + 1) * (L + 1)]) {
-  S[0] = one;
-  sh_for<L>([&](auto IL) {
-    constexpr int l = IL;
-    constexpr double c = sect_coef(l);
-    if constexpr (l == 0) {
-      S[lm_index(1, 1)] = x;
-      S[lm_index(1, -1)] = y;
-    } else {
-      S[lm_index(l + 1, l + 1)] = Ops::lin(c, Ops::mul(x, S[lm_index(l, l)]), -c, Ops::mul(y, S[lm_index(l, -l)]));
-      S[lm_index(l + 1, -(l + 1))] = Ops::lin(c, Ops::mul(y, S[lm_index(l, l)]), c, Ops::mul(x, S[lm_index(l, -l)]));
-    }
-    sh_for<2 * l + 1>([&](auto IM) {
-      constexpr int m = int(IM) - l;
-      constexpr double a = zc_coef(l, m);
-      if constexpr (m >= -(l - 1) && m <= l - 1) {
-        constexpr double b = rc_coef(l, m);
-        S[lm_index(l + 1, m)] = Ops::lin(a, Ops::mul(z, S[lm_index(l, m)]), -b, Ops::mul(r2, S[lm_index(l - 1, m)]));
-      } else {
-        S[lm_index(l + 1, m)] = Ops::scale(a, Ops::mul(z, S[lm_index(l, m)]));
-      }
-    });
-  });
-}
-
-template <typename T>
-__device__ __forceinline__ double load_unit(const T* __restrict__ v, double& ux, double& uy, double& uz) {
-  const double x = v[0], y = v[1], z = v[2];
-  const double r = sqrt(x * x + y * y + z * z);
-  const double inv = r > 0.0 ? 1.0 / r : 0.0;
-  ux = x * inv;
-  uy = y * inv;
-  uz = z * inv;
-  return r;
-}
+using namespace shx;
 
 template <typename T, int L>
 __global__ __launch_bounds__(256) void k_sh(int64_t n, const T* __restrict__ vec, T* __restrict__ Y) {
   constexpr int D = (L + 1) * (L + 1);
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= n) return;
-  double x, y, z;
-  const double r = load_unit(vec + 3 * e, x, y, z);
-  double S[D];
-  solid_harmonics<L, double, PlainOps<double>>(x, y, z, 1.0, 1.0, S);
+  const T* v = vec + 3 * e;
   T* yr = Y + e * D;
-  const bool dir = r > 0.0;  // a zero vector keeps only Y_00 = 1
-  sh_for<L + 1>([&](auto IL) {
-    constexpr int l = IL;
-    constexpr double nl = cg::csqrt(2.0 * l + 1.0);
-    sh_for<2 * l + 1>([&](auto IM) {
-      constexpr int k = l * l + int(IM);
-      yr[k] = (dir || k == 0) ? T(nl * S[k]) : T(0);
-    });
-  });
+  sh_values<L>(double(v[0]), double(v[1]), double(v[2]), [&](int k, double val) { yr[k] = T(val); });
 }
 
-// grad_vec[e] = sum_lm grad_Y[e, lm] sqrt(2l+1) (grad S_lm(u) - l S_lm(u) u) / |r|,  u = r / |r|
+// grad_vec[e] = sum_lm grad_Y[e, lm] dY_lm/dvec (sh_vec_grad)
 template <typename T, int L>
 __global__ __launch_bounds__(256) void k_sh_backward(int64_t n, const T* __restrict__ vec, const T* __restrict__ gY,
                                                      T* __restrict__ gvec) {
   constexpr int D = (L + 1) * (L + 1);
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= n) return;
-  double x, y, z;
-  const double r = load_unit(vec + 3 * e, x, y, z);
-  T* out = gvec + 3 * e;
-  if (!(r > 0.0)) {
-    out[0] = out[1] = out[2] = T(0);
-    return;
-  }
-  using D64 = Dual<double>;
-  const D64 X{x, 1.0, 0.0, 0.0}, Yv{y, 0.0, 1.0, 0.0}, Z{z, 0.0, 0.0, 1.0};
-  const D64 R2{1.0, 2.0 * x, 2.0 * y, 2.0 * z};
-  const D64 ONE{1.0, 0.0, 0.0, 0.0};
-  D64 S[D];
-  solid_harmonics<L, D64, DualOps<double>>(X, Yv, Z, R2, ONE, S);
+  const T* v = vec + 3 * e;
   const T* g = gY + e * D;
-  double ax = 0.0, ay = 0.0, az = 0.0;
-  sh_for<L + 1>([&](auto IL) {
-    constexpr int l = IL;
-    constexpr double nl = cg::csqrt(2.0 * l + 1.0);
-    sh_for<2 * l + 1>([&](auto IM) {
-      constexpr int k = l * l + int(IM);
-      const double w = nl * double(g[k]);
-      const double ls = double(l) * S[k].v;
-      ax += w * (S[k].dx - ls * x);
-      ay += w * (S[k].dy - ls * y);
-      az += w * (S[k].dz - ls * z);
-    });
-  });
-  const double inv = 1.0 / r;
-  out[0] = T(ax * inv);
-  out[1] = T(ay * inv);
-  out[2] = T(az * inv);
+  double gx, gy, gz;
+  sh_vec_grad<L>(double(v[0]), double(v[1]), double(v[2]), [&](int k) { return double(g[k]); }, gx, gy, gz);
+  T* out = gvec + 3 * e;
+  out[0] = T(gx);
+  out[1] = T(gy);
+  out[2] = T(gz);
 }
 
 // grad_pos[j] = sum over edges leaving j of grad_vec - sum over edges entering j:

@@ -48,7 +48,7 @@ struct KernelArgs {
   int32_t lps_log2;     // log2 of lanes per edge slot: next power of two >= U
   int32_t nslots;       // edges a wave processes side by side: 64 >> lps_log2
   int32_t d_in, d_out, d_sh;
-  int32_t pad0;
+  int32_t from_vec;     // 1: the kernels evaluate Y from the edge vectors `vec` themselves (full plans)
   int64_t wstride;      // weight_numel
   uint64_t pmask_lo;    // bit t: triple t is a path of the plan (t < 64)
   uint64_t pmask_hi;    // bit t-64
@@ -79,6 +79,8 @@ struct KernelArgs {
   void* out;            // forward: out; backward: grad_x; double backward: grad_G or grad_x (may be null)
   void* dY;             // backward kernels: grad_Y (may be null)
   void* dW;             // backward kernels: grad_W (may be null)
+  const void* vec;      // from_vec: the edge vectors [E][3] (Y unused)
+  void* gvec;           // backward with vec: grad_vec [E][3] in place of grad_Y (may be null)
 };
 
 // Launchers, one per (lmax, dtype), defined by tp_kernels.hip compiled once

@@ -37,11 +37,19 @@
 //  * fp64 contractions sum the products that share an (m3, |c|) pair before
 //    one multiply by the coefficient (Grouped), because an fp64 coefficient
 //    is no inline literal.
+//
+// With KernelArgs::from_vec set (template parameter SHV; one launch per plan) the forward and
+// backward evaluate each edge's harmonics themselves from the edge vector
+// (sh_eval.hpp, fp64, one lane per edge for a chunk of the row's edges at a
+// time, kept in a per-wave LDS block the slots read), and the backward turns
+// each chunk's channel-summed dY, kept in LDS, into grad_vec [E][3] the same
+// way: Y and dY never reach device memory.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
 #include <utility>
 
+#include "sh_eval.hpp"
 #include "tp_common.hpp"
 
 #ifndef TPCONV_L
@@ -78,6 +86,15 @@ __device__ __forceinline__ void pin_vgpr(T& v) {
 template <typename T>
 __device__ __forceinline__ T ldg_stream(const T* p) {
   return __builtin_nontemporal_load(p);
+}
+
+// Orders one wavefront's LDS accesses around a hand-over between its lanes
+// (one lane writes, another reads): a code-motion barrier for the compiler;
+// the hardware runs a wavefront's LDS instructions in order.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // Row accumulators: a row sums one term per edge, so for fp32 data it is
@@ -645,9 +662,12 @@ __device__ __forceinline__ void row_part(int beg, int end, int nsl, int part, in
 
 // Forward (DD = false): out = the convolution.  Double backward's first pass
 // (DD = true): out = grad_G, from the cotangents a (gathered like x), b (like
-// Y) and c (like W); a null cotangent reads as zeros.
-template <typename T, int L, class P, bool DD, int R>
+// Y) and c (like W); a null cotangent reads as zeros.  SHV: Y of each edge from
+// its vector a.vec, evaluated per chunk of kChunk row edges (one lane each)
+// into the wave's LDS block s_y.
+template <typename T, int L, class P, bool DD, int R, bool SHV = false>
 __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
+  static_assert(!(SHV && DD), "harmonics from edge vectors: forward only");
   using F = Fwd<T, L, P>;
   using FD = FwdDD<T, L, P>;
   using A = typename RowAcc<T>::type;
@@ -709,12 +729,27 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
   const int nsl = P::nslots(a);
   int beg, end;
   row_part<R>(has_row ? a.row_ptr[node] : 0, has_row ? a.row_ptr[node + 1] : 0, nsl, part, beg, end);
-  // the row's edge ids and neighbours are loaded 64 at a time, one per lane,
-  // and handed to the slots with lane shuffles while the wave is converged
-  for (int cb = beg; cb < end; cb += 64) {
-    const int cn = min(64, end - cb);
+  // 32 edges per chunk with SHV keeps four blocks per CU within the LDS
+  constexpr int kChunk = SHV ? 32 : 64;
+  __shared__ T s_y[SHV ? 4 : 1][SHV ? kChunk : 1][SHV ? NL : 1];
+  const T* __restrict__ VEC = static_cast<const T*>(a.vec);
+  // the row's edge ids and neighbours are loaded a chunk at a time, one per
+  // lane, and handed to the slots with lane shuffles while the wave is
+  // converged
+  for (int cb = beg; cb < end; cb += kChunk) {
+    const int cn = min(kChunk, end - cb);
     const int my_e = lane < cn ? a.eid[cb + lane] : 0;
     const int my_j = lane < cn ? a.col[cb + lane] : 0;
+    if constexpr (SHV) {
+      wave_lds_sync();  // the previous chunk's reads of s_y come first
+      if (lane < cn) {
+        const T* v = VEC + 3 * (int64_t)my_e;
+        T* yl = &s_y[wave][lane][0];
+        shx::sh_values<L>(double(v[0]), double(v[1]), double(v[2]),
+                          [&](int k, double val) { yl[k] = k < d_sh ? T(val) : T(0); });
+      }
+      wave_lds_sync();
+    }
     const int iters = (cn + nsl - 1) / nsl;
     for (int it = 0; it < iters; ++it) {
     const int q = it * nsl + slot;
@@ -741,7 +776,11 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
       });
     };
     load_x(X, x);
-    load_y(Yp, y);
+    if constexpr (SHV) {
+      static_for<NL>([&](auto I) { y[I] = s_y[wave][q][I]; });
+    } else {
+      load_y(Yp, y);
+    }
     load_w<T, L, P>(a, Wp, wstride, uc, e, w);
     T te[NL];
     if constexpr (DD) {
@@ -1109,9 +1148,13 @@ constexpr bool bwd_pipelined() {
 // Backward (DD = false): grad_x (out), grad_Y (dY), grad_W (dW) of <G, out>.
 // Double backward's second pass (DD = true): the same three outputs of
 // <a, dx> + <b, dY> + <c, dW>, with the cotangents a (row-resident like x),
-// b and c; a null cotangent reads as zeros.
-template <typename T, int L, class P, bool DD, int R>
+// b and c; a null cotangent reads as zeros.  SHV: Y from the edge vectors
+// a.vec per chunk of 64 row edges (as in the forward), each edge's
+// channel-summed dY into the wave's LDS block, and at the chunk's end
+// grad_vec (a.gvec) of its edges, one lane each.
+template <typename T, int L, class P, bool DD, int R, bool SHV = false>
 __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
+  static_assert(!(SHV && DD), "harmonics from edge vectors: backward only");
   using B = Bwd<T, L, P>;
   using BD = BwdDD<T, L, P>;
   using In = EdgeIn<T, L, DD>;
@@ -1147,6 +1190,16 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
   const T* __restrict__ WC = static_cast<const T*>(a.Wc);
   const int d_out = P::d_out(a), d_sh = P::d_sh(a);
   const int64_t wstride = P::wstride(a);
+  const T* __restrict__ VEC = static_cast<const T*>(a.vec);
+  T* __restrict__ GV = static_cast<T*>(a.gvec);
+  // SHV: per wave, the current chunk's harmonics and channel-summed dY (row
+  // position within the chunk major), and the vectors and edge ids of the
+  // chunk by its parity (a chunk's ids are fetched one step before the
+  // previous chunk's last step has run)
+  __shared__ T s_vy[SHV ? 4 : 1][SHV ? 64 : 1][SHV ? NL : 1];
+  __shared__ T s_vdy[SHV ? 4 : 1][SHV ? 64 : 1][SHV ? NL : 1];
+  __shared__ T s_vv[SHV ? 4 : 1][SHV ? 2 : 1][SHV ? 64 : 1][SHV ? 3 : 1];
+  __shared__ int s_ve[SHV ? 4 : 1][SHV ? 2 : 1][SHV ? 64 : 1];
 
   // this source node's features (and for the double backward its cotangent
   // a) stay in registers for the whole row; idle lanes hold zeros so they
@@ -1229,6 +1282,26 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
     // would also wait for every store still in flight
     pin_vgpr(my_e);
     pin_vgpr(my_i);
+    if constexpr (SHV) {
+      // this chunk's harmonics, one lane per edge; lanes past the row's end
+      // take a zero vector (Y = (1, 0, ...)), so every entry is defined
+      const int par = (k >> lg) & 1;
+      double vx = 0.0, vy = 0.0, vz = 0.0;
+      if (p < deg) {
+        const T* v = VEC + 3 * (int64_t)my_e;
+        vx = double(v[0]);
+        vy = double(v[1]);
+        vz = double(v[2]);
+      }
+      wave_lds_sync();  // the previous chunk's reads of s_vy come first
+      T* yl = &s_vy[wave][lane][0];
+      shx::sh_values<L>(vx, vy, vz, [&](int kk, double val) { yl[kk] = kk < d_sh ? T(val) : T(0); });
+      s_vv[wave][par][lane][0] = T(vx);
+      s_vv[wave][par][lane][1] = T(vy);
+      s_vv[wave][par][lane][2] = T(vz);
+      s_ve[wave][par][lane] = my_e;
+      wave_lds_sync();
+    }
   };
   auto load_y = [&](const T* __restrict__ base, bool present, int e, T (&y)[NL]) {
     const T* yr = base + (int64_t)e * d_sh;
@@ -1249,7 +1322,7 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
       }
     });
   };
-  auto load_edge = [&](int e, int i, In& in) {
+  auto load_edge = [&](int e, int i, int q, In& in) {
     const T* gr = Gp + (int64_t)i * d_out;
     static_for<L + 1>([&](auto I) {
       constexpr int l = I;
@@ -1259,7 +1332,11 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
         else in.g[l * l + M] = T(0);
       });
     });
-    load_y(Yp, true, e, in.y);
+    if constexpr (SHV) {
+      static_for<NL>([&](auto I) { in.y[I] = s_vy[wave][q][I]; });
+    } else {
+      load_y(Yp, true, e, in.y);
+    }
     load_wrow(Wp, true, e, in.w);
     if constexpr (DD) {
       load_y(YB, YB != nullptr, e, in.yb);
@@ -1272,21 +1349,21 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
   // Loads and arithmetic run unconditionally: a slot past the end of the row
   // reads edge 0 / node 0 (its ids are 0) and only its stores and its share
   // of dx are masked, which keeps every load out of divergent control flow.
-  auto prefetch = [&](int k, int& e, bool& valid, In& in) {
+  auto prefetch = [&](int k, int& e, bool& valid, int& q, In& in) {
     const int r = k & chunk_mask;
     if (r == 0) fetch_ids(k);
-    const int q = (r << lgs) + slot;
+    q = (r << lgs) + slot;  // position within the chunk
     e = __shfl(my_e, q, 64);
     const int i = __shfl(my_i, q, 64);
     valid = (k << lgs) + slot < deg;
-    load_edge(e, i, in);
+    load_edge(e, i, q, in);
   };
   struct Pending {
     T dw[NT];  // unused, and removed, unless kLate
     T dy[kLate ? NV : 1];
     int base, nv;
   };
-  auto compute = [&](const int e, const bool valid, const In& in, Pending& pd) {
+  auto compute = [&](const int e, const bool valid, const int q, const In& in, Pending& pd) {
     T dya[NV], dxe[NL];
     static_for<NV>([&](auto I) { dya[I] = T(0); });
     // idle lanes (u >= U) aim their dW stores at channel 0 of the same row
@@ -1314,7 +1391,7 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
       }
     });
 
-    if (DY != nullptr) {
+    if (SHV ? GV != nullptr : DY != nullptr) {
       // reduce-scatter of the NV dY values over the slot's lanes.  Step s
       // pairs lanes across bit b = lps >> (s+1); while more than one value is
       // left, lanes with bit b set keep the upper half, the others the lower.
@@ -1349,6 +1426,13 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
         static_for<NV>([&](auto V) { pd.dy[V] = dya[V]; });
         pd.base = base;
         pd.nv = nv;
+      } else if constexpr (SHV) {
+        const int plain_mask = lps > NV ? lps / NV - 1 : 0;
+        if ((u & plain_mask) == 0 && valid) {
+          static_for<NV>([&](auto J) {
+            if (J < nv && base + J < d_sh) s_vdy[wave][q][base + J] = dya[J];
+          });
+        }
       } else {
         // bits below lps/NV were plain sums: one lane of each such group stores
         const int plain_mask = lps > NV ? lps / NV - 1 : 0;
@@ -1387,35 +1471,63 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
     }
   };
 
+  // SHV: after a chunk's last step, grad_vec of the chunk's edges (one lane
+  // each) from their vectors and channel-summed dY in LDS
+  auto vec_pass = [&](int k) {
+    if constexpr (SHV) {
+      if (GV == nullptr) return;
+      if (((k + 1) & chunk_mask) != 0 && k + 1 < n_steps) return;  // wave-uniform
+      wave_lds_sync();  // the chunk's dY writes come first
+      const int par = (k >> lg) & 1;
+      const int pos = ((k >> lg) << 6) + lane;  // this lane's row position in the chunk
+      if (pos < deg) {
+        const int e = s_ve[wave][par][lane];
+        const T* vv = &s_vv[wave][par][lane][0];
+        const T* gy = &s_vdy[wave][lane][0];
+        double gx, gyv, gz;
+        shx::sh_vec_grad<L>(double(vv[0]), double(vv[1]), double(vv[2]),
+                            [&](int kk) { return kk < d_sh ? double(gy[kk]) : 0.0; }, gx, gyv, gz);
+        T* o = GV + 3 * (int64_t)e;
+        o[0] = T(gx);
+        o[1] = T(gyv);
+        o[2] = T(gz);
+      }
+      wave_lds_sync();  // and the next chunk's dY writes after these reads
+    }
+  };
+
   In ia;
-  int ea = 0;
+  int ea = 0, qa = 0;
   bool va = false;
   Pending pd;
   if constexpr (bwd_pipelined<T, L, P, DD>()) {
     In ib;
-    int eb = 0;
+    int eb = 0, qb = 0;
     bool vb = false;
-    if (n_steps > 0) prefetch(0, ea, va, ia);
+    if (n_steps > 0) prefetch(0, ea, va, qa, ia);
     for (int k = 0; k < n_steps; k += 2) {  // wave-uniform trip count
-      prefetch(k + 1, eb, vb, ib);
-      compute(ea, va, ia, pd);
+      prefetch(k + 1, eb, vb, qb, ib);
+      compute(ea, va, qa, ia, pd);
+      vec_pass(k);
       if (k + 1 >= n_steps) break;
-      prefetch(k + 2, ea, va, ia);
-      compute(eb, vb, ib, pd);
+      prefetch(k + 2, ea, va, qa, ia);
+      compute(eb, vb, qb, ib, pd);
+      vec_pass(k + 1);
     }
   } else if constexpr (kLate) {
-    if (n_steps > 0) prefetch(0, ea, va, ia);
+    if (n_steps > 0) prefetch(0, ea, va, qa, ia);
     for (int k = 0; k < n_steps; ++k) {  // wave-uniform trip count
-      compute(ea, va, ia, pd);
+      compute(ea, va, qa, ia, pd);
       const int e_done = ea;
       const bool v_done = va;
-      if (k + 1 < n_steps) prefetch(k + 1, ea, va, ia);
+      if (k + 1 < n_steps) prefetch(k + 1, ea, va, qa, ia);
       store_pending(e_done, v_done, pd);
     }
   } else {
     for (int k = 0; k < n_steps; ++k) {
-      prefetch(k, ea, va, ia);
-      compute(ea, va, ia, pd);
+      prefetch(k, ea, va, qa, ia);
+      compute(ea, va, qa, ia, pd);
+      vec_pass(k);
     }
   }
 
@@ -1852,21 +1964,21 @@ constexpr bool kDD = TPCONV_DD != 0;
 // its memory latency behind.
 constexpr int kSplitRows = 1024;
 
-template <typename T, class P, int R = 1>
+template <typename T, class P, int R = 1, bool SHV = false>
 hipError_t launch_fwd(const KernelArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
   const int rows_per_block = 4 / R;
   const int blocks = (a.n_rows + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL((fwd_kernel<T, TPCONV_L, P, kDD, R>), dim3(blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((fwd_kernel<T, TPCONV_L, P, kDD, R, SHV>), dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <typename T, class P, int R = 1>
+template <typename T, class P, int R = 1, bool SHV = false>
 hipError_t launch_bwd(const KernelArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
   const int rows_per_block = 4 / R;
   const int blocks = (a.n_rows + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL((bwd_kernel<T, TPCONV_L, P, kDD, R>), dim3(blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((bwd_kernel<T, TPCONV_L, P, kDD, R, SHV>), dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1890,14 +2002,33 @@ template <int... Us>
 struct UList {};
 using FullMuls = UList<16, 32, 64>;
 
+template <typename T, bool FWD, bool SHV, class FP>
+hipError_t launch_full_rows(const KernelArgs& a, hipStream_t s) {
+  // the fp64 l = 4 backward with harmonics from vectors holds ~117 KB of LDS
+  // per block: no room for the split rows' LDS as well
+  constexpr bool kWhole = SHV && !FWD && sizeof(T) == 8 && TPCONV_L >= 4;
+  if constexpr (FWD) {
+    if (a.n_rows <= kSplitRows) return launch_fwd<T, FP, 4, SHV>(a, s);
+    return launch_fwd<T, FP, 1, SHV>(a, s);
+  } else {
+    if constexpr (!kWhole) {
+      if (a.n_rows <= kSplitRows) return launch_bwd<T, FP, 4, SHV>(a, s);
+    }
+    return launch_bwd<T, FP, 1, SHV>(a, s);
+  }
+}
+
 template <typename T, bool FWD, int U0, int... Us>
 bool launch_full(const KernelArgs& a, hipStream_t s, hipError_t& err, UList<U0, Us...>) {
   if (a.mul == U0) {
     using FP = FullPlan<TPCONV_L, U0>;
-    if (a.n_rows <= kSplitRows)
-      err = FWD ? launch_fwd<T, FP, 4>(a, s) : launch_bwd<T, FP, 4>(a, s);
-    else
-      err = FWD ? launch_fwd<T, FP>(a, s) : launch_bwd<T, FP>(a, s);
+    if constexpr (!kDD) {
+      if (a.from_vec) {
+        err = launch_full_rows<T, FWD, true, FP>(a, s);
+        return true;
+      }
+    }
+    err = launch_full_rows<T, FWD, false, FP>(a, s);
     return true;
   }
   if constexpr (sizeof...(Us) > 0) {
@@ -1907,13 +2038,22 @@ bool launch_full(const KernelArgs& a, hipStream_t s, hipError_t& err, UList<U0, 
   }
 }
 
+template <typename T, bool FWD, bool SHV>
+hipError_t dispatch_rt(const KernelArgs& a, hipStream_t s) {
+  using PE = RtPlan<TPCONV_L, kEvenOnly>;
+  using PA = RtPlan<TPCONV_L, kAnyParity>;
+  if (all_even(a)) return FWD ? launch_fwd<T, PE, 1, SHV>(a, s) : launch_bwd<T, PE, 1, SHV>(a, s);
+  return FWD ? launch_fwd<T, PA, 1, SHV>(a, s) : launch_bwd<T, PA, 1, SHV>(a, s);
+}
+
 template <typename T, bool FWD>
 hipError_t dispatch(const KernelArgs& a, hipStream_t s) {
   hipError_t err = hipSuccess;
   if (a.full_plan && launch_full<T, FWD>(a, s, err, FullMuls{})) return err;
-  if (all_even(a))
-    return FWD ? launch_fwd<T, RtPlan<TPCONV_L, kEvenOnly>>(a, s) : launch_bwd<T, RtPlan<TPCONV_L, kEvenOnly>>(a, s);
-  return FWD ? launch_fwd<T, RtPlan<TPCONV_L, kAnyParity>>(a, s) : launch_bwd<T, RtPlan<TPCONV_L, kAnyParity>>(a, s);
+  if constexpr (!kDD) {
+    if (a.from_vec) return dispatch_rt<T, FWD, true>(a, s);
+  }
+  return dispatch_rt<T, FWD, false>(a, s);
 }
 
 }  // namespace

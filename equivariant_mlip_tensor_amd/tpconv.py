@@ -30,7 +30,7 @@ STATUS = {0: "TPCONV_OK", 1: "TPCONV_E_INVALID_ARG", 2: "TPCONV_E_IRREPS", 3: "T
 EXPORTS = ("tpconv_plan", "tpconv_plan_query", "tpconv_plan_paths", "tpconv_plan_table", "tpconv_plan_destroy",
            "tpconv_graph_workspace_bytes", "tpconv_graph_create", "tpconv_graph_export", "tpconv_graph_destroy",
            "tpconv_forward", "tpconv_backward", "tpconv_double_backward", "tpconv_radial_forward",
-           "tpconv_radial_backward", "tpconv_sh", "tpconv_sh_backward",
+           "tpconv_radial_backward", "tpconv_sh", "tpconv_sh_backward", "tpconv_forward_vec", "tpconv_backward_vec",
            "tpconv_positions_backward", "tpconv_so2_weight_numel", "tpconv_so2_rotations", "tpconv_so2_forward",
            "tpconv_so2_workspace_bytes", "tpconv_so2_backward", "tpconv_so2_backward_noalloc",
            "tpconv_so2_double_backward",
@@ -74,6 +74,8 @@ def _load():
         "tpconv_forward": (i32, [vp, vp, vp, vp, vp, vp, vp]),
         "tpconv_backward": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "tpconv_double_backward": (i32, [vp] * 14),
+        "tpconv_forward_vec": (i32, [vp, vp, vp, vp, vp, vp, vp]),
+        "tpconv_backward_vec": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "tpconv_sh": (i32, [vp, i64, vp, vp, vp]),
         "tpconv_sh_backward": (i32, [vp, i64, vp, vp, vp, vp]),
         "tpconv_positions_backward": (i32, [vp, vp, vp, vp, vp]),
@@ -392,6 +394,47 @@ def tpconv_sh_backward(plan: Plan, vec, grad_Y, grad_vec=None, stream=None) -> t
     _need(grad_vec, (E, 3), plan.torch_dtype, "grad_vec")
     _check(_lib.tpconv_sh_backward(plan.handle, E, _ptr(vec), _ptr(grad_Y), _ptr(grad_vec), _stream_handle(stream)))
     return grad_vec
+
+
+@_on_launch_stream
+def tpconv_forward_vec(plan: Plan, graph: Graph, x, vec, W, out=None, stream=None) -> torch.Tensor:
+    """out = tpconv_forward(x, tpconv_sh(vec), W), the harmonics evaluated inside the kernel."""
+    N, E, dt = graph.n_nodes, graph.n_edges, plan.torch_dtype
+    _need(x, (N, plan.dim_in), dt, "x")
+    _need(vec, (E, 3), dt, "vec")
+    _need(W, (E, plan.weight_numel), dt, "W")
+    if out is None:
+        out = torch.empty((N, plan.dim_out), dtype=dt, device=x.device)
+    _need(out, (N, plan.dim_out), dt, "out")
+    _check(_lib.tpconv_forward_vec(plan.handle, graph.handle, _ptr(x), _ptr(vec), _ptr(W), _ptr(out),
+                                   _stream_handle(stream)))
+    return out
+
+
+@_on_launch_stream
+def tpconv_backward_vec(plan: Plan, graph: Graph, x, vec, W, grad_out, grad_x=None, grad_vec=None, grad_W=None,
+                        need=(True, True, True), stream=None) -> Tuple[Optional[torch.Tensor], ...]:
+    """Returns (grad_x, grad_vec, grad_W) with the harmonics of vec evaluated inside the kernel;
+    an output is None when `need` turns it off."""
+    N, E, dt = graph.n_nodes, graph.n_edges, plan.torch_dtype
+    _need(x, (N, plan.dim_in), dt, "x")
+    _need(vec, (E, 3), dt, "vec")
+    _need(W, (E, plan.weight_numel), dt, "W")
+    _need(grad_out, (N, plan.dim_out), dt, "grad_out")
+    dev = x.device
+    if need[0] and grad_x is None:
+        grad_x = torch.empty((N, plan.dim_in), dtype=dt, device=dev)
+    if need[1] and grad_vec is None:
+        grad_vec = torch.empty((E, 3), dtype=dt, device=dev)
+    if need[2] and grad_W is None:
+        grad_W = torch.empty((E, plan.weight_numel), dtype=dt, device=dev)
+    for t, shp, nm in ((grad_x, (N, plan.dim_in), "grad_x"), (grad_vec, (E, 3), "grad_vec"),
+                       (grad_W, (E, plan.weight_numel), "grad_W")):
+        if t is not None:
+            _need(t, shp, dt, nm)
+    _check(_lib.tpconv_backward_vec(plan.handle, graph.handle, _ptr(x), _ptr(vec), _ptr(W), _ptr(grad_out),
+                                    _ptr(grad_x), _ptr(grad_vec), _ptr(grad_W), _stream_handle(stream)))
+    return grad_x, grad_vec, grad_W
 
 
 @_on_launch_stream

@@ -256,8 +256,8 @@ tpconv_status tpconv_radial_backward(tpconv_plan_t plan, tpconv_graph_t g, int h
  * vectors and the atom positions (forces are -dE/dpos).  The LunaTP and
  * TrimSO(2) abstracts place the operator in force-field training; the pages
  * give no formula for this step, which follows from the harmonics'
- * definition.  Separate streaming kernels (not fused into the convolution,
- * whose kernels are bound by arithmetic issue).
+ * definition.  Separate streaming kernels here; tpconv_forward_vec and
+ * tpconv_backward_vec below fuse the same step into the convolution.
  *
  * tpconv_sh: Y[E][(L+1)^2] (L = the plan's sh_lmax, plan dtype) =
  * component-normalised real harmonics of vec[e] / |vec[e]|, (l, m) at column
@@ -281,6 +281,33 @@ tpconv_status tpconv_sh_backward(tpconv_plan_t plan, int64_t n_edges, const void
  * grad_vec: [E][3]; grad_pos is overwritten.  Errors as tpconv_sh. */
 tpconv_status tpconv_positions_backward(tpconv_plan_t plan, tpconv_graph_t g, const void* grad_vec, void* grad_pos,
                                         hipStream_t stream);
+
+/* The same step inside the convolution kernels ("SH on the fly"): the forward
+ * and backward below take the edge vectors instead of Y and evaluate each
+ * edge's harmonics themselves (fp64 arithmetic, the values of tpconv_sh), a
+ * chunk of a row's edges at a time into on-chip memory; the backward turns
+ * each edge's channel-summed dY into grad_vec there.  Y and dY never reach
+ * device memory (the LunaTP abstract: reuse across levels of the memory
+ * hierarchy; the FlashTP page, "Problem": per-edge intermediates).
+ *
+ * Supported: every plan of tpconv_forward except those holding both parities
+ * of one l (they run as several passes): TPCONV_E_UNSUPPORTED for those (use
+ * tpconv_sh, tpconv_forward, tpconv_backward, tpconv_sh_backward).  vec:
+ * device [E][3] in the plan's dtype, may be NULL when the graph has no edges.
+ *
+ * tpconv_forward_vec: out = tpconv_forward(x, tpconv_sh(vec), W), overwritten.
+ * Errors as tpconv_forward, plus TPCONV_E_UNSUPPORTED as above. */
+tpconv_status tpconv_forward_vec(tpconv_plan_t plan, tpconv_graph_t g, const void* x, const void* vec,
+                                 const void* W, void* out, hipStream_t stream);
+
+/* tpconv_backward_vec: gradients of <G, out> for G = grad_out with
+ * Y = tpconv_sh(vec): grad_x [N][D_in], grad_W [E][weight_numel] as
+ * tpconv_backward, and grad_vec [E][3] = tpconv_sh_backward(vec, grad_Y)
+ * in place of grad_Y; tpconv_positions_backward turns grad_vec into forces.
+ * Each output is overwritten; NULL skips one.  Errors as tpconv_forward_vec. */
+tpconv_status tpconv_backward_vec(tpconv_plan_t plan, tpconv_graph_t g, const void* x, const void* vec,
+                                  const void* W, const void* grad_out, void* grad_x, void* grad_vec,
+                                  void* grad_W, hipStream_t stream);
 
 /* ------------------------------------------------ SO(2) convolution ------
  * The convolution of SO(2)-based potentials (TrimSO(2), Abstract: rotation
