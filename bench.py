@@ -103,7 +103,7 @@ def kernel_source_hash():
     """Hash of the kernel sources' code (comments removed: the counters depend
     on what is compiled, not on how it is annotated)."""
     h = hashlib.sha256()
-    for f in ("tp_kernels.hip", "cg_real.hpp", "tp_common.hpp"):
+    for f in ("tp_kernels.hip", "cg_real.hpp", "tp_common.hpp", "sh_eval.hpp"):
         with open(os.path.join(ROOT, "equivariant_mlip_tensor_amd", "csrc", f)) as fh:
             h.update(strip_comments(fh.read()).encode())
     return h.hexdigest()[:16]

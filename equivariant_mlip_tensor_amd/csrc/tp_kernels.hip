@@ -38,7 +38,7 @@
 //    one multiply by the coefficient (Grouped), because an fp64 coefficient
 //    is no inline literal.
 //
-// With KernelArgs::from_vec set (template parameter SHV; one launch per plan) the forward and
+// With KernelArgs::from_vec set (template parameter YS = kYVec; one launch per plan) the forward and
 // backward evaluate each edge's harmonics themselves from the edge vector
 // (sh_eval.hpp, fp64, one lane per edge for a chunk of the row's edges at a
 // time, kept in a per-wave LDS block the slots read), and the backward turns
@@ -96,6 +96,15 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
+
+// Where a kernel takes each edge's harmonics from (template parameter YS):
+// every lane of the edge's slot loads the row from Y (kYGlobal); one lane per
+// edge evaluates them from the edge vector into the wave's LDS block for a
+// chunk of the row's edges (kYVec); or, in the forward, one lane per edge
+// copies the Y row into that block (kYRows: c4k forward 0.150 -> 0.147 ms;
+// the same staging of Y and dY rows made the backward slower, 0.316 ->
+// 0.330 ms, so the backward loads per slot).
+constexpr int kYGlobal = 0, kYVec = 1, kYRows = 2;
 
 // Row accumulators: a row sums one term per edge, so for fp32 data it is
 // kept in fp64 (full rate on CDNA); each edge's own sum over its paths stays
@@ -662,12 +671,14 @@ __device__ __forceinline__ void row_part(int beg, int end, int nsl, int part, in
 
 // Forward (DD = false): out = the convolution.  Double backward's first pass
 // (DD = true): out = grad_G, from the cotangents a (gathered like x), b (like
-// Y) and c (like W); a null cotangent reads as zeros.  SHV: Y of each edge from
+// Y) and c (like W); a null cotangent reads as zeros.  kYVec: Y of each edge from
 // its vector a.vec, evaluated per chunk of kChunk row edges (one lane each)
 // into the wave's LDS block s_y.
-template <typename T, int L, class P, bool DD, int R, bool SHV = false>
+template <typename T, int L, class P, bool DD, int R, int YS = kYGlobal>
 __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
-  static_assert(!(SHV && DD), "harmonics from edge vectors: forward only");
+  constexpr bool SHV = YS == kYVec;
+  constexpr bool kStage = YS != kYGlobal;  // the chunk's Y rows staged in LDS
+  static_assert(!(kStage && DD), "staged harmonics: forward only");
   using F = Fwd<T, L, P>;
   using FD = FwdDD<T, L, P>;
   using A = typename RowAcc<T>::type;
@@ -729,9 +740,9 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
   const int nsl = P::nslots(a);
   int beg, end;
   row_part<R>(has_row ? a.row_ptr[node] : 0, has_row ? a.row_ptr[node + 1] : 0, nsl, part, beg, end);
-  // 32 edges per chunk with SHV keeps four blocks per CU within the LDS
-  constexpr int kChunk = SHV ? 32 : 64;
-  __shared__ T s_y[SHV ? 4 : 1][SHV ? kChunk : 1][SHV ? NL : 1];
+  // 32 edges per chunk when staging keeps four blocks per CU within the LDS
+  constexpr int kChunk = kStage ? 32 : 64;
+  __shared__ T s_y[kStage ? 4 : 1][kStage ? kChunk : 1][kStage ? NL : 1];
   const T* __restrict__ VEC = static_cast<const T*>(a.vec);
   // the row's edge ids and neighbours are loaded a chunk at a time, one per
   // lane, and handed to the slots with lane shuffles while the wave is
@@ -740,13 +751,18 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
     const int cn = min(kChunk, end - cb);
     const int my_e = lane < cn ? a.eid[cb + lane] : 0;
     const int my_j = lane < cn ? a.col[cb + lane] : 0;
-    if constexpr (SHV) {
+    if constexpr (kStage) {
       wave_lds_sync();  // the previous chunk's reads of s_y come first
       if (lane < cn) {
-        const T* v = VEC + 3 * (int64_t)my_e;
         T* yl = &s_y[wave][lane][0];
-        shx::sh_values<L>(double(v[0]), double(v[1]), double(v[2]),
-                          [&](int k, double val) { yl[k] = k < d_sh ? T(val) : T(0); });
+        if constexpr (SHV) {
+          const T* v = VEC + 3 * (int64_t)my_e;
+          shx::sh_values<L>(double(v[0]), double(v[1]), double(v[2]),
+                            [&](int k, double val) { yl[k] = k < d_sh ? T(val) : T(0); });
+        } else {
+          const T* yr = Yp + (int64_t)my_e * d_sh;
+          static_for<NL>([&](auto I) { yl[I] = I < d_sh ? ldg_stream(yr + I) : T(0); });
+        }
       }
       wave_lds_sync();
     }
@@ -776,7 +792,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KernelArgs a) {
       });
     };
     load_x(X, x);
-    if constexpr (SHV) {
+    if constexpr (kStage) {
       static_for<NL>([&](auto I) { y[I] = s_y[wave][q][I]; });
     } else {
       load_y(Yp, y);
@@ -1148,12 +1164,14 @@ constexpr bool bwd_pipelined() {
 // Backward (DD = false): grad_x (out), grad_Y (dY), grad_W (dW) of <G, out>.
 // Double backward's second pass (DD = true): the same three outputs of
 // <a, dx> + <b, dY> + <c, dW>, with the cotangents a (row-resident like x),
-// b and c; a null cotangent reads as zeros.  SHV: Y from the edge vectors
+// b and c; a null cotangent reads as zeros.  kYVec: Y from the edge vectors
 // a.vec per chunk of 64 row edges (as in the forward), each edge's
 // channel-summed dY into the wave's LDS block, and at the chunk's end
 // grad_vec (a.gvec) of its edges, one lane each.
-template <typename T, int L, class P, bool DD, int R, bool SHV = false>
+template <typename T, int L, class P, bool DD, int R, int YS = kYGlobal>
 __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
+  constexpr bool SHV = YS == kYVec;
+  static_assert(YS != kYRows, "the backward loads Y per slot or evaluates it from vectors");
   static_assert(!(SHV && DD), "harmonics from edge vectors: backward only");
   using B = Bwd<T, L, P>;
   using BD = BwdDD<T, L, P>;
@@ -1192,7 +1210,7 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
   const int64_t wstride = P::wstride(a);
   const T* __restrict__ VEC = static_cast<const T*>(a.vec);
   T* __restrict__ GV = static_cast<T*>(a.gvec);
-  // SHV: per wave, the current chunk's harmonics and channel-summed dY (row
+  // kYVec: per wave, the current chunk's harmonics and channel-summed dY (row
   // position within the chunk major), and the vectors and edge ids of the
   // chunk by its parity (a chunk's ids are fetched one step before the
   // previous chunk's last step has run)
@@ -1471,9 +1489,9 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
     }
   };
 
-  // SHV: after a chunk's last step, grad_vec of the chunk's edges (one lane
+  // kYVec: after a chunk's last step, grad_vec of the chunk's edges (one lane
   // each) from their vectors and channel-summed dY in LDS
-  auto vec_pass = [&](int k) {
+  auto chunk_pass = [&](int k) {
     if constexpr (SHV) {
       if (GV == nullptr) return;
       if (((k + 1) & chunk_mask) != 0 && k + 1 < n_steps) return;  // wave-uniform
@@ -1482,8 +1500,8 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
       const int pos = ((k >> lg) << 6) + lane;  // this lane's row position in the chunk
       if (pos < deg) {
         const int e = s_ve[wave][par][lane];
-        const T* vv = &s_vv[wave][par][lane][0];
         const T* gy = &s_vdy[wave][lane][0];
+        const T* vv = &s_vv[wave][par][lane][0];
         double gx, gyv, gz;
         shx::sh_vec_grad<L>(double(vv[0]), double(vv[1]), double(vv[2]),
                             [&](int kk) { return kk < d_sh ? double(gy[kk]) : 0.0; }, gx, gyv, gz);
@@ -1508,11 +1526,11 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
     for (int k = 0; k < n_steps; k += 2) {  // wave-uniform trip count
       prefetch(k + 1, eb, vb, qb, ib);
       compute(ea, va, qa, ia, pd);
-      vec_pass(k);
+      chunk_pass(k);
       if (k + 1 >= n_steps) break;
       prefetch(k + 2, ea, va, qa, ia);
       compute(eb, vb, qb, ib, pd);
-      vec_pass(k + 1);
+      chunk_pass(k + 1);
     }
   } else if constexpr (kLate) {
     if (n_steps > 0) prefetch(0, ea, va, qa, ia);
@@ -1527,7 +1545,7 @@ __global__ __launch_bounds__(256) void bwd_kernel(const KernelArgs a) {
     for (int k = 0; k < n_steps; ++k) {
       prefetch(k, ea, va, qa, ia);
       compute(ea, va, qa, ia, pd);
-      vec_pass(k);
+      chunk_pass(k);
     }
   }
 
@@ -1964,21 +1982,21 @@ constexpr bool kDD = TPCONV_DD != 0;
 // its memory latency behind.
 constexpr int kSplitRows = 1024;
 
-template <typename T, class P, int R = 1, bool SHV = false>
+template <typename T, class P, int R = 1, int YS = kYGlobal>
 hipError_t launch_fwd(const KernelArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
   const int rows_per_block = 4 / R;
   const int blocks = (a.n_rows + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL((fwd_kernel<T, TPCONV_L, P, kDD, R, SHV>), dim3(blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((fwd_kernel<T, TPCONV_L, P, kDD, R, YS>), dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <typename T, class P, int R = 1, bool SHV = false>
+template <typename T, class P, int R = 1, int YS = kYGlobal>
 hipError_t launch_bwd(const KernelArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
   const int rows_per_block = 4 / R;
   const int blocks = (a.n_rows + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL((bwd_kernel<T, TPCONV_L, P, kDD, R, SHV>), dim3(blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((bwd_kernel<T, TPCONV_L, P, kDD, R, YS>), dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -2002,21 +2020,22 @@ template <int... Us>
 struct UList {};
 using FullMuls = UList<16, 32, 64>;
 
-template <typename T, bool FWD, bool SHV, class FP>
+template <typename T, bool FWD, int YS, class FP>
 hipError_t launch_full_rows(const KernelArgs& a, hipStream_t s) {
   // the fp64 l = 4 backward with harmonics from vectors holds ~117 KB of LDS
   // per block: no room for the split rows' LDS as well
-  constexpr bool kWhole = SHV && !FWD && sizeof(T) == 8 && TPCONV_L >= 4;
+  constexpr bool kWhole = YS == kYVec && !FWD && sizeof(T) == 8 && TPCONV_L >= 4;
   if constexpr (FWD) {
-    if (a.n_rows <= kSplitRows) return launch_fwd<T, FP, 4, SHV>(a, s);
-    return launch_fwd<T, FP, 1, SHV>(a, s);
+    if (a.n_rows <= kSplitRows) return launch_fwd<T, FP, 4, YS>(a, s);
+    return launch_fwd<T, FP, 1, YS>(a, s);
   } else {
     if constexpr (!kWhole) {
-      if (a.n_rows <= kSplitRows) return launch_bwd<T, FP, 4, SHV>(a, s);
+      if (a.n_rows <= kSplitRows) return launch_bwd<T, FP, 4, YS>(a, s);
     }
-    return launch_bwd<T, FP, 1, SHV>(a, s);
+    return launch_bwd<T, FP, 1, YS>(a, s);
   }
 }
+
 
 template <typename T, bool FWD, int U0, int... Us>
 bool launch_full(const KernelArgs& a, hipStream_t s, hipError_t& err, UList<U0, Us...>) {
@@ -2024,11 +2043,13 @@ bool launch_full(const KernelArgs& a, hipStream_t s, hipError_t& err, UList<U0, 
     using FP = FullPlan<TPCONV_L, U0>;
     if constexpr (!kDD) {
       if (a.from_vec) {
-        err = launch_full_rows<T, FWD, true, FP>(a, s);
+        err = launch_full_rows<T, FWD, kYVec, FP>(a, s);
         return true;
       }
+      err = launch_full_rows<T, FWD, FWD ? kYRows : kYGlobal, FP>(a, s);
+      return true;
     }
-    err = launch_full_rows<T, FWD, false, FP>(a, s);
+    err = launch_full_rows<T, FWD, kYGlobal, FP>(a, s);
     return true;
   }
   if constexpr (sizeof...(Us) > 0) {
@@ -2038,12 +2059,12 @@ bool launch_full(const KernelArgs& a, hipStream_t s, hipError_t& err, UList<U0, 
   }
 }
 
-template <typename T, bool FWD, bool SHV>
+template <typename T, bool FWD, int YS>
 hipError_t dispatch_rt(const KernelArgs& a, hipStream_t s) {
   using PE = RtPlan<TPCONV_L, kEvenOnly>;
   using PA = RtPlan<TPCONV_L, kAnyParity>;
-  if (all_even(a)) return FWD ? launch_fwd<T, PE, 1, SHV>(a, s) : launch_bwd<T, PE, 1, SHV>(a, s);
-  return FWD ? launch_fwd<T, PA, 1, SHV>(a, s) : launch_bwd<T, PA, 1, SHV>(a, s);
+  if (all_even(a)) return FWD ? launch_fwd<T, PE, 1, YS>(a, s) : launch_bwd<T, PE, 1, YS>(a, s);
+  return FWD ? launch_fwd<T, PA, 1, YS>(a, s) : launch_bwd<T, PA, 1, YS>(a, s);
 }
 
 template <typename T, bool FWD>
@@ -2051,9 +2072,9 @@ hipError_t dispatch(const KernelArgs& a, hipStream_t s) {
   hipError_t err = hipSuccess;
   if (a.full_plan && launch_full<T, FWD>(a, s, err, FullMuls{})) return err;
   if constexpr (!kDD) {
-    if (a.from_vec) return dispatch_rt<T, FWD, true>(a, s);
+    if (a.from_vec) return dispatch_rt<T, FWD, kYVec>(a, s);
   }
-  return dispatch_rt<T, FWD, false>(a, s);
+  return dispatch_rt<T, FWD, kYGlobal>(a, s);
 }
 
 }  // namespace
