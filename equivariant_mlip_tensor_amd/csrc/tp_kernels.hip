@@ -36,7 +36,8 @@
 //    block, which meet in LDS (row_part, template parameter R);
 //  * fp64 contractions sum the products that share an (m3, |c|) pair before
 //    one multiply by the coefficient (Grouped), because an fp64 coefficient
-//    is no inline literal.
+//    is no inline literal; the fp64 forward forms each product where it is
+//    summed (an FMA per entry) instead of once per (l1, l2) group.
 //
 // With KernelArgs::from_vec set (template parameter YS = kYVec; one launch per plan) the forward and
 // backward evaluate each edge's harmonics themselves from the edge vector
@@ -470,10 +471,14 @@ struct Fwd {
         // a group with an l = 0 leg holds the one path (l1, l2, max(l1, l2));
         // its weight and scalar factor are folded first, so no products
         constexpr bool kDiagGroup = (l1 == 0 || l2 == 0) && TabInfo<l1, l2, (l1 > l2 ? l1 : l2)>::kDiag != 0;
+        // fp64: each product x[m1] Y[m2] is formed where its entry is summed
+        // (one FMA per entry in place of a product per pair plus an add per
+        // entry): fewer instructions and no product array in registers
+        constexpr bool kAtUse = sizeof(T) == 8;
         T pr[n1 * n2];
         static_for<n1>([&](auto M1) {
           static_for<n2>([&](auto M2) {
-            if constexpr (!kDiagGroup && group_uses<L, P::kPar, l1, l2>(M1, M2))
+            if constexpr (!kAtUse && !kDiagGroup && group_uses<L, P::kPar, l1, l2>(M1, M2))
               pr[M1 * n2 + M2] = x[l1 * l1 + M1] * y[l2 * l2 + M2];
           });
         });
@@ -501,10 +506,17 @@ struct Fwd {
                   T acc_g = T(0);
                   static_for<GR::ord.n>([&](auto K) {
                     constexpr cg::Entry en = TI::tab.e[GR::ord.idx[K]];
-                    const T p = pr[en.m1 * n2 + en.m2];
-                    if constexpr (GR::ord.open[K]) acc_g = p;
-                    else if constexpr (GR::ord.sub[K]) acc_g = acc_g - p;
-                    else acc_g = acc_g + p;
+                    if constexpr (kAtUse) {
+                      const T xv = x[l1 * l1 + en.m1], yv = y[l2 * l2 + en.m2];
+                      if constexpr (GR::ord.open[K]) acc_g = xv * yv;
+                      else if constexpr (GR::ord.sub[K]) acc_g = fmaT(-xv, yv, acc_g);
+                      else acc_g = fmaT(xv, yv, acc_g);
+                    } else {
+                      const T p = pr[en.m1 * n2 + en.m2];
+                      if constexpr (GR::ord.open[K]) acc_g = p;
+                      else if constexpr (GR::ord.sub[K]) acc_g = acc_g - p;
+                      else acc_g = acc_g + p;
+                    }
                     if constexpr (GR::ord.close[K]) {
                       constexpr T c = GR::ord.flip[K] ? T(-en.mag) : T(en.mag);
                       if constexpr (GR::ord.first_m3[K])
