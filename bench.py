@@ -62,7 +62,8 @@ def parse():
                         "fused and unfused (0 skips); reported as radial")
     p.add_argument("--radial-hidden", type=int, default=64)
     p.add_argument("--copy-calibration-mib", type=int, default=0,
-                   help="also run one plain device copy of this many MiB (scales rocprofv3 FETCH/WRITE_SIZE)")
+                   help="also run one plain device copy of this many MiB, then a random-order gather of 64-byte "
+                        "rows of the same size (scale rocprofv3 FETCH/WRITE_SIZE)")
     return p.parse_args()
 
 
@@ -214,7 +215,15 @@ def main():
         a_dst = torch.empty_like(a_src)
         a_dst.copy_(a_src)
         torch.cuda.synchronize()
-        del a_src, a_dst
+        # and a gather of the same bytes in random order: rows of 16 floats
+        # (64 B) read once each through a random permutation (int64 indices),
+        # the access pattern of the kernels' neighbour gathers
+        rows = n // 16
+        perm = torch.randperm(rows, device=dev)
+        torch.cuda.synchronize()
+        torch.index_select(a_src.view(rows, 16), 0, perm, out=a_dst.view(rows, 16))
+        torch.cuda.synchronize()
+        del a_src, a_dst, perm
 
     for _ in range(args.warmup):
         step()
