@@ -284,6 +284,22 @@ struct FullPlan {
   }
 };
 
+// A full plan restricted to the paths into the output l's in OUT (bit l):
+// the forward of a plan too wide for the register file runs as launches over
+// disjoint sets of output l's, each writing only its own output columns.
+template <int L, int U, int OUT>
+struct FullPlanPart : FullPlan<L, U> {
+  template <int t>
+  static __device__ __forceinline__ constexpr bool on(const KernelArgs&) {
+    constexpr bool v = triple_even(L, t) && ((OUT >> triple_at(L, t).l3) & 1);
+    return v;
+  }
+  static __device__ __forceinline__ constexpr int out_off(const KernelArgs&, int l) {
+    return ((OUT >> l) & 1) ? U * l * l : -1;
+  }
+  static __device__ __forceinline__ constexpr bool out_l(const KernelArgs&, int l) { return (OUT >> l) & 1; }
+};
+
 // Compile-time facts about a CG table.
 template <int L1, int L2, int L3>
 struct TabInfo {
@@ -2056,6 +2072,15 @@ bool launch_full(const KernelArgs& a, hipStream_t s, hipError_t& err, UList<U0, 
     if constexpr (!kDD) {
       if (a.from_vec) {
         err = launch_full_rows<T, FWD, kYVec, FP>(a, s);
+        return true;
+      }
+      if constexpr (FWD && sizeof(T) == 8 && TPCONV_L == 4) {
+        // fp64, l <= 4: output l's {0, 1, 4} and {2, 3} in two launches (one
+        // launch needs 256 VGPRs + ~100 AGPRs, one wavefront per SIMD; each
+        // part fits 221-239 VGPRs, two wavefronts per SIMD; c2k forward
+        // 0.221 -> 0.206 ms)
+        err = launch_full_rows<T, true, kYRows, FullPlanPart<4, U0, 0b10011>>(a, s);
+        if (err == hipSuccess) err = launch_full_rows<T, true, kYRows, FullPlanPart<4, U0, 0b01100>>(a, s);
         return true;
       }
       err = launch_full_rows<T, FWD, FWD ? kYRows : kYGlobal, FP>(a, s);
