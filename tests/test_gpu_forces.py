@@ -151,3 +151,31 @@ def test_force_chain(tp, name):
     # internal forces sum to zero (every edge adds to one atom what it takes from another)
     gp = gpos.cpu().numpy().astype(np.float64)
     assert np.abs(gp.sum(axis=0)).max() <= 1e-5 * np.abs(gp).sum()
+
+
+def test_force_chain_c4k_sampled(tp):
+    """The three-kernel force chain (tpconv_sh -> tpconv_backward -> tpconv_sh_backward ->
+    tpconv_positions_backward) on the full 4096-atom workload, checked at sampled atoms: each
+    sampled atom's force needs grad_vec of every edge touching it, which the oracle computes
+    for those edges only."""
+    import torch
+    w = workloads.WORKLOADS["c4k"]
+    prob = TPProblem.build(w.irreps_in, w.sh_lmax, w.irreps_out)
+    d = workloads.make_inputs(w, len(prob.paths), prob.weight_numel)
+    N, src, dst = d["n_nodes"], d["src"], d["dst"]
+    vec = d["vec"].astype(w.np_dtype)
+    plan = tp.tpconv_plan(w.irreps_in, w.sh_lmax, w.irreps_out, w.dtype)
+    g = tp.tpconv_graph_create(N, dev(src), dev(dst))
+    v = dev(vec)
+    Y = tp.tpconv_sh(plan, v)
+    _, dY, _ = tp.tpconv_backward(plan, g, dev(d["x"]), Y, dev(d["W"]), dev(d["G"]), need=(False, True, False))
+    gpos = tp.tpconv_positions_backward(plan, g, tp.tpconv_sh_backward(plan, v, dY)).cpu().numpy()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(13)
+    atoms = np.unique(np.concatenate([rng.choice(N, 60, replace=False), [0, N - 1]]))
+    m = np.isin(src, atoms) | np.isin(dst, atoms)
+    _, rdY, _ = tp_backward(prob, d["x"], sh_edges(w.sh_lmax, vec[m]), d["W"][m], d["G"], src[m], dst[m], N)
+    ref = positions_backward(sh_backward(w.sh_lmax, vec[m], rdY), src[m], dst[m], N)
+    err = rel_err(gpos[atoms], ref[atoms])
+    log(f"[forces] chain c4k at {len(atoms)} atoms ({int(m.sum())} edges): grad_pos error {err:.3e}")
+    assert err <= TOL[w.dtype]
