@@ -36,8 +36,9 @@
 //    block, which meet in LDS (row_part, template parameter R);
 //  * fp64 contractions sum the products that share an (m3, |c|) pair before
 //    one multiply by the coefficient (Grouped), because an fp64 coefficient
-//    is no inline literal; the fp64 forward forms each product where it is
-//    summed (an FMA per entry) instead of once per (l1, l2) group.
+//    is no inline literal; the fp64 forward and double-backward grad_G pass
+//    form each product where it is summed (an FMA per entry) instead of once
+//    per (l1, l2) group.
 //
 // With KernelArgs::from_vec set (template parameter YS = kYVec; one launch per plan) the forward and
 // backward evaluate each edge's harmonics themselves from the edge vector
@@ -585,10 +586,12 @@ struct FwdDD {
         if (!group_on<L, P, l1, l2>(a)) return;
         constexpr int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1;
         constexpr bool kDiagGroup = (l1 == 0 || l2 == 0) && TabInfo<l1, l2, (l1 > l2 ? l1 : l2)>::kDiag != 0;
+        // fp64: products formed where each entry is summed, as in the forward
+        constexpr bool kAtUse = sizeof(T) == 8;
         T p1[n1 * n2], p2[n1 * n2];
         static_for<n1>([&](auto M1) {
           static_for<n2>([&](auto M2) {
-            if constexpr (!kDiagGroup && group_uses<L, P::kPar, l1, l2>(M1, M2)) {
+            if constexpr (!kAtUse && !kDiagGroup && group_uses<L, P::kPar, l1, l2>(M1, M2)) {
               const T xv = x[l1 * l1 + M1], yv = y[l2 * l2 + M2];
               p1[M1 * n2 + M2] = xv * yv;
               p2[M1 * n2 + M2] = fmaT(xa[l1 * l1 + M1], yv, xv * yb[l2 * l2 + M2]);
@@ -628,7 +631,20 @@ struct FwdDD {
                 static_for<GR::ord.n>([&](auto K) {
                   constexpr cg::Entry en = TI::tab.e[GR::ord.idx[K]];
                   constexpr int pi = en.m1 * n2 + en.m2;
-                  if constexpr (GR::ord.open[K]) {
+                  if constexpr (kAtUse) {
+                    const T xv = x[l1 * l1 + en.m1], av = xa[l1 * l1 + en.m1];
+                    const T yv = y[l2 * l2 + en.m2], bv = yb[l2 * l2 + en.m2];
+                    if constexpr (GR::ord.open[K]) {
+                      g1 = xv * yv;
+                      g2 = fmaT(av, yv, xv * bv);
+                    } else if constexpr (GR::ord.sub[K]) {
+                      g1 = fmaT(-xv, yv, g1);
+                      g2 = fmaT(-av, yv, fmaT(-xv, bv, g2));
+                    } else {
+                      g1 = fmaT(xv, yv, g1);
+                      g2 = fmaT(av, yv, fmaT(xv, bv, g2));
+                    }
+                  } else if constexpr (GR::ord.open[K]) {
                     g1 = p1[pi];
                     g2 = p2[pi];
                   } else if constexpr (GR::ord.sub[K]) {
