@@ -86,7 +86,7 @@ def test_plan_matches_oracle_paths_and_cg(tp, case):
     assert nnz == plan.cg_nnz
 
 
-def test_survey_sizes(tp):
+def test_workload_path_and_table_sizes(tp):
     # path count, nonzeros and distinct values of the l<=3 and l<=4 workloads
     w3 = workloads.WORKLOADS["c4k"]
     p3 = tp.tpconv_plan(w3.irreps_in, 3, w3.irreps_out, "f32")
