@@ -2086,6 +2086,13 @@ bool launch_full(const KernelArgs& a, hipStream_t s, hipError_t& err, UList<U0, 
   if (a.mul == U0) {
     using FP = FullPlan<TPCONV_L, U0>;
     if constexpr (!kDD) {
+      if constexpr (FWD && sizeof(T) == 8 && TPCONV_L == 4) {
+        if (a.from_vec) {  // the same split with the harmonics evaluated in each launch
+          err = launch_full_rows<T, true, kYVec, FullPlanPart<4, U0, 0b10011>>(a, s);
+          if (err == hipSuccess) err = launch_full_rows<T, true, kYVec, FullPlanPart<4, U0, 0b01100>>(a, s);
+          return true;
+        }
+      }
       if (a.from_vec) {
         err = launch_full_rows<T, FWD, kYVec, FP>(a, s);
         return true;
