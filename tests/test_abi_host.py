@@ -131,6 +131,8 @@ def test_null_and_size_errors_need_no_gpu(tp):
     assert lib.tpconv_plan_query(None, None) == 1
     assert lib.tpconv_forward(None, None, None, None, None, None, None) == 1
     assert lib.tpconv_backward(None, None, None, None, None, None, None, None, None, None) == 1
+    assert lib.tpconv_forward_vec(None, None, None, None, None, None, None) == 1
+    assert lib.tpconv_backward_vec(None, None, None, None, None, None, None, None, None, None) == 1
     assert lib.tpconv_double_backward(*([None] * 14)) == 1
     assert lib.tpconv_sh(None, 0, None, None, None) == 1
     assert lib.tpconv_sh_backward(None, 0, None, None, None, None) == 1
